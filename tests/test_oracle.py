@@ -1,0 +1,339 @@
+"""Pins for the fp64 oracle: closed forms, invariants, brute force, finite
+differences and an independent library routine (torch CPU fp64 SDPA)."""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from oracle.attention import safe_softmax, validity
+
+RTOL = 1e-12
+
+
+def rnd(shape, seed, std=1.0):
+    return np.random.default_rng(seed).standard_normal(shape) * std
+
+
+def small_case(B=2, H=2, N=37, d=8, seed=0):
+    return rnd((B, H, N, d), seed), rnd((B, H, N, d), seed + 1), rnd((B, H, N, d), seed + 2), \
+        rnd((B, H, N, d), seed + 3)
+
+
+def mask_variants(N, B):
+    T = -(-N // 128)
+    bm = np.ones((T, T), np.uint8)
+    if T > 1:
+        bm[0, T - 1] = 0
+    return [dict(causal=False), dict(causal=True),
+            dict(causal=False, key_lens=np.array([N // 2, N][:B])),
+            dict(causal=True, key_lens=np.array([5, N - 3][:B])),
+            dict(causal=False, block_mask=bm)]
+
+
+# ---------------------------------------------------------------- golden fixtures
+
+def test_golden_causal_mask(golden_dir):
+    rows = [l.split() for l in open(f"{golden_dir}/causal_mask_4x4.txt") if not l.startswith("#")]
+    want = np.array(rows, dtype=int).astype(bool)
+    got = validity(np.arange(4), 4, causal=True)
+    assert (got == want).all()
+
+
+def test_golden_shape_trace(golden_dir):
+    kv = {}
+    for line in open(f"{golden_dir}/shape_trace.txt"):
+        if line.startswith("#") or not line.strip():
+            continue
+        k, *v = line.split()
+        kv[k] = [int(x) for x in v]
+    b, s, h, hd = kv["batch"][0], kv["seq_len"][0], kv["num_heads"][0], kv["head_dim"][0]
+    q = rnd((b, h, s, hd), 1)
+    k = rnd((b, h, s, hd), 2)
+    v = rnd((b, h, s, hd), 3)
+    scale = 1.0 / kv["scale_divisor"][0]
+    assert scale == 1.0 / np.sqrt(hd)
+    O, L = oracle.attn_fwd(q, k, v, scale)
+    assert list(q.shape) == kv["q_shape"] and list(O.shape) == kv["out_shape"]
+    # the score matrix is seq x seq per head: check by materialising one head
+    S = scale * q[0, 0] @ k[0, 0].T
+    assert [b, h, *S.shape] == kv["scores_shape"]
+
+
+# ---------------------------------------------------------------- softmax / merge
+
+def test_rows_sum_to_one():
+    rng = np.random.default_rng(0)
+    S = rng.standard_normal((50, 70)) * 30
+    A = rng.random((50, 70)) < 0.3
+    A[7] = False
+    P, lse, m, l = safe_softmax(S, A)
+    has = A.any(axis=1)
+    assert np.allclose(P[has].sum(axis=1), 1.0, rtol=0, atol=RTOL)
+    assert (P[~A] == 0).all()
+    assert (P[7] == 0).all() and lse[7] == -np.inf
+    # LSE is the log of the normaliser of the exponentials
+    ref = np.array([np.log(np.exp(S[i][A[i]]).sum()) if A[i].any() else -np.inf for i in range(50)])
+    assert np.allclose(lse[has], ref[has], rtol=1e-13, atol=0)
+
+
+@pytest.mark.parametrize("seed", range(5))
+def test_two_block_merge_formula(seed):
+    """m(x) = max(m1, m2), l(x) = e^{m1-m} l1 + e^{m2-m} l2 equals the one-pass values,
+    including a split where one part is entirely -inf."""
+    rng = np.random.default_rng(seed)
+    x = rng.standard_normal(64) * 20
+    if seed == 3:
+        x[:20] = -np.inf
+    cut = [1, 20, 33, 63, 40][seed]
+    x1, x2 = x[:cut], x[cut:]
+
+    def stats(z):
+        m = z.max()
+        return m, (np.exp(z - m).sum() if np.isfinite(m) else 0.0)
+    m1, l1 = stats(x1)
+    m2, l2 = stats(x2)
+    m = max(m1, m2)
+    l = (np.exp(m1 - m) * l1 if np.isfinite(m1) else 0.0) + (np.exp(m2 - m) * l2 if np.isfinite(m2) else 0.0)
+    mf, lf = stats(x)
+    assert m == mf
+    assert abs(l - lf) <= 1e-12 * lf
+
+
+@pytest.mark.parametrize("Br,Bc", [(1, 1), (7, 13), (16, 16), (64, 32), (37, 5)])
+@pytest.mark.parametrize("variant", range(5))
+def test_tiled_merge_equals_full_row_softmax(Br, Bc, variant):
+    q, k, v, _ = small_case(B=2, H=1, N=37, d=8, seed=10 + variant)
+    kw = mask_variants(37, 2)[variant]
+    O, L = oracle.attn_fwd(q, k, v, 0.3, **kw)
+    Ot, Lt = oracle.tiled_fwd(q, k, v, 0.3, Br, Bc, **kw)
+    assert np.allclose(Ot, O, rtol=0, atol=1e-12)
+    fin = np.isfinite(L)
+    assert (np.isfinite(Lt) == fin).all()
+    assert np.allclose(Lt[fin], L[fin], rtol=0, atol=1e-12)
+
+
+# ---------------------------------------------------------------- closed forms
+
+@pytest.mark.parametrize("variant", range(5))
+def test_constant_v_gives_constant_output(variant):
+    q, k, _, _ = small_case(B=2, H=2, N=300, d=8, seed=3)
+    vrow = rnd((8,), 9)
+    v = np.broadcast_to(vrow, q.shape).copy()
+    kw = mask_variants(300, 2)[variant]
+    O, L = oracle.attn_fwd(q, k, v, 0.5, **kw)
+    assert np.allclose(O, vrow, rtol=0, atol=1e-12)
+
+
+@pytest.mark.parametrize("variant", range(5))
+def test_zero_query_closed_form(variant):
+    """Q = 0: P is uniform over the valid keys; O is their mean; LSE = ln(count)."""
+    N = 300
+    _, k, v, _ = small_case(B=2, H=1, N=N, d=8, seed=4)
+    q = np.zeros_like(k)
+    kw = mask_variants(N, 2)[variant]
+    O, L = oracle.attn_fwd(q, k, v, 0.7, **kw)
+    for b in range(2):
+        kl = None if kw.get("key_lens") is None else kw["key_lens"][b]
+        A = validity(np.arange(N), N, kw.get("causal", False), kl, kw.get("block_mask"))
+        cnt = A.sum(axis=1)
+        want = (A.astype(float) @ v[b, 0]) / cnt[:, None]
+        assert np.allclose(O[b, 0], want, rtol=0, atol=1e-12)
+        assert np.allclose(L[b, 0], np.log(cnt), rtol=0, atol=1e-12)
+
+
+def test_causal_first_row():
+    q, k, v, _ = small_case(B=1, H=3, N=50, d=16, seed=5)
+    scale = 0.25
+    O, L = oracle.attn_fwd(q, k, v, scale, causal=True)
+    assert np.allclose(O[:, :, 0], v[:, :, 0], rtol=0, atol=1e-15)
+    s32 = float(np.float32(scale))
+    assert np.allclose(L[:, :, 0], s32 * np.einsum("bhd,bhd->bh", q[:, :, 0], k[:, :, 0]), atol=1e-13)
+
+
+def test_single_key():
+    q, k, v, _ = small_case(B=1, H=1, N=1, d=8, seed=6)
+    O, L = oracle.attn_fwd(q, k, v, 0.1)
+    assert np.allclose(O, v) and np.allclose(L[0, 0, 0], float(np.float32(0.1)) * (q[0, 0, 0] @ k[0, 0, 0]))
+
+
+# ---------------------------------------------------------------- invariants
+
+def test_key_value_permutation_equivariance():
+    q, k, v, _ = small_case(B=1, H=2, N=64, d=8, seed=7)
+    perm = np.random.default_rng(1).permutation(64)
+    O, L = oracle.attn_fwd(q, k, v, 0.4)
+    Op, Lp = oracle.attn_fwd(q, k[:, :, perm], v[:, :, perm], 0.4)
+    assert np.allclose(O, Op, atol=1e-12) and np.allclose(L, Lp, atol=1e-12)
+    # permuting query rows permutes the outputs
+    Oq, Lq = oracle.attn_fwd(q[:, :, perm], k, v, 0.4)
+    assert np.allclose(Oq, O[:, :, perm], atol=1e-12) and np.allclose(Lq, L[:, :, perm], atol=1e-12)
+
+
+@pytest.mark.parametrize("mag", [1.0, 1e3])
+def test_shift_invariance(mag):
+    q, k, v, _ = small_case(B=1, H=2, N=40, d=8, seed=8)
+    u = rnd((8,), 11) * mag
+    scale = 0.5
+    O, L = oracle.attn_fwd(q, k, v, scale, causal=True)
+    Os, Ls = oracle.attn_fwd(q, k + u, v, scale, causal=True)
+    s32 = float(np.float32(scale))
+    assert np.all(np.isfinite(Os))
+    assert np.allclose(Os, O, atol=1e-9 * mag)
+    assert np.allclose(Ls, L + s32 * (q @ u), rtol=1e-12, atol=1e-9 * mag)
+
+
+def test_fully_masked_rows():
+    q, k, v, do = small_case(B=2, H=1, N=20, d=4, seed=9)
+    kl = np.array([0, 20])
+    O, L = oracle.attn_fwd(q, k, v, 0.5, key_lens=kl)
+    assert (O[0] == 0).all() and (L[0] == -np.inf).all() and np.isfinite(L[1]).all()
+    dq, dk, dv, D = oracle.attn_bwd(q, k, v, do, 0.5, key_lens=kl)
+    assert (dq[0] == 0).all() and (dk[0] == 0).all() and (dv[0] == 0).all()
+
+
+# ---------------------------------------------------------------- library routine
+
+def _sdpa_ref(q, k, v, do, scale, causal, key_lens, block_mask):
+    tq, tk, tv = (torch.tensor(x, dtype=torch.float64, requires_grad=True) for x in (q, k, v))
+    B, H, N, d = q.shape
+    mask = torch.ones(B, 1, N, N, dtype=torch.bool)
+    if causal:
+        mask &= torch.ones(N, N, dtype=torch.bool).tril()
+    if key_lens is not None:
+        mask &= (torch.arange(N)[None, :] < torch.tensor(key_lens)[:, None])[:, None, None, :]
+    if block_mask is not None:
+        idx = torch.arange(N) // 128
+        mask &= torch.tensor(block_mask).bool()[idx[:, None], idx[None, :]]
+    o = torch.nn.functional.scaled_dot_product_attention(
+        tq, tk, tv, attn_mask=mask, scale=float(np.float32(scale)))
+    o.backward(torch.tensor(do))
+    return o.detach().numpy(), tq.grad.numpy(), tk.grad.numpy(), tv.grad.numpy()
+
+
+@pytest.mark.parametrize("variant", range(5))
+def test_against_torch_sdpa_fp64(variant):
+    N = 300
+    q, k, v, do = small_case(B=2, H=2, N=N, d=16, seed=20 + variant)
+    kw = mask_variants(N, 2)[variant]
+    if variant == 3:          # every row needs a valid key for SDPA (it NaNs empty rows)
+        kw["key_lens"] = np.array([N - 100, N - 3])
+    scale = 0.21
+    O, L = oracle.attn_fwd(q, k, v, scale, **kw)
+    dq, dk, dv, _ = oracle.attn_bwd(q, k, v, do, scale, **kw)
+    Or, dqr, dkr, dvr = _sdpa_ref(q, k, v, do, scale, kw.get("causal", False),
+                                  kw.get("key_lens"), kw.get("block_mask"))
+    assert np.allclose(O, Or, rtol=0, atol=1e-12)
+    for a, b in ((dq, dqr), (dk, dkr), (dv, dvr)):
+        assert np.allclose(a, b, rtol=0, atol=1e-11)
+
+
+# ---------------------------------------------------------------- gradients
+
+def _loss(q, k, v, do, scale, kw):
+    O, _ = oracle.attn_fwd(q, k, v, scale, **kw)
+    return float((O * do).sum())
+
+
+@pytest.mark.parametrize("variant", ["dense", "causal", "padding", "block", "dropout"])
+def test_finite_differences(variant):
+    N, d = 12, 4
+    q, k, v, do = small_case(B=1, H=1, N=N, d=d, seed=31)
+    kw = {}
+    if variant == "causal":
+        kw = dict(causal=True)
+    elif variant == "padding":
+        kw = dict(key_lens=np.array([7]))
+    elif variant == "block":
+        kw = dict(block_mask=np.array([[1]], np.uint8), causal=True)
+    elif variant == "dropout":
+        kw = dict(dropout_p=0.3, seed=123, rng_offset=5)
+    scale = 0.37
+    dq, dk, dv, _ = oracle.attn_bwd(q, k, v, do, scale, **kw)
+    h = 1e-6
+    for name, x, g in (("q", q, dq), ("k", k, dk), ("v", v, dv)):
+        num = np.zeros_like(x)
+        it = np.nditer(x, flags=["multi_index"])
+        for _ in it:
+            idx = it.multi_index
+            xp = x.copy(); xp[idx] += h
+            xm = x.copy(); xm[idx] -= h
+            args = dict(q=q, k=k, v=v)
+            args[name] = xp
+            fp = _loss(args["q"], args["k"], args["v"], do, scale, kw)
+            args[name] = xm
+            fm = _loss(args["q"], args["k"], args["v"], do, scale, kw)
+            num[idx] = (fp - fm) / (2 * h)
+        err = np.abs(num - g).max() / max(np.abs(g).max(), 1e-300)
+        assert err < 1e-6, (name, err)
+
+
+@pytest.mark.parametrize("variant", range(5))
+def test_dk_sums_to_zero_and_D_two_ways(variant):
+    N = 200
+    q, k, v, do = small_case(B=2, H=2, N=N, d=8, seed=40 + variant)
+    kw = mask_variants(N, 2)[variant]
+    kw.update(dropout_p=0.2, seed=7) if variant == 2 else None
+    dq, dk, dv, D = oracle.attn_bwd(q, k, v, do, 0.3, **kw)
+    assert np.allclose(dk.sum(axis=2), 0.0, atol=1e-10)
+    O, _ = oracle.attn_fwd(q, k, v, 0.3, **kw)
+    assert np.allclose(D, (do * O).sum(axis=-1), atol=1e-12)
+
+
+@pytest.mark.parametrize("dropout", [False, True])
+def test_backward_matches_explicit_jacobian(dropout):
+    N = 24
+    q, k, v, do = small_case(B=1, H=2, N=N, d=4, seed=50)
+    kw = dict(causal=True, key_lens=np.array([19]))
+    Z = None
+    if dropout:
+        kw.update(dropout_p=0.25, seed=99, rng_offset=3)
+        Z = np.stack([np.stack([oracle.keep_mask(99, 3, 0.25, 0, h, 2, np.arange(N), np.arange(N))
+                                for h in range(2)])])
+    dq, dk, dv, _ = oracle.attn_bwd(q, k, v, do, 0.6, **kw)
+    jq, jk, jv = oracle.attn_bwd_jacobian(q, k, v, do, 0.6, causal=True, key_lens=np.array([19]),
+                                          Z=Z, dropout_p=kw.get("dropout_p", 0.0))
+    for a, b in ((dq, jq), (dk, jk), (dv, jv)):
+        assert np.allclose(a, b, atol=1e-12)
+
+
+def test_sampled_rows_and_columns_match_full_pass():
+    N = 300
+    q, k, v, do = small_case(B=2, H=2, N=N, d=8, seed=60)
+    kw = dict(causal=True, key_lens=np.array([250, 300]), dropout_p=0.1, seed=4)
+    O, L = oracle.attn_fwd(q, k, v, 0.3, **kw)
+    dq, dk, dv, D = oracle.attn_bwd(q, k, v, do, 0.3, **kw)
+    rows = np.array([0, 1, 5, 129, 299])
+    cols = np.array([0, 3, 128, 249, 250, 299])
+    Or, Lr = oracle.attn_fwd(q, k, v, 0.3, rows=rows, **kw)
+    assert np.allclose(Or, O[:, :, rows], atol=1e-13) and np.allclose(Lr, L[:, :, rows], atol=1e-13)
+    Ls, Ds = oracle.attn_stats(q, k, v, do, 0.3, **kw)
+    assert np.allclose(Ls, L, atol=1e-13) and np.allclose(Ds, D, atol=1e-12)
+    sq, sk, sv = oracle.attn_bwd_rows_cols(q, k, v, do, 0.3, rows, cols, Ls, Ds, **kw)
+    assert np.allclose(sq, dq[:, :, rows], atol=1e-12)
+    assert np.allclose(sk, dk[:, :, cols], atol=1e-12)
+    assert np.allclose(sv, dv[:, :, cols], atol=1e-12)
+
+
+# ---------------------------------------------------------------- dropout placement
+
+def test_dropout_zero_is_dense():
+    q, k, v, do = small_case(B=1, H=2, N=30, d=8, seed=70)
+    a = oracle.attn_fwd(q, k, v, 0.3, dropout_p=0.0, seed=5)
+    b = oracle.attn_fwd(q, k, v, 0.3)
+    assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
+
+
+def test_dropout_is_unbiased_and_lse_undropped():
+    """E_Z[O] = O at p = 0 (inverted dropout), statistically over seeds; LSE
+    ignores the mask."""
+    q, k, v, _ = small_case(B=1, H=1, N=6, d=3, seed=71)
+    O0, L0 = oracle.attn_fwd(q, k, v, 0.5)
+    outs = []
+    for s in range(3000):
+        O, L = oracle.attn_fwd(q, k, v, 0.5, dropout_p=0.5, seed=s)
+        assert np.array_equal(L, L0)
+        outs.append(O)
+    outs = np.stack(outs)
+    mean, se = outs.mean(0), outs.std(0) / np.sqrt(len(outs))
+    assert (np.abs(mean - O0) <= 5 * se + 1e-12).all()

@@ -1,0 +1,62 @@
+"""Pins for the expected tile-visit sets and valid-pair counts (brute force)."""
+
+import numpy as np
+import pytest
+
+import oracle
+from oracle.attention import validity
+
+
+def brute_tiles(N, Br, Bc, B, causal, key_lens, block_mask):
+    Tr, Tc = -(-N // Br), -(-N // Bc)
+    out = np.zeros((B, Tr, Tc), np.uint8)
+    for b in range(B):
+        kl = None if key_lens is None else key_lens[b]
+        A = validity(np.arange(N), N, causal, kl, block_mask)
+        for i in range(Tr):
+            for j in range(Tc):
+                out[b, i, j] = A[i * Br:(i + 1) * Br, j * Bc:(j + 1) * Bc].any()
+    return out
+
+
+@pytest.mark.parametrize("N", [1, 100, 257, 400])
+@pytest.mark.parametrize("Br,Bc", [(128, 64), (32, 128), (64, 64), (48, 80)])
+def test_expected_tiles_brute_force(N, Br, Bc):
+    rng = np.random.default_rng(N + Br)
+    T = -(-N // 128)
+    bm = (rng.random((T, T)) < 0.5).astype(np.uint8)
+    kls = np.array([0, max(N // 3, 1), N])
+    for causal in (False, True):
+        for key_lens in (None, kls):
+            for block_mask in (None, bm):
+                got = oracle.expected_tiles(N, Br, Bc, 3, causal, key_lens, block_mask)
+                want = brute_tiles(N, Br, Bc, 3, causal, key_lens, block_mask)
+                assert np.array_equal(got, want)
+
+
+def test_causal_tile_count_and_ones_mask():
+    T = 16
+    t = oracle.expected_tiles(T * 64, 64, 64, 1, causal=True)
+    assert t.sum() == T * (T + 1) // 2
+    ones = np.ones((8, 8), np.uint8)
+    assert np.array_equal(oracle.expected_tiles(1000, 128, 64, 2, block_mask=ones),
+                          oracle.expected_tiles(1000, 128, 64, 2))
+
+
+@pytest.mark.parametrize("N", [5, 130, 300])
+def test_valid_pair_count_brute_force(N):
+    rng = np.random.default_rng(N)
+    T = -(-N // 128)
+    bm = (rng.random((T, T)) < 0.6).astype(np.uint8)
+    kls = np.array([N // 2, N])
+    for causal in (False, True):
+        for key_lens in (None, kls):
+            for block_mask in (None, bm):
+                want = sum(validity(np.arange(N), N, causal, None if key_lens is None else key_lens[b],
+                                    block_mask).sum() for b in range(2)) * 3
+                assert oracle.valid_pair_count(N, 2, 3, causal, key_lens, block_mask) == want
+
+
+def test_valid_pairs_closed_forms():
+    assert oracle.valid_pair_count(1024, 8, 12, causal=True) == 8 * 12 * 1024 * 1025 // 2
+    assert oracle.valid_pair_count(16384, 1, 16, causal=True) == 2147614720
