@@ -1,0 +1,260 @@
+#!/usr/bin/env python3
+"""Throughput of tiled exact attention (forward + backward) on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload long]
+
+A step is one full pass of the hot path on one batch: the forward kernel
+(O, LSE) followed by the backward (D pre-pass, the S/P-recomputing kernel,
+dQ conversion), on inputs already resident in device memory.  The default
+workload is the long-context causal case (B=1, H=16, N=16384, d=128, bf16),
+the d=128, N>=4K configuration the fraction-of-peak target is stated for.
+
+Algorithmic work counts valid (query, key) pairs only: the forward does
+4*d FLOP per pair (S = Q K^T and P V), the backward 10*d (S recomputed, dP,
+dV, dK, dQ).  Peak: MI355X dense bf16/fp16 MFMA, 2.5 PFLOP/s.
+
+Prints one JSON line (rank 0).  Timing uses HIP events on the stream the
+kernels run on; the backward's main kernel is bracketed by events the
+library records around that one launch.
+"""
+
+from __future__ import annotations
+
+import argparse
+import ctypes
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+PEAK_TFLOPS = {"bf16": 2500.0, "fp16": 2500.0, "fp32": 157.3}
+HBM_GBPS = 8000.0
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="long")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-rows", type=int, default=3072,
+                    help="leading causal rows per head the oracle baseline computes")
+    ap.add_argument("--sweep", action="store_true", help="also time the N sweep (extra JSON lines)")
+    return ap.parse_args()
+
+
+class HipEvents:
+    """hipEvent_t handles through the HIP runtime torch already loaded."""
+
+    def __init__(self):
+        self.hip = ctypes.CDLL("libamdhip64.so.7")
+        self.hip.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        self.hip.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+        self.hip.hipEventSynchronize.argtypes = [ctypes.c_void_p]
+        self.hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p, ctypes.c_void_p]
+        self.hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
+
+    def create(self):
+        ev = ctypes.c_void_p()
+        assert self.hip.hipEventCreate(ctypes.byref(ev)) == 0
+        return ev.value
+
+    def record(self, ev, stream):
+        assert self.hip.hipEventRecord(ev, stream) == 0
+
+    def ms(self, a, b):
+        out = ctypes.c_float()
+        assert self.hip.hipEventSynchronize(b) == 0
+        assert self.hip.hipEventElapsedTime(ctypes.byref(out), a, b) == 0
+        return float(out.value)
+
+    def destroy(self, ev):
+        self.hip.hipEventDestroy(ev)
+
+
+def valid_pairs(x, w):
+    """Number of valid (query, key) pairs over all heads: the unit of
+    algorithmic work.  Valid: (not causal or j <= i) and j < len_b and the
+    128 x 128 block of (i, j) is set in the block mask."""
+    N, T = w.N, 128
+    rows = np.arange(N, dtype=np.int64)
+    bm = None if x["block_mask"] is None else x["block_mask"].numpy().astype(bool)
+    total = 0
+    for b in range(w.B):
+        L = N if x["key_lens"] is None else int(min(max(int(x["key_lens"][b]), 0), N))
+        if bm is None:
+            lim = np.full(N, L, dtype=np.int64)
+            if w.causal:
+                lim = np.minimum(lim, rows + 1)
+            total += int(lim.sum())
+            continue
+        for bi in range(bm.shape[0]):
+            r = rows[bi * T:(bi + 1) * T]
+            for bj in np.flatnonzero(bm[bi]):
+                c0, c1 = bj * T, min((bj + 1) * T, L)
+                if c1 <= c0:
+                    continue
+                hi = np.minimum(r + 1, c1) if w.causal else np.full(len(r), c1)
+                total += int(np.clip(hi - c0, 0, None).sum())
+    return total * w.H
+
+
+def time_workload(w, steps, warmup, ev):
+    import torch
+    import io_aware_exact_tiled_amd as fa
+    import workloads as W
+
+    x = W.make_inputs(w)
+    dev = torch.device("cuda:0")
+    q, k, v, do = (x[n].to(dev) for n in ("q", "k", "v", "do"))
+    kw = dict(causal=w.causal, dropout_p=w.dropout_p, seed=w.dropout_seed, rng_offset=w.rng_offset,
+              key_lens=None if x["key_lens"] is None else x["key_lens"].to(dev),
+              block_mask=None if x["block_mask"] is None else x["block_mask"].to(dev), scale=w.scale)
+    o = torch.empty_like(q)
+    lse = torch.empty(w.B, w.H, w.N, dtype=torch.float32, device=dev)
+    grads = tuple(torch.empty_like(q) for _ in range(3))
+    ws = torch.empty(fa.bwd_workspace_bytes(w.B, w.H, w.N, w.d), dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream(dev).cuda_stream
+    n_ev = steps
+    f0 = [ev.create() for _ in range(n_ev)]
+    f1 = [ev.create() for _ in range(n_ev)]
+    b0 = [ev.create() for _ in range(n_ev)]
+    b1 = [ev.create() for _ in range(n_ev)]
+    s0 = [ev.create() for _ in range(n_ev)]
+    s1 = [ev.create() for _ in range(n_ev)]
+
+    def step(i=None):
+        if i is not None:
+            ev.record(s0[i], stream)
+        fa.fwd(q, k, v, out=o, lse=lse, events=None if i is None else (f0[i], f1[i]), **kw)
+        fa.bwd(q, k, v, o, do, lse, grads=grads, workspace=ws,
+               events=None if i is None else (b0[i], b1[i]), **kw)
+        if i is not None:
+            ev.record(s1[i], stream)
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        step(i)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    fwd_ms = [ev.ms(f0[i], f1[i]) for i in range(steps)]
+    bwd_ms = [ev.ms(b0[i], b1[i]) for i in range(steps)]
+    step_ms = [ev.ms(s0[i], s1[i]) for i in range(steps)]
+    for e in f0 + f1 + b0 + b1 + s0 + s1:
+        ev.destroy(e)
+    pairs = valid_pairs(x, w)
+    return dict(x=x, pairs=pairs, wall_s=wall, fwd_ms=fwd_ms, bwd_main_ms=bwd_ms, step_ms=step_ms)
+
+
+def cpu_baseline(w, rows):
+    """The fp64 oracle (untuned) on a bounded sample of the same workload: the
+    leading `rows` query rows of every head.  For causal attention those rows
+    see only keys < rows, so the sample is an exact sub-problem: its forward
+    (O, LSE) and backward (dQ, dK, dV restricted to those rows' pairs)."""
+    import oracle
+    import workloads as W
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        threads = os.cpu_count()
+    x = W.make_inputs(w)
+    R = min(rows, w.N)
+    sub = {n: x[n][:, :, :R] for n in ("q", "k", "v", "do")}
+    kl = None if x["key_lens"] is None else x["key_lens"].numpy()
+    t0 = time.perf_counter()
+    oracle.attn_fwd(sub["q"], sub["k"], sub["v"], w.scale, causal=w.causal, key_lens=kl)
+    oracle.attn_bwd(sub["q"], sub["k"], sub["v"], sub["do"], w.scale, causal=w.causal, key_lens=kl)
+    dt = time.perf_counter() - t0
+    pairs = oracle.valid_pair_count(R, w.B, w.H, w.causal, kl, None)
+    flops = 14.0 * w.d * pairs
+    return {"value": round(flops / dt / 1e12, 6), "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
+            "seconds": round(dt, 2),
+            "sample": f"fp64 numpy oracle fwd+bwd over the leading {R} causal query rows of all "
+                      f"{w.B * w.H} heads (an exact sub-problem: causal rows < {R} see only keys < {R}); "
+                      f"{pairs} valid pairs, 14*d FLOP each"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path (each (b, h) head is "
+              "independent; sharding over heads is described in DESIGN.md). Run with --gpus 1.",
+              file=sys.stderr)
+        sys.exit(2)
+    import torch
+    import workloads as W
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    ev = HipEvents()
+    w = W.WORKLOADS[args.workload]
+    r = time_workload(w, args.steps, args.warmup, ev)
+    fwd_flop = 4.0 * w.d * r["pairs"]
+    bwd_flop = 10.0 * w.d * r["pairs"]
+    med = lambda a: float(np.median(a))
+    step_ms = med(r["step_ms"])
+    fwd_ms, bwd_ms = med(r["fwd_ms"]), med(r["bwd_main_ms"])
+    peak = PEAK_TFLOPS[w.dtype]
+    total_tflops = (fwd_flop + bwd_flop) / (step_ms * 1e-3) / 1e12
+    fwd_tf = fwd_flop / (fwd_ms * 1e-3) / 1e12
+    bwd_tf = bwd_flop / (bwd_ms * 1e-3) / 1e12
+    # dominant kernel: whichever main kernel takes longer per step
+    avg_fwd = float(np.mean(r["fwd_ms"]))
+    avg_bwd = float(np.mean(r["bwd_main_ms"]))
+    if avg_bwd >= avg_fwd:
+        dom, dom_ms, dom_flop = "bwd_main_kernel", avg_bwd, bwd_flop
+    else:
+        dom, dom_ms, dom_flop = "fwd_kernel", avg_fwd, fwd_flop
+    achieved = dom_flop / (dom_ms * 1e-3) / 1e12
+    out = {
+        "metric": "attention fwd/bwd TFLOP/s (bf16, d=64/128, N 1K-16K), % of MFMA peak",
+        "value": round(total_tflops, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(step_ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic (seeded Gaussian Q, K, V, dO)",
+        "config": {"workload": f"{w.name}: B={w.B} H={w.H} N={w.N} d={w.d} {w.dtype}"
+                               f"{' causal' if w.causal else ''}", "B": w.B, "H": w.H, "N": w.N, "d": w.d,
+                   "causal": w.causal, "valid_pairs": r["pairs"]},
+        "pct_peak": round(100 * total_tflops / peak, 2),
+        "fwd_tflops": round(fwd_tf, 2), "fwd_pct_peak": round(100 * fwd_tf / peak, 2), "fwd_ms": round(fwd_ms, 4),
+        "bwd_tflops": round(bwd_tf, 2), "bwd_pct_peak": round(100 * bwd_tf / peak, 2),
+        "bwd_main_ms": round(bwd_ms, 4),
+        "roofline": {"bound": "mfma", "kernel": dom, "achieved": round(achieved, 2), "peak": peak,
+                     "unit": "TFLOP/s", "frac": round(achieved / peak, 4), "traffic": None,
+                     "avg_launch_ms": round(dom_ms, 4), "flop_per_launch": dom_flop},
+        "wall_s": round(r["wall_s"], 3),
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(w, args.cpu_rows)
+    print(json.dumps(out), flush=True)
+    if args.sweep:
+        for d in (64, 128):
+            for causal in (False, True):
+                for N in (1024, 2048, 4096, 8192, 16384):
+                    ws = W.Workload(f"sweep", 16384 // N, 16, N, d, "bf16", seed=7, causal=causal)
+                    rr = time_workload(ws, max(3, args.steps // 2), 2, ev)
+                    ff, bf = 4.0 * d * rr["pairs"], 10.0 * d * rr["pairs"]
+                    fm, bm = med(rr["fwd_ms"]), med(rr["bwd_main_ms"])
+                    print(json.dumps({"sweep": True, "B": ws.B, "H": 16, "N": N, "d": d, "causal": causal,
+                                      "fwd_ms": round(fm, 4), "bwd_main_ms": round(bm, 4),
+                                      "fwd_tflops": round(ff / fm / 1e9, 1), "bwd_tflops": round(bf / bm / 1e9, 1),
+                                      "fwd_pct": round(100 * ff / fm / 1e9 / peak, 2),
+                                      "bwd_pct": round(100 * bf / bm / 1e9 / peak, 2)}), flush=True)
+
+
+if __name__ == "__main__":
+    main()

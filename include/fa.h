@@ -1,0 +1,165 @@
+/*
+ * fa.h -- tiled exact attention (FlashAttention forward and backward) for
+ * AMD Instinct MI355X (gfx950), C ABI.
+ *
+ * The operation is exact attention per (batch b, head h):
+ *     S = scale * Q K^T,   P = softmax over keys of S with invalid scores at -inf,
+ *     O = (P o Z / (1 - p)) V
+ * computed tile by tile with an online softmax so that no N x N matrix ever
+ * reaches device memory (FlashAttention summary, xyznot.com/vi/paper/2205.14135,
+ * "Method": block scores S_ij, block statistics, merged (m, l), rescaled O_i;
+ * Self-Attention tutorial, infra-guide, sections 12.2-12.3 tiling and online
+ * softmax).  The backward pass recomputes S and P tile by tile from the saved
+ * log-sum-exp instead of storing P (summary, core ideas, recomputation;
+ * azimuth.plus explainer, "three ideas in one kernel", recomputation).
+ *
+ * Valid pair (i, j): (causal == 0 || j <= i) && j < key_len[b] &&
+ * block_mask[i / 128][j / 128] != 0.  Masks compose by AND (causal mask:
+ * tutorial section 10.2, lower triangle kept including the diagonal; block
+ * mask: summary, "Block-Sparse FlashAttention").  Tiles without a valid pair
+ * are skipped entirely: not loaded, not computed.
+ *
+ * Dropout (kernel-fused, after softmax and before the product with V;
+ * explainer, kernel fusion) uses Philox4x32-10 (Salmon et al., SC'11) with
+ *     counter = (j >> 2, i, b*H + h, (uint32) rng_offset),
+ *     key     = ((uint32) seed, (uint32)(seed >> 32)),
+ * 32-bit word (j & 3) = r, kept iff r >= min(floor(p * 2^32), 2^32 - 1) with p
+ * taken as float.  Kept entries are scaled by 1 / (1 - p).  The softmax
+ * statistics (and LSE) use the undropped P.
+ *
+ * Conventions for every entry point:
+ *  - Pointers are device memory owned by the caller (allocated by whatever
+ *    allocator the caller uses).  The library never allocates or frees
+ *    device memory and never synchronises; all work is enqueued on `stream`
+ *    in order and the call returns before it completes.
+ *  - Q, K, V, O, dO, dQ, dK, dV are contiguous [B][H][N][d] row-major with
+ *    16-byte aligned base addresses.  LSE and D are float [B][H][N].
+ *    Outputs must not alias inputs.
+ *  - LSE_i = ln sum_j exp(S_ij) over valid j (natural log, scaled scores);
+ *    a row without any valid key has O = 0, LSE = -inf and zero gradients.
+ *  - Validation is done on the host before any launch; on error nothing is
+ *    enqueued and nothing is written.  A failed launch returns FA_ERR_HIP
+ *    and fa_last_hip_error() names it.  Device-side faults are asynchronous
+ *    and surface at the caller's next synchronisation.  Device-resident
+ *    arguments (key_lens, block_mask) are not read on the host; key lengths
+ *    are clamped to [0, N] on the device.
+ *  - Supported: d in {64, 128}; dtype fp32, fp16, bf16; any N >= 1;
+ *    1 <= B, H <= 65535 with N*d < 2^31 and B*H*N < 2^31; 0 <= p < 1;
+ *    scale finite and > 0.
+ *  - Entry points are thread-safe and keep no state between calls apart from
+ *    a thread-local error string.
+ */
+#ifndef FA_H_
+#define FA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define FA_ABI_VERSION 1
+
+typedef enum { FA_F32 = 0, FA_F16 = 1, FA_BF16 = 2 } fa_dtype;
+
+typedef enum {
+    FA_OK = 0,
+    FA_ERR_NULL = -1,       /* a required pointer is NULL                          */
+    FA_ERR_SHAPE = -2,      /* B, H or N < 1, or the tensor is too large           */
+    FA_ERR_HEAD_DIM = -3,   /* d not in {64, 128}                                   */
+    FA_ERR_DTYPE = -4,      /* unknown dtype                                        */
+    FA_ERR_DROPOUT = -5,    /* p not in [0, 1) or not finite                        */
+    FA_ERR_SCALE = -6,      /* scale not finite or <= 0                             */
+    FA_ERR_ALIGN = -7,      /* a tensor base address is not 16-byte aligned         */
+    FA_ERR_WORKSPACE = -8,  /* workspace NULL, too small or misaligned              */
+    FA_ERR_HIP = -9,        /* a HIP launch failed (see fa_last_hip_error)          */
+    FA_ERR_OPTS = -10       /* opts->struct_size unknown or flags invalid           */
+} fa_status;
+
+enum {
+    FA_FLAG_RECORD_TILES = 1u << 0,  /* write the tile-visit map to opts->tile_visits */
+    FA_FLAG_REVERSE_KV = 1u << 1     /* forward only: walk key tiles last-to-first
+                                        (a check that the result does not depend on
+                                        the order of the online-softmax merges)   */
+};
+
+/* Optional settings; pass NULL for all defaults.  struct_size must be
+ * sizeof(fa_opts) of the caller's header (ABI versioning). */
+typedef struct {
+    uint32_t struct_size;
+    int32_t o_fp32;             /* nonzero: O is stored as fp32 (fwd writes it, bwd
+                                   reads it); 0 (and opts == NULL): O has the
+                                   input dtype                                   */
+    const int32_t* key_lens;    /* device int32[B]: keys j >= key_lens[b] are masked;
+                                   NULL = no key padding                          */
+    uint64_t rng_offset;        /* Philox counter word 3 (low 32 bits used)      */
+    uint32_t flags;             /* FA_FLAG_*                                      */
+    uint8_t* tile_visits;       /* device uint8[B][H][ceil(N/Br)][ceil(N/Bc)] with
+                                   (Br, Bc) from fa_tile_shape for the pass; every
+                                   entry is written (1 = tile visited) when
+                                   FA_FLAG_RECORD_TILES is set                  */
+    hipEvent_t main_begin;      /* profiling: when both are non-NULL they are    */
+    hipEvent_t main_end;        /* recorded on `stream` right before and right
+                                   after the pass's main kernel (the forward
+                                   kernel, or the backward's S/P-recomputing
+                                   kernel without its pre- and post-pass)       */
+} fa_opts;
+
+/* Forward pass.  Q, K, V: [B][H][N][d] of `dtype`.  O: [B][H][N][d] of
+ * `dtype`, or fp32 when opts->o_fp32 is set.  LSE: float [B][H][N].
+ * causal: nonzero for the lower-triangular mask.  dropout_p in [0, 1); seed
+ * selects the Philox key.  block_mask: device uint8[ceil(N/128)][ceil(N/128)],
+ * shared by all (b, h), nonzero = compute; NULL = dense. */
+fa_status fa_fwd(const void* Q, const void* K, const void* V, void* O, float* LSE,
+                 int32_t B, int32_t H, int32_t N, int32_t d, fa_dtype dtype,
+                 float scale, int32_t causal, float dropout_p, uint64_t seed,
+                 const uint8_t* block_mask, const fa_opts* opts, hipStream_t stream);
+
+/* Bytes of device workspace fa_bwd needs: an fp32 dQ accumulator
+ * [B][H][N][d] followed by D = rowsum(dO o O) float [B][H][N], each part
+ * 256-byte aligned.  Returns 0 for invalid sizes. */
+size_t fa_bwd_workspace_bytes(int32_t B, int32_t H, int32_t N, int32_t d);
+
+/* Backward pass.  Q, K, V, dO: [B][H][N][d] of `dtype`; O as the forward
+ * wrote it (fp32 if opts->o_fp32, else `dtype`); LSE from the forward.  dQ, dK, dV:
+ * [B][H][N][d] of `dtype`.  All of scale, causal, dropout_p, seed,
+ * block_mask, key_lens and rng_offset must equal the forward call's; a
+ * mismatch gives wrong gradients and is not detected.  workspace: device
+ * memory of at least fa_bwd_workspace_bytes(B, H, N, d) bytes, 256-byte
+ * aligned; its contents on return are unspecified.  Gradients of rows and
+ * keys that take part in no valid pair are zero. */
+fa_status fa_bwd(const void* Q, const void* K, const void* V, const void* O,
+                 const void* dO, const float* LSE, void* dQ, void* dK, void* dV,
+                 int32_t B, int32_t H, int32_t N, int32_t d, fa_dtype dtype,
+                 float scale, int32_t causal, float dropout_p, uint64_t seed,
+                 const uint8_t* block_mask, const fa_opts* opts,
+                 void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* Dropout keep bits of every element, for tests: keep is device
+ * uint8[B][H][N][N], 1 = kept.  Uses the same device generator as the
+ * attention kernels.  O(N^2) memory: test sizes only. */
+fa_status fa_dropout_keep_mask(uint64_t seed, uint64_t rng_offset, float dropout_p,
+                               int32_t B, int32_t H, int32_t N, uint8_t* keep,
+                               hipStream_t stream);
+
+/* Tile shape (rows Br of queries, columns Bc of keys) the given pass
+ * (0 = forward, 1 = backward) uses for head dim d and dtype; these index
+ * the tile-visit map.  Both divide 128, so a tile lies inside one block of
+ * the 128 x 128 block mask. */
+fa_status fa_tile_shape(int32_t d, fa_dtype dtype, int32_t pass, int32_t* Br, int32_t* Bc);
+
+/* Static description of a status code. */
+const char* fa_status_string(fa_status s);
+
+/* Thread-local text of the last HIP error behind FA_ERR_HIP ("" if none). */
+const char* fa_last_hip_error(void);
+
+int32_t fa_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FA_H_ */

@@ -1,0 +1,163 @@
+"""Tiled exact attention (FlashAttention forward and backward) for MI355X.
+
+Thin binding over the C ABI in include/fa.h: it checks tensor placement and
+layout, allocates outputs with torch on the inputs' device and passes raw
+device pointers plus torch's current HIP stream.  Every step of the
+computation runs in the HIP kernels of libfa.so; when the library is missing
+the calls raise.
+
+    o, lse = fwd(q, k, v, causal=True)
+    dq, dk, dv = bwd(q, k, v, o, do, lse, causal=True)
+"""
+
+from __future__ import annotations
+
+import ctypes
+import math
+from typing import Optional
+
+import torch
+
+from . import _lib
+from ._lib import FaOpts, check
+
+__all__ = ["fwd", "bwd", "dropout_keep_mask", "tile_shape", "bwd_workspace_bytes", "abi_version"]
+
+_DT = {torch.float32: _lib.FA_F32, torch.float16: _lib.FA_F16, torch.bfloat16: _lib.FA_BF16}
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype not in _DT:
+        raise TypeError(f"unsupported dtype {t.dtype}")
+    return _DT[t.dtype]
+
+
+def _check_qkv(*ts: torch.Tensor):
+    ref = ts[0]
+    if ref.dim() != 4:
+        raise ValueError("expected [B, H, N, d] tensors")
+    for t in ts:
+        if not t.is_cuda:
+            raise ValueError("tensors must be on a GPU device")
+        if t.shape != ref.shape or t.dtype != ref.dtype or t.device != ref.device:
+            raise ValueError("q, k, v (and dO) must share shape, dtype and device")
+        if not t.is_contiguous():
+            raise ValueError("tensors must be contiguous [B, H, N, d]")
+
+
+def _stream(dev: torch.device) -> ctypes.c_void_p:
+    return ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
+
+
+def _opts(B, H, N, d, pass_, key_lens, rng_offset, o_fp32, record_tiles, reverse_kv, device, dtype_code,
+          events=None):
+    opts = FaOpts()
+    if events is not None:
+        opts.main_begin, opts.main_end = events
+    opts.struct_size = ctypes.sizeof(FaOpts)
+    opts.o_fp32 = 1 if o_fp32 else 0
+    keep = []
+    if key_lens is not None:
+        kl = key_lens.to(device=device, dtype=torch.int32).contiguous()
+        keep.append(kl)
+        opts.key_lens = kl.data_ptr()
+    opts.rng_offset = int(rng_offset)
+    tiles = None
+    if record_tiles:
+        br, bc = tile_shape(d, dtype_code, pass_)
+        tiles = torch.full((B, H, -(-N // br), -(-N // bc)), 7, dtype=torch.uint8, device=device)
+        opts.tile_visits = tiles.data_ptr()
+        opts.flags |= _lib.FA_FLAG_RECORD_TILES
+    if reverse_kv:
+        opts.flags |= _lib.FA_FLAG_REVERSE_KV
+    return opts, keep, tiles
+
+
+def _mask_ptr(block_mask, device, N):
+    if block_mask is None:
+        return None, None
+    T = -(-N // 128)
+    bm = block_mask.to(device=device, dtype=torch.uint8).contiguous()
+    if bm.shape != (T, T):
+        raise ValueError(f"block_mask must be [{T}, {T}]")
+    return bm, bm.data_ptr()
+
+
+def fwd(q, k, v, *, causal=False, dropout_p=0.0, seed=0, rng_offset=0, key_lens=None, block_mask=None,
+        scale: Optional[float] = None, o_fp32=False, record_tiles=False, reverse_kv=False,
+        out=None, lse=None, events=None):
+    """Forward pass.  Returns (O, LSE) or (O, LSE, tile_visits) when
+    record_tiles is set.  `events` = (hipEvent_t, hipEvent_t) raw handles
+    recorded around the kernel (profiling).  O is fp32 when o_fp32, else q's dtype; LSE is fp32
+    [B, H, N]."""
+    _check_qkv(q, k, v)
+    B, H, N, d = q.shape
+    scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    dt = _dtype_code(q)
+    o = out if out is not None else torch.empty(q.shape, dtype=torch.float32 if o_fp32 else q.dtype,
+                                                device=q.device)
+    l = lse if lse is not None else torch.empty((B, H, N), dtype=torch.float32, device=q.device)
+    opts, keep, tiles = _opts(B, H, N, d, 0, key_lens, rng_offset, o_fp32, record_tiles, reverse_kv,
+                              q.device, dt, events)
+    bm, bmp = _mask_ptr(block_mask, q.device, N)
+    code = _lib.lib().fa_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), l.data_ptr(),
+                             B, H, N, d, dt, scale, 1 if causal else 0, float(dropout_p), int(seed),
+                             bmp, ctypes.byref(opts), _stream(q.device))
+    check(code, "fa_fwd")
+    del keep, bm
+    return (o, l, tiles) if record_tiles else (o, l)
+
+
+def bwd_workspace_bytes(B, H, N, d) -> int:
+    return int(_lib.lib().fa_bwd_workspace_bytes(B, H, N, d))
+
+
+def bwd(q, k, v, o, do, lse, *, causal=False, dropout_p=0.0, seed=0, rng_offset=0, key_lens=None,
+        block_mask=None, scale: Optional[float] = None, record_tiles=False, workspace=None, grads=None,
+        events=None):
+    """Backward pass.  Returns (dQ, dK, dV) [+ tile_visits], in q's dtype.
+    O may be fp32 (if the forward wrote it so) or q's dtype."""
+    _check_qkv(q, k, v, do)
+    B, H, N, d = q.shape
+    scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    dt = _dtype_code(q)
+    if o.shape != q.shape or not o.is_contiguous() or o.dtype not in (q.dtype, torch.float32):
+        raise ValueError("O must be contiguous [B, H, N, d] of q's dtype or fp32")
+    if lse.shape != (B, H, N) or lse.dtype != torch.float32 or not lse.is_contiguous():
+        raise ValueError("LSE must be contiguous fp32 [B, H, N]")
+    o_fp32 = o.dtype == torch.float32 and q.dtype != torch.float32
+    if grads is None:
+        dq, dk, dv = (torch.empty_like(q) for _ in range(3))
+    else:
+        dq, dk, dv = grads
+    need = bwd_workspace_bytes(B, H, N, d)
+    ws = workspace if workspace is not None else torch.empty(need, dtype=torch.uint8, device=q.device)
+    opts, keep, tiles = _opts(B, H, N, d, 1, key_lens, rng_offset, o_fp32, record_tiles, False, q.device, dt,
+                              events)
+    bm, bmp = _mask_ptr(block_mask, q.device, N)
+    code = _lib.lib().fa_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), do.data_ptr(),
+                             lse.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), B, H, N, d, dt,
+                             scale, 1 if causal else 0, float(dropout_p), int(seed), bmp, ctypes.byref(opts),
+                             ws.data_ptr(), ws.numel(), _stream(q.device))
+    check(code, "fa_bwd")
+    del keep, bm
+    return (dq, dk, dv, tiles) if record_tiles else (dq, dk, dv)
+
+
+def dropout_keep_mask(seed, rng_offset, p, B, H, N, device="cuda"):
+    """uint8 [B, H, N, N] keep bits from the device generator (tests only)."""
+    keep = torch.empty((B, H, N, N), dtype=torch.uint8, device=device)
+    code = _lib.lib().fa_dropout_keep_mask(int(seed), int(rng_offset), float(p), B, H, N, keep.data_ptr(),
+                                           _stream(keep.device))
+    check(code, "fa_dropout_keep_mask")
+    return keep
+
+
+def tile_shape(d: int, dtype_code: int, pass_: int):
+    br, bc = ctypes.c_int32(), ctypes.c_int32()
+    check(_lib.lib().fa_tile_shape(d, dtype_code, pass_, ctypes.byref(br), ctypes.byref(bc)), "fa_tile_shape")
+    return br.value, bc.value
+
+
+def abi_version() -> int:
+    return int(_lib.lib().fa_abi_version())

@@ -1,0 +1,152 @@
+// Device helpers for the gfx950 attention kernels: MFMA operand traits,
+// swizzled LDS tile addressing, the Philox4x32-10 generator and small
+// wave-level utilities.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace fa {
+
+typedef __bf16 bf16;
+typedef _Float16 f16;
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+constexpr int WAVE = 64;
+
+
+// ---------------------------------------------------------------------------
+// MFMA 32x32 traits.  For every 32x32xK instruction used here a lane l holds
+//   A[m = l % 32][k = (l / 32) * E + e]      e = 0..E-1
+//   B[k = (l / 32) * E + e][n = l % 32]
+//   C[m = 8 * (r / 4) + 4 * (l / 32) + r % 4][n = l % 32]   r = 0..15
+// with K = 2E.  16-bit inputs use the gfx950 32x32x16 shapes (E = 8), fp32
+// inputs the 32x32x2 fp32 shape (E = 1).
+template <class T> struct Mma;
+
+template <> struct Mma<bf16> {
+    static constexpr int E = 8;
+    typedef bf16x8 frag;
+    __device__ static inline f32x16 mma(frag a, frag b, f32x16 c) {
+        return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+    }
+};
+template <> struct Mma<f16> {
+    static constexpr int E = 8;
+    typedef f16x8 frag;
+    __device__ static inline f32x16 mma(frag a, frag b, f32x16 c) {
+        return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
+    }
+};
+template <> struct Mma<float> {
+    static constexpr int E = 1;
+    typedef float frag;
+    __device__ static inline f32x16 mma(frag a, frag b, f32x16 c) {
+        return __builtin_amdgcn_mfma_f32_32x32x2f32(a, b, c, 0, 0, 0);
+    }
+};
+
+// Type used for the probability operand of P*V (and for V in LDS).  For bf16
+// inputs P is rounded to fp16 (11-bit significand) instead of bf16 (8 bits)
+// and V is converted bf16 -> fp16 while it is staged; the conversion is exact
+// for |v| in [2^-14, 65504] and loses at most 2^-25 absolute below.
+template <class T> struct PvType { typedef T type; };
+template <> struct PvType<bf16> { typedef f16 type; };
+
+template <class T> __device__ inline float to_f32(T x) { return (float)x; }
+template <class T> __device__ inline T from_f32(float x) { return (T)x; }
+
+// fragment <-> 16-byte (or 4-byte) memory
+template <class T> __device__ inline typename Mma<T>::frag load_frag(const T* p) {
+    if constexpr (Mma<T>::E == 8) {
+        return *reinterpret_cast<const typename Mma<T>::frag*>(p);
+    } else {
+        return *p;
+    }
+}
+
+template <class T> __device__ inline typename Mma<T>::frag zero_frag() {
+    typename Mma<T>::frag z;
+    if constexpr (Mma<T>::E == 8) {
+        for (int e = 0; e < 8; ++e) z[e] = (T)0.0f;
+    } else {
+        z = 0.0f;
+    }
+    return z;
+}
+
+__device__ inline f32x16 zero16() {
+    f32x16 z;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) z[i] = 0.0f;
+    return z;
+}
+
+// ---------------------------------------------------------------------------
+// Row-major LDS tile of ROWS x COLS elements of T, addressed in 16-byte units
+// with an XOR swizzle of the unit index by the row so that lanes reading the
+// same column of consecutive rows fall in different banks.
+template <class T, int COLS>
+struct Swz {
+    static constexpr int EPU = 16 / (int)sizeof(T);   // elements per 16-byte unit
+    static constexpr int U = COLS / EPU;              // units per row
+    static_assert(COLS % EPU == 0, "row must be a whole number of 16-byte units");
+    __device__ static inline int f(int row) {
+        if constexpr (U >= 8) return (row ^ (row >> 3)) & 7;
+        else if constexpr (U == 4) return ((row >> 1) ^ (row >> 3)) & 3;
+        else if constexpr (U == 2) return ((row >> 2) ^ (row >> 3)) & 1;
+        else return 0;
+    }
+    // element offset of (row, col); a run of up to EPU elements starting at a
+    // col that is a multiple of the run length stays contiguous.
+    __device__ static inline int off(int row, int col) {
+        const int u = col / EPU;
+        return row * COLS + ((u ^ f(row)) * EPU) + (col % EPU);
+    }
+};
+
+// ---------------------------------------------------------------------------
+// Philox4x32-10 (Salmon, Moraes, Dror, Shaw, SC'11): ten rounds of two
+// 32x32->64-bit products on counter words 0 and 2, the key added into the
+// high halves, and the key advanced by the two Weyl increments per round.
+struct u32q { uint32_t x, y, z, w; };
+
+__device__ inline u32q philox4x32_10(uint32_t c0, uint32_t c1, uint32_t c2, uint32_t c3,
+                                     uint32_t k0, uint32_t k1) {
+#pragma unroll
+    for (int r = 0; r < 10; ++r) {
+        const uint32_t lo0 = 0xD2511F53u * c0;
+        const uint32_t hi0 = __umulhi(0xD2511F53u, c0);
+        const uint32_t lo1 = 0xCD9E8D57u * c2;
+        const uint32_t hi1 = __umulhi(0xCD9E8D57u, c2);
+        const uint32_t n0 = hi1 ^ c1 ^ k0;
+        const uint32_t n2 = hi0 ^ c3 ^ k1;
+        c0 = n0; c1 = lo1; c2 = n2; c3 = lo0;
+        k0 += 0x9E3779B9u;
+        k1 += 0xBB67AE85u;
+    }
+    return {c0, c1, c2, c3};
+}
+
+// Keep bits of the four consecutive keys 4*g .. 4*g+3 of query row i, as a
+// 4-bit mask (bit e = key 4*g + e).
+__device__ inline uint32_t keep4(uint32_t g, uint32_t i, uint32_t bh, uint32_t off,
+                                 uint32_t k0, uint32_t k1, uint32_t thr) {
+    const u32q r = philox4x32_10(g, i, bh, off, k0, k1);
+    return (uint32_t)(r.x >= thr) | ((uint32_t)(r.y >= thr) << 1) |
+           ((uint32_t)(r.z >= thr) << 2) | ((uint32_t)(r.w >= thr) << 3);
+}
+
+// ---------------------------------------------------------------------------
+__device__ inline float wave_xor32(float v) { return __shfl_xor(v, 32, WAVE); }
+
+__device__ inline float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+}  // namespace fa

@@ -1,0 +1,301 @@
+// Forward pass of tiled exact attention for gfx950.
+//
+// One workgroup (4 waves) owns BR = 128 query rows of one (b, h); each wave
+// owns 32 of them.  The workgroup walks the key/value tiles of BC = 64 keys
+// that hold at least one valid pair (FlashAttention summary, xyznot.com,
+// "Method"; the query-outer / key-inner loop order of the tutorial's section
+// 12.2 pseudocode), staging K_j and V_j^T in LDS, and per tile:
+//   S^T = K_j Q_i^T          MFMA, fp32 accumulation, one query per lane column
+//   masks on edge tiles      causal j > i, key padding j >= len_b, N tail
+//   m_new = max(m, rowmax)   lane-local max over 16 keys + one cross-half swap
+//   P = exp2(S*scale*log2e - m_new),  l = e^{m - m_new} l + rowsum(P)
+//   dropout keep bits        Philox4x32-10, one call per 4 keys
+//   O^T = e^{m - m_new} O^T + V_j^T P^T     MFMA
+// and finally writes O = O^T / l and LSE = m + ln l (incremental softmax of
+// the summary's "Method" steps 2-4 with the normalisation deferred to the end,
+// as in the explainer's simplified forward, azimuth.plus).
+//
+// Layout choices (MI355X-specific, not from the pages):
+//  * S is computed transposed (keys on MFMA rows, queries on columns) so that
+//    every lane holds one query row: the row max needs one cross-half swap,
+//    the row sum none until the epilogue, and the per-row rescale of O is a
+//    lane-local multiply.
+//  * K rows are stored in LDS in MFMA row order: MFMA row m takes key
+//    16*((m/4)%2) + 4*(m/8) + m%4, so that lane (l/32) of the accumulator
+//    holds 16 *consecutive* keys in registers r = 0..15.  Those 16 values are
+//    then exactly the B operand of the P*V product (8 consecutive keys per
+//    MFMA per lane half), with no register shuffles.
+//  * V is stored transposed (d rows, key columns) so the A operand of V^T P^T
+//    is one 16-byte LDS read per MFMA.
+#include "fa_device.hpp"
+#include "fa_internal.hpp"
+
+namespace fa {
+
+namespace {
+
+template <class TV> __device__ inline void store4(TV* p, float a, float b, float c, float d);
+template <> __device__ inline void store4<f16>(f16* p, float a, float b, float c, float d) {
+    f16x4 w = {(f16)a, (f16)b, (f16)c, (f16)d};
+    *reinterpret_cast<f16x4*>(p) = w;
+}
+template <> __device__ inline void store4<bf16>(bf16* p, float a, float b, float c, float d) {
+    bf16x4 w = {(bf16)a, (bf16)b, (bf16)c, (bf16)d};
+    *reinterpret_cast<bf16x4*>(p) = w;
+}
+template <> __device__ inline void store4<float>(float* p, float a, float b, float c, float d) {
+    f32x4 w = {a, b, c, d};
+    *reinterpret_cast<f32x4*>(p) = w;
+}
+
+template <class TV> __device__ inline typename Mma<TV>::frag pack_p(const float* p) {
+    if constexpr (Mma<TV>::E == 8) {
+        typename Mma<TV>::frag f;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) f[e] = (TV)p[e];
+        return f;
+    } else {
+        return p[0];
+    }
+}
+
+// MFMA row slot of key r within a 32-key block (see the file comment).
+__device__ inline int key_slot(int r) {
+    return (r & ~31) | (((r >> 2) & 3) * 8 + ((r >> 4) & 1) * 4 + (r & 3));
+}
+
+}  // namespace
+
+template <class T, int D, bool DROP>
+__global__ __launch_bounds__(256, 2) void fwd_kernel(FwdArgs a) {
+    typedef typename PvType<T>::type TV;
+    typedef Mma<T> MS;
+    typedef Mma<TV> MV;
+    constexpr int E = MS::E;
+    constexpr int EV = MV::E;
+    constexpr int BR = FWD_BR, BC = FWD_BC;
+    constexpr int KS = D / (2 * E);     // MFMA steps over d in S^T
+    constexpr int KB = BC / 32;         // 32-key blocks per tile
+    constexpr int DB = D / 32;          // 32-wide column blocks of O
+    constexpr int PU = 16 / EV;         // P*V MFMAs per 32-key block
+    constexpr int EPU = 16 / (int)sizeof(T);
+    typedef Swz<T, D> LK;
+    typedef Swz<TV, BC> LV;
+
+    __shared__ __attribute__((aligned(16))) T sK[BC * D];
+    __shared__ __attribute__((aligned(16))) TV sV[D * BC];
+
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int hl = lane >> 5, ln = lane & 31;
+    const int N = a.N, H = a.H;
+    const int Tr = (N + BR - 1) / BR, Tc = (N + BC - 1) / BC;
+    const int b = blockIdx.z, h = blockIdx.y;
+    // causal: heaviest query tiles (most key tiles) are launched first
+    const int it = a.mask.causal ? (Tr - 1 - (int)blockIdx.x) : (int)blockIdx.x;
+    const int q0 = it * BR, qw0 = q0 + wave * 32;
+    const size_t bh = (size_t)b * H + h;
+    const size_t hoff = bh * (size_t)N * D;
+    const T* __restrict__ Qg = (const T*)a.q + hoff;
+    const T* __restrict__ Kg = (const T*)a.k + hoff;
+    const T* __restrict__ Vg = (const T*)a.v + hoff;
+
+    int kend = N;
+    if (a.mask.key_lens) {
+        const int L = a.mask.key_lens[b];
+        kend = L < 0 ? 0 : (L > N ? N : L);
+    }
+    int j_end = min(Tc, (kend + BC - 1) / BC);
+    if (a.mask.causal) j_end = min(j_end, (min(q0 + BR, N) - 1) / BC + 1);
+
+    uint8_t* vis = a.tile_visits ? a.tile_visits + (bh * Tr + it) * (size_t)Tc : nullptr;
+    if (vis)
+        for (int j = j_end + tid; j < Tc; j += 256) vis[j] = 0;
+
+    // Q_i^T as the B operand: lane column = query qw0 + ln, rows = d
+    const int qrow = qw0 + ln;
+    typename MS::frag qf[KS];
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks)
+        qf[ks] = (qrow < N) ? load_frag<T>(Qg + (size_t)qrow * D + ks * 2 * E + hl * E)
+                            : zero_frag<T>();
+
+    float m_run = -INFINITY, l_run = 0.0f;
+    f32x16 oacc[DB];
+#pragma unroll
+    for (int db = 0; db < DB; ++db) oacc[db] = zero16();
+
+    const float c = a.scale_log2;
+    const int causal = a.mask.causal;
+    const uint8_t* bmask = a.mask.block_mask ? a.mask.block_mask + (size_t)(q0 / MASK_TILE) * a.mask.mask_T
+                                             : nullptr;
+
+    for (int jj = 0; jj < j_end; ++jj) {
+        const int j = a.reverse_kv ? (j_end - 1 - jj) : jj;
+        const int kv0 = j * BC;
+        if (bmask && bmask[kv0 / MASK_TILE] == 0) {
+            if (vis && tid == 0) vis[j] = 0;
+            continue;
+        }
+        if (vis && tid == 0) vis[j] = 1;
+
+        __syncthreads();   // previous tile fully consumed
+        // ---- stage K_j (MFMA row order) and V_j^T into LDS
+        {
+            constexpr int UPR = D / EPU;
+            for (int u = tid; u < BC * UPR; u += 256) {
+                const int r = u / UPR, cu = u % UPR;
+                const int key = kv0 + r;
+                u32x4 val = {0u, 0u, 0u, 0u};
+                if (key < N) val = *reinterpret_cast<const u32x4*>(Kg + (size_t)key * D + cu * EPU);
+                *reinterpret_cast<u32x4*>(sK + LK::off(key_slot(r), cu * EPU)) = val;
+            }
+            constexpr int DC = D / EPU;                 // 16-byte column chunks per row
+            for (int t = tid; t < (BC / 4) * DC; t += 256) {
+                const int dc = t % DC, kg = t / DC;
+                T x[4][EPU];
+#pragma unroll
+                for (int kk = 0; kk < 4; ++kk) {
+                    const int key = kv0 + kg * 4 + kk;
+                    u32x4 val = {0u, 0u, 0u, 0u};
+                    if (key < N) val = *reinterpret_cast<const u32x4*>(Vg + (size_t)key * D + dc * EPU);
+                    *reinterpret_cast<u32x4*>(&x[kk][0]) = val;
+                }
+#pragma unroll
+                for (int dd = 0; dd < EPU; ++dd)
+                    store4<TV>(sV + LV::off(dc * EPU + dd, kg * 4), to_f32(x[0][dd]), to_f32(x[1][dd]),
+                               to_f32(x[2][dd]), to_f32(x[3][dd]));
+            }
+        }
+        __syncthreads();
+
+        if (causal && kv0 > qw0 + 31) continue;   // no valid key for this wave's rows
+
+        // ---- S^T = K_j Q^T
+        f32x16 s[KB];
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb) {
+            s[kb] = zero16();
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks) {
+                const typename MS::frag ak = load_frag<T>(sK + LK::off(kb * 32 + ln, ks * 2 * E + hl * E));
+                s[kb] = MS::mma(ak, qf[ks], s[kb]);
+            }
+        }
+        // ---- element masks on edge tiles
+        const bool edge = (kv0 + BC > kend) || (causal && kv0 + BC - 1 > qw0);
+        if (edge) {
+#pragma unroll
+            for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const int key = kv0 + kb * 32 + hl * 16 + r;
+                    if (key >= kend || (causal && key > qrow)) s[kb][r] = -INFINITY;
+                }
+        }
+        // ---- online softmax
+        float mx = -INFINITY;
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
+        mx = fmaxf(mx, wave_xor32(mx));
+        const float m_new = fmaxf(m_run, mx * c);
+        const float m_ref = (m_new == -INFINITY) ? 0.0f : m_new;
+        const float alpha = fast_exp2(m_run - m_ref);
+        m_run = m_new;
+        l_run *= alpha;
+#pragma unroll
+        for (int db = 0; db < DB; ++db)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
+
+        float p[KB][16];
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                p[kb][r] = fast_exp2(fmaf(s[kb][r], c, -m_ref));
+                l_run += p[kb][r];
+            }
+        if constexpr (DROP) {
+            const uint32_t g0 = (uint32_t)(kv0 + hl * 16) >> 2;
+#pragma unroll
+            for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+                for (int g = 0; g < 4; ++g) {
+                    const uint32_t bits = keep4(g0 + kb * 8 + g, (uint32_t)qrow, (uint32_t)bh, a.drop.off,
+                                                a.drop.k0, a.drop.k1, a.drop.thr);
+#pragma unroll
+                    for (int e = 0; e < 4; ++e)
+                        if (!((bits >> e) & 1u)) p[kb][g * 4 + e] = 0.0f;
+                }
+        }
+        // ---- O^T += V_j^T P^T
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+            for (int u = 0; u < PU; ++u) {
+                const typename MV::frag bp = pack_p<TV>(&p[kb][u * EV]);
+#pragma unroll
+                for (int db = 0; db < DB; ++db) {
+                    const typename MV::frag av =
+                        load_frag<TV>(sV + LV::off(db * 32 + ln, kb * 32 + hl * 16 + u * EV));
+                    oacc[db] = MV::mma(av, bp, oacc[db]);
+                }
+            }
+    }
+
+    // ---- epilogue: O = O^T / l, LSE = m + ln l
+    const float l_tot = l_run + wave_xor32(l_run);
+    float inv = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
+    if constexpr (DROP) inv *= a.drop.keep_scale;
+    if (qrow < N) {
+        const size_t orow = hoff + (size_t)qrow * D;
+#pragma unroll
+        for (int db = 0; db < DB; ++db)
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                const int dcol = db * 32 + 8 * g + 4 * hl;
+                const float v0 = oacc[db][4 * g] * inv, v1 = oacc[db][4 * g + 1] * inv;
+                const float v2 = oacc[db][4 * g + 2] * inv, v3 = oacc[db][4 * g + 3] * inv;
+                if (a.o_f32) store4<float>((float*)a.o + orow + dcol, v0, v1, v2, v3);
+                else store4<T>((T*)a.o + orow + dcol, v0, v1, v2, v3);
+            }
+        if (hl == 0)
+            a.lse[bh * N + qrow] = l_tot > 0.0f ? (m_run + log2f(l_tot)) * 0.69314718055994530942f
+                                                : -INFINITY;
+    }
+}
+
+namespace {
+template <class T, int D, bool DROP>
+hipError_t launch_t(const FwdArgs& a, hipStream_t s) {
+    dim3 grid((a.N + FWD_BR - 1) / FWD_BR, a.H, a.B);
+    FwdArgs copy = a;
+    void* args[] = {(void*)&copy};
+    if (a.ev_begin) {
+        const hipError_t e = hipEventRecord(a.ev_begin, s);
+        if (e != hipSuccess) return e;
+    }
+    const hipError_t e = hipLaunchKernel((const void*)&fwd_kernel<T, D, DROP>, grid, dim3(256), args, 0, s);
+    if (e != hipSuccess || !a.ev_end) return e;
+    return hipEventRecord(a.ev_end, s);
+}
+
+template <class T>
+hipError_t launch_d(const FwdArgs& a, int d, hipStream_t s) {
+    const bool drop = a.drop.thr != 0;
+    if (d == 64) return drop ? launch_t<T, 64, true>(a, s) : launch_t<T, 64, false>(a, s);
+    return drop ? launch_t<T, 128, true>(a, s) : launch_t<T, 128, false>(a, s);
+}
+}  // namespace
+
+hipError_t launch_fwd(const FwdArgs& a, fa_dtype dt, int d, hipStream_t s) {
+    switch (dt) {
+        case FA_BF16: return launch_d<bf16>(a, d, s);
+        case FA_F16: return launch_d<f16>(a, d, s);
+        default: return launch_d<float>(a, d, s);
+    }
+}
+
+}  // namespace fa

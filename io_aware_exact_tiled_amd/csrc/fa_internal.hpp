@@ -1,0 +1,79 @@
+// Host-side view of the kernels: argument blocks and launchers shared by the
+// C-ABI layer (fa_api.cpp) and the kernel translation units.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "../../include/fa.h"
+
+namespace fa {
+
+// Tile shapes.  Forward: a workgroup owns BR query rows (4 waves x 32) and
+// walks key tiles of BC.  Backward: a workgroup owns BC_B keys (4 waves x 32)
+// and walks query tiles of BR_B.  All divide the 128-token block-mask tile.
+constexpr int MASK_TILE = 128;   // block-mask granularity (tokens)
+constexpr int FWD_BR = 128;
+constexpr int FWD_BC = 64;
+constexpr int BWD_BR = 32;
+constexpr int BWD_BC = 128;
+
+struct MaskArgs {
+    int causal;
+    const int32_t* key_lens;    // device [B] or null
+    const uint8_t* block_mask;  // device [T][T] or null
+    int mask_T;                 // ceil(N / 128)
+};
+
+struct DropArgs {
+    uint32_t thr;         // drop iff r < thr; 0 = no dropout
+    float keep_scale;     // 1 / (1 - p)
+    uint32_t k0, k1;      // Philox key (seed low, high)
+    uint32_t off;         // Philox counter word 3
+};
+
+struct FwdArgs {
+    const void* q;
+    const void* k;
+    const void* v;
+    void* o;
+    float* lse;
+    int B, H, N;
+    float scale_log2;     // scale * log2(e)
+    int o_f32;            // O stored as fp32 instead of the input dtype
+    MaskArgs mask;
+    DropArgs drop;
+    uint8_t* tile_visits; // null unless recording
+    int reverse_kv;
+    hipEvent_t ev_begin, ev_end;   // optional profiling events around the kernel
+};
+
+struct BwdArgs {
+    const void* q;
+    const void* k;
+    const void* v;
+    const void* o;
+    const void* dout;
+    const float* lse;
+    void* dq;
+    void* dk;
+    void* dv;
+    float* dq_acc;        // fp32 [B][H][N][d] workspace
+    float* delta;         // fp32 [B][H][N] workspace: D = rowsum(dO o O)
+    int B, H, N;
+    float scale;
+    float scale_log2;
+    int o_f32;
+    MaskArgs mask;
+    DropArgs drop;
+    uint8_t* tile_visits;
+    hipEvent_t ev_begin, ev_end;   // optional profiling events around bwd_main
+};
+
+hipError_t launch_fwd(const FwdArgs& a, fa_dtype dt, int d, hipStream_t s);
+hipError_t launch_bwd(const BwdArgs& a, fa_dtype dt, int d, hipStream_t s);
+hipError_t launch_keep_mask(uint32_t k0, uint32_t k1, uint32_t off, uint32_t thr,
+                            int B, int H, int N, uint8_t* keep, hipStream_t s);
+
+}  // namespace fa

@@ -95,34 +95,39 @@ def _rows_scores(q, k, rows, scale):
     return scale * (q[rows] @ k.T)
 
 
+def _pairs(B, H, pairs):
+    return pairs if pairs is not None else [(b, h) for b in range(B) for h in range(H)]
+
+
 def attn_fwd(q, k, v, scale, causal=False, key_lens=None, block_mask=None,
-             dropout_p=0.0, seed=0, rng_offset=0, rows=None, chunk=512):
-    """O [B,H,R,d] and LSE [B,H,R] for query rows `rows` (default: all)."""
+             dropout_p=0.0, seed=0, rng_offset=0, rows=None, chunk=512, pairs=None):
+    """O [B,H,R,d] and LSE [B,H,R] for query rows `rows` (default: all).
+    `pairs` restricts the work to a list of (b, h) (other heads stay 0)."""
     q, k, v = as_f64(q), as_f64(k), as_f64(v)
     B, H, N, d = q.shape
     sc = scale_f32(scale)
     rows = np.arange(N) if rows is None else np.asarray(rows)
     O = np.zeros((B, H, len(rows), v.shape[-1]))
     LSE = np.zeros((B, H, len(rows)))
-    for b in range(B):
+    for b, h in _pairs(B, H, pairs):
         kl = _key_len(key_lens, b)
-        for h in range(H):
-            for s in range(0, len(rows), chunk):
-                r = rows[s:s + chunk]
-                S = _rows_scores(q[b, h], k[b, h], r, sc)
-                A = validity(r, N, causal, kl, block_mask)
-                P, lse, _, _ = safe_softmax(S, A)
-                if dropout_p > 0.0:
-                    Z = keep_mask(seed, rng_offset, dropout_p, b, h, H, r, np.arange(N))
-                    P = P * Z / (1.0 - float(np.float32(dropout_p)))
-                O[b, h, s:s + chunk] = P @ v[b, h]
-                LSE[b, h, s:s + chunk] = lse
+        for s in range(0, len(rows), chunk):
+            r = rows[s:s + chunk]
+            S = _rows_scores(q[b, h], k[b, h], r, sc)
+            A = validity(r, N, causal, kl, block_mask)
+            P, lse, _, _ = safe_softmax(S, A)
+            if dropout_p > 0.0:
+                Z = keep_mask(seed, rng_offset, dropout_p, b, h, H, r, np.arange(N))
+                P = P * Z / (1.0 - float(np.float32(dropout_p)))
+            O[b, h, s:s + chunk] = P @ v[b, h]
+            LSE[b, h, s:s + chunk] = lse
     return O, LSE
 
 
 def attn_bwd(q, k, v, do, scale, causal=False, key_lens=None, block_mask=None,
-             dropout_p=0.0, seed=0, rng_offset=0, chunk=512):
-    """dQ, dK, dV [B,H,N,d] and D [B,H,N] over all rows."""
+             dropout_p=0.0, seed=0, rng_offset=0, chunk=512, pairs=None):
+    """dQ, dK, dV [B,H,N,d] and D [B,H,N] over all rows (of the heads in
+    `pairs`, default all)."""
     q, k, v, do = as_f64(q), as_f64(k), as_f64(v), as_f64(do)
     B, H, N, d = q.shape
     sc = scale_f32(scale)
@@ -131,33 +136,32 @@ def attn_bwd(q, k, v, do, scale, causal=False, key_lens=None, block_mask=None,
     dk = np.zeros_like(k)
     dv = np.zeros_like(v)
     Dall = np.zeros((B, H, N))
-    for b in range(B):
+    for b, h in _pairs(B, H, pairs):
         kl = _key_len(key_lens, b)
-        for h in range(H):
-            for s in range(0, N, chunk):
-                r = np.arange(s, min(s + chunk, N))
-                S = _rows_scores(q[b, h], k[b, h], r, sc)
-                A = validity(r, N, causal, kl, block_mask)
-                P, _, _, _ = safe_softmax(S, A)
-                if dropout_p > 0.0:
-                    Z = keep_mask(seed, rng_offset, dropout_p, b, h, H, r, np.arange(N))
-                else:
-                    Z = np.ones_like(P, dtype=bool)
-                P_hat = P * Z * keep_scale
-                dP_hat = do[b, h, r] @ v[b, h].T
-                dv[b, h] += P_hat.T @ do[b, h, r]
-                dP = dP_hat * Z * keep_scale
-                D = (P * dP).sum(axis=1)
-                dS = P * (dP - D[:, None])
-                dq[b, h, r] = sc * (dS @ k[b, h])
-                dk[b, h] += sc * (dS.T @ q[b, h, r])
-                Dall[b, h, r] = D
+        for s in range(0, N, chunk):
+            r = np.arange(s, min(s + chunk, N))
+            S = _rows_scores(q[b, h], k[b, h], r, sc)
+            A = validity(r, N, causal, kl, block_mask)
+            P, _, _, _ = safe_softmax(S, A)
+            if dropout_p > 0.0:
+                Z = keep_mask(seed, rng_offset, dropout_p, b, h, H, r, np.arange(N))
+            else:
+                Z = np.ones_like(P, dtype=bool)
+            P_hat = P * Z * keep_scale
+            dP_hat = do[b, h, r] @ v[b, h].T
+            dv[b, h] += P_hat.T @ do[b, h, r]
+            dP = dP_hat * Z * keep_scale
+            D = (P * dP).sum(axis=1)
+            dS = P * (dP - D[:, None])
+            dq[b, h, r] = sc * (dS @ k[b, h])
+            dk[b, h] += sc * (dS.T @ q[b, h, r])
+            Dall[b, h, r] = D
     return dq, dk, dv, Dall
 
 
 def attn_bwd_rows_cols(q, k, v, do, scale, rows, cols, lse_all, D_all,
                        causal=False, key_lens=None, block_mask=None,
-                       dropout_p=0.0, seed=0, rng_offset=0, chunk=1024):
+                       dropout_p=0.0, seed=0, rng_offset=0, chunk=1024, pairs=None):
     """Gradients at sampled positions of a large input.
 
     dQ for query rows `rows` needs only those rows' full score rows.
@@ -175,32 +179,31 @@ def attn_bwd_rows_cols(q, k, v, do, scale, rows, cols, lse_all, D_all,
     dq = np.zeros((B, H, len(rows), d))
     dk = np.zeros((B, H, len(cols), d))
     dv = np.zeros((B, H, len(cols), d))
-    for b in range(B):
+    for b, h in _pairs(B, H, pairs):
         kl = _key_len(key_lens, b)
-        for h in range(H):
-            # dQ rows: full rows of S
-            S = _rows_scores(q[b, h], k[b, h], rows, sc)
-            A = validity(rows, N, causal, kl, block_mask)
-            P, _, _, _ = safe_softmax(S, A)
-            Z = (keep_mask(seed, rng_offset, dropout_p, b, h, H, rows, np.arange(N))
-                 if dropout_p > 0 else np.ones_like(P, dtype=bool))
-            dP = (do[b, h, rows] @ v[b, h].T) * Z * keep_scale
-            D = (P * dP).sum(axis=1)
-            dq[b, h] = sc * ((P * (dP - D[:, None])) @ k[b, h])
-            # dK, dV columns: all query rows, selected keys
-            for s in range(0, N, chunk):
-                r = np.arange(s, min(s + chunk, N))
-                Sc = sc * (q[b, h, r] @ k[b, h, cols].T)
-                Ac = validity(r, N, causal, kl, block_mask)[:, cols]
-                lse = lse_all[b, h, r]
-                live = np.isfinite(lse)[:, None] & Ac
-                Pc = np.where(live, np.exp(np.where(live, Sc - lse[:, None], -np.inf)), 0.0)
-                Zc = (keep_mask(seed, rng_offset, dropout_p, b, h, H, r, cols)
-                      if dropout_p > 0 else np.ones_like(Pc, dtype=bool))
-                dv[b, h] += (Pc * Zc * keep_scale).T @ do[b, h, r]
-                dPc = (do[b, h, r] @ v[b, h, cols].T) * Zc * keep_scale
-                dSc = Pc * (dPc - D_all[b, h, r][:, None])
-                dk[b, h] += sc * (dSc.T @ q[b, h, r])
+        # dQ rows: full rows of S
+        S = _rows_scores(q[b, h], k[b, h], rows, sc)
+        A = validity(rows, N, causal, kl, block_mask)
+        P, _, _, _ = safe_softmax(S, A)
+        Z = (keep_mask(seed, rng_offset, dropout_p, b, h, H, rows, np.arange(N))
+             if dropout_p > 0 else np.ones_like(P, dtype=bool))
+        dP = (do[b, h, rows] @ v[b, h].T) * Z * keep_scale
+        D = (P * dP).sum(axis=1)
+        dq[b, h] = sc * ((P * (dP - D[:, None])) @ k[b, h])
+        # dK, dV columns: all query rows, selected keys
+        for s in range(0, N, chunk):
+            r = np.arange(s, min(s + chunk, N))
+            Sc = sc * (q[b, h, r] @ k[b, h, cols].T)
+            Ac = validity(r, N, causal, kl, block_mask)[:, cols]
+            lse = lse_all[b, h, r]
+            live = np.isfinite(lse)[:, None] & Ac
+            Pc = np.where(live, np.exp(np.where(live, Sc - lse[:, None], -np.inf)), 0.0)
+            Zc = (keep_mask(seed, rng_offset, dropout_p, b, h, H, r, cols)
+                  if dropout_p > 0 else np.ones_like(Pc, dtype=bool))
+            dv[b, h] += (Pc * Zc * keep_scale).T @ do[b, h, r]
+            dPc = (do[b, h, r] @ v[b, h, cols].T) * Zc * keep_scale
+            dSc = Pc * (dPc - D_all[b, h, r][:, None])
+            dk[b, h] += sc * (dSc.T @ q[b, h, r])
     return dq, dk, dv
 
 
@@ -214,8 +217,7 @@ def attn_stats(q, k, v, do, scale, causal=False, key_lens=None, block_mask=None,
     keep_scale = 1.0 / (1.0 - float(np.float32(dropout_p))) if dropout_p > 0 else 1.0
     LSE = np.zeros((B, H, N))
     Dall = np.zeros((B, H, N))
-    pairs = heads if heads is not None else [(b, h) for b in range(B) for h in range(H)]
-    for b, h in pairs:
+    for b, h in _pairs(B, H, heads):
         kl = _key_len(key_lens, b)
         for s in range(0, N, chunk):
             r = np.arange(s, min(s + chunk, N))

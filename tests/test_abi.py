@@ -1,0 +1,121 @@
+"""The C-ABI library loads, exports every symbol include/fa.h declares, and its
+host-side validation rejects bad arguments before touching the GPU (these
+calls return before any HIP call, so they run without a device)."""
+
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "fa.h")
+
+lib_mod = pytest.importorskip("io_aware_exact_tiled_amd._lib")
+
+
+def _lib():
+    if not os.path.exists(lib_mod.LIB_PATH):
+        pytest.skip("libfa.so not built")
+    return lib_mod.lib()
+
+
+def declared_symbols():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?[\w]+\s*\*?\s*(fa_\w+)\s*\(", text, re.M)))
+
+
+def test_header_and_binding_agree():
+    assert declared_symbols() == sorted(lib_mod.EXPORTS)
+
+
+def test_library_exports_every_declared_symbol():
+    L = _lib()
+    out = subprocess.run(["nm", "-D", "--defined-only", lib_mod.LIB_PATH], capture_output=True, text=True).stdout
+    exported = set(re.findall(r" T (fa_\w+)", out))
+    for s in declared_symbols():
+        assert s in exported, s
+        assert hasattr(L, s)
+
+
+def test_scalars():
+    L = _lib()
+    assert L.fa_abi_version() == 1
+    for code in list(lib_mod.STATUS) + [-99]:
+        assert isinstance(L.fa_status_string(code), bytes)
+    br, bc = ctypes.c_int32(), ctypes.c_int32()
+    for d in (64, 128):
+        for dt in (0, 1, 2):
+            for p in (0, 1):
+                assert L.fa_tile_shape(d, dt, p, ctypes.byref(br), ctypes.byref(bc)) == 0
+                assert 128 % br.value == 0 and 128 % bc.value == 0
+    assert L.fa_tile_shape(96, 2, 0, ctypes.byref(br), ctypes.byref(bc)) == -3
+    assert L.fa_tile_shape(64, 7, 0, ctypes.byref(br), ctypes.byref(bc)) == -4
+    assert L.fa_bwd_workspace_bytes(1, 2, 256, 64) == 1 * 2 * 256 * 64 * 4 + 2048
+    assert L.fa_bwd_workspace_bytes(1, 1, 3, 64) == 768 + 256
+    assert L.fa_bwd_workspace_bytes(0, 1, 3, 64) == 0
+
+
+P = 0x10000  # a 256-byte aligned fake device address: never dereferenced on these paths
+
+
+def fwd(L, q=P, k=P, v=P, o=P, lse=P, B=1, H=1, N=8, d=64, dt=2, scale=0.125, causal=0, p=0.0, seed=0,
+        mask=None, opts=None):
+    return L.fa_fwd(q, k, v, o, lse, B, H, N, d, dt, scale, causal, p, seed, mask, opts, None)
+
+
+def bwd(L, B=1, H=1, N=8, d=64, dt=2, scale=0.125, p=0.0, opts=None, ws=P, ws_bytes=1 << 20, ptrs=None):
+    ptrs = ptrs or [P] * 9
+    return L.fa_bwd(*ptrs, B, H, N, d, dt, scale, 0, p, 0, None, opts, ws, ws_bytes, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(q=None), -1), (dict(lse=None), -1),
+    (dict(B=0), -2), (dict(N=0), -2), (dict(H=70000), -2), (dict(N=1 << 26, d=64), -2),
+    (dict(d=96), -3), (dict(d=0), -3),
+    (dict(dt=5), -4),
+    (dict(p=1.0), -5), (dict(p=-0.1), -5), (dict(p=float("nan")), -5),
+    (dict(scale=0.0), -6), (dict(scale=-1.0), -6), (dict(scale=float("inf")), -6), (dict(scale=float("nan")), -6),
+    (dict(o=P + 8), -7), (dict(k=P + 2), -7),
+])
+def test_fwd_validation(kw, code):
+    assert fwd(_lib(), **kw) == code
+
+
+def test_opts_validation():
+    L = _lib()
+    o = lib_mod.FaOpts()
+    o.struct_size = 3
+    assert fwd(L, opts=ctypes.byref(o)) == -10
+    o.struct_size = ctypes.sizeof(lib_mod.FaOpts)
+    o.flags = 1 << 7
+    assert fwd(L, opts=ctypes.byref(o)) == -10
+    o.flags = lib_mod.FA_FLAG_RECORD_TILES
+    o.tile_visits = None
+    assert fwd(L, opts=ctypes.byref(o)) == -1
+    o.flags = lib_mod.FA_FLAG_REVERSE_KV
+    assert bwd(L, opts=ctypes.byref(o)) == -10      # forward-only flag
+
+
+def test_bwd_validation():
+    L = _lib()
+    need = L.fa_bwd_workspace_bytes(1, 1, 8, 64)
+    assert bwd(L, ws=None) == -8
+    assert bwd(L, ws_bytes=need - 1) == -8
+    assert bwd(L, ws=P + 16) == -8                  # not 256-byte aligned
+    assert bwd(L, d=80) == -3
+    assert bwd(L, p=2.0) == -5
+    ptrs = [P] * 9
+    ptrs[4] = None                                  # dO
+    assert bwd(L, ptrs=ptrs) == -1
+    ptrs = [P] * 9
+    ptrs[6] = P + 4                                 # dQ misaligned
+    assert bwd(L, ptrs=ptrs) == -7
+
+
+def test_keep_mask_validation():
+    L = _lib()
+    assert L.fa_dropout_keep_mask(0, 0, 0.1, 1, 1, 8, None, None) == -1
+    assert L.fa_dropout_keep_mask(0, 0, 1.5, 1, 1, 8, P, None) == -5
+    assert L.fa_dropout_keep_mask(0, 0, 0.1, 0, 1, 8, P, None) == -2

@@ -1,0 +1,190 @@
+"""GPU parity of the HIP forward and backward kernels against the fp64
+oracle, through the C ABI, at sizes the oracle finishes in seconds: several
+tiles plus a ragged tail, every mask kind, dropout, and the degenerate cases."""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads as W
+from helpers import (check_grad, check_lse, check_o, cuda, f64, fa_kw, oracle_kw)
+
+pytestmark = pytest.mark.gpu
+
+fa = pytest.importorskip("io_aware_exact_tiled_amd")
+
+DT = {"bf16": torch.bfloat16, "fp16": torch.float16, "fp32": torch.float32}
+
+
+def run_and_check(x, bwd=True, label=""):
+    print(f"[case] {label}", flush=True)
+    q, k, v, do = (cuda(x[n]) for n in ("q", "k", "v", "do"))
+    dtype = q.dtype
+    okw = oracle_kw(x)
+    O, L = oracle.attn_fwd(x["q"], x["k"], x["v"], x["scale"], **okw)
+    o32, lse = fa.fwd(q, k, v, o_fp32=True, **fa_kw(x))
+    o, lse2 = fa.fwd(q, k, v, **fa_kw(x))
+    torch.cuda.synchronize()
+    e_o = check_o(o32, O, dtype)
+    check_o(o, O, dtype, "O(stored)", stored=True)
+    e_l = check_lse(lse, L, dtype)
+    assert torch.equal(lse, lse2)
+    res = dict(o=e_o, lse=e_l)
+    if bwd:
+        dq, dk, dv = fa.bwd(q, k, v, o32 if dtype != torch.float32 else o, do, lse, **fa_kw(x))
+        torch.cuda.synchronize()
+        rq, rk, rv, _ = oracle.attn_bwd(x["q"], x["k"], x["v"], x["do"], x["scale"], **okw)
+        res.update(dq=check_grad(dq, rq, dtype, "dQ"), dk=check_grad(dk, rk, dtype, "dK"),
+                   dv=check_grad(dv, rv, dtype, "dV"))
+    print(f"[ok] {label} {res}", flush=True)
+    return res
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp32"])
+def test_tiny_workload(dtype):
+    w = W.WORKLOADS["tiny"]
+    run_and_check(W.make_inputs(w, dtype=dtype), label=f"tiny {dtype}")
+
+
+CASES = [
+    # (N, d, dtype, causal, key_lens, sparse, dropout)
+    (1, 64, "bf16", False, None, False, 0.0),
+    (17, 64, "bf16", True, None, False, 0.0),
+    (64, 128, "bf16", False, None, False, 0.0),
+    (129, 128, "fp16", True, None, False, 0.0),
+    (255, 64, "fp16", False, "mixed", False, 0.0),
+    (300, 128, "bf16", True, "mixed", False, 0.0),
+    (300, 64, "bf16", False, None, True, 0.0),
+    (384, 128, "bf16", True, None, True, 0.0),
+    (200, 64, "fp16", False, "mixed", False, 0.1),
+    (257, 128, "bf16", True, None, False, 0.5),
+    (300, 64, "bf16", True, "mixed", True, 0.2),
+    (100, 64, "fp32", True, "mixed", False, 0.0),
+    (130, 128, "fp32", False, None, False, 0.25),
+    (513, 64, "bf16", True, None, False, 0.0),
+    (640, 128, "fp16", False, None, False, 0.0),
+]
+
+
+@pytest.mark.parametrize("case", CASES, ids=lambda c: "N%d-d%d-%s-c%d-kl%s-sp%d-p%g" % c)
+def test_edge_matrix(case):
+    N, d, dtype, causal, kl, sparse, p = case
+    x = W.random_case(2, 2, N, d, dtype=dtype, seed=N * 7 + d, causal=causal,
+                      dropout_p=p, dropout_seed=N + 11, rng_offset=3 if p else 0,
+                      sparse_density=0.4 if sparse else None)
+    if kl == "mixed":
+        x["key_lens"] = torch.tensor([max(N // 3, 1), N], dtype=torch.int32)
+    run_and_check(x, label=str(case))
+
+
+def test_fully_masked_rows_and_empty_keys():
+    x = W.random_case(3, 2, 200, 64, dtype="bf16", seed=5)
+    x["key_lens"] = torch.tensor([0, 1, 200], dtype=torch.int32)
+    r = run_and_check(x, label="key_lens 0/1/N")
+    o, lse = fa.fwd(cuda(x["q"]), cuda(x["k"]), cuda(x["v"]), key_lens=cuda(x["key_lens"]))
+    assert (o[0] == 0).all() and torch.isneginf(lse[0]).all()
+
+
+def test_block_mask_all_zero_rows():
+    x = W.random_case(1, 2, 384, 64, dtype="bf16", seed=8)
+    bm = torch.ones(3, 3, dtype=torch.uint8)
+    bm[1] = 0                   # query rows 128..255 see nothing
+    bm[2, 0] = 0
+    x["block_mask"] = bm
+    run_and_check(x, label="block mask with an empty row")
+
+
+def test_dropout_keep_mask_bit_exact():
+    B, H, N = 2, 3, 203
+    for seed, off, p in ((3, 0, 0.1), (2 ** 40 + 5, 7, 0.5), (0, 0, 0.9)):
+        keep = fa.dropout_keep_mask(seed, off, p, B, H, N).cpu().numpy()
+        for b in range(B):
+            for h in range(H):
+                want = oracle.keep_mask(seed, off, p, b, h, H, np.arange(N), np.arange(N))
+                assert np.array_equal(keep[b, h].astype(bool), want), (seed, off, p, b, h)
+
+
+@pytest.mark.parametrize("case", [
+    dict(N=1000, causal=True), dict(N=1000, causal=False, kl=True), dict(N=700, causal=True, sparse=True),
+    dict(N=384, causal=False, sparse=True, kl=True)])
+def test_tile_visits_bit_exact(case):
+    N = case["N"]
+    x = W.random_case(2, 2, N, 64, dtype="bf16", seed=N, causal=case["causal"],
+                      sparse_density=0.3 if case.get("sparse") else None)
+    if case.get("kl"):
+        x["key_lens"] = torch.tensor([N // 5, N - 1], dtype=torch.int32)
+    q, k, v, do = (cuda(x[n]) for n in ("q", "k", "v", "do"))
+    o, lse, tf = fa.fwd(q, k, v, record_tiles=True, **fa_kw(x))
+    dq, dk, dv, tb = fa.bwd(q, k, v, o, do, lse, record_tiles=True, **fa_kw(x))
+    okw = oracle_kw(x)
+    for pass_, t in ((0, tf), (1, tb)):
+        br, bc = fa.tile_shape(64, 2, pass_)
+        want = oracle.expected_tiles(N, br, bc, 2, okw["causal"], okw["key_lens"], okw["block_mask"])
+        got = t.cpu().numpy()
+        for h in range(2):
+            assert np.array_equal(got[:, h], want), f"pass {pass_} head {h}"
+
+
+def test_forward_is_deterministic_and_order_free():
+    x = W.random_case(2, 4, 777, 128, dtype="bf16", seed=9, causal=True)
+    q, k, v = (cuda(x[n]) for n in ("q", "k", "v"))
+    a = fa.fwd(q, k, v, causal=True, o_fp32=True)
+    b = fa.fwd(q, k, v, causal=True, o_fp32=True)
+    assert torch.equal(a[0], b[0]) and torch.equal(a[1], b[1])
+    r = fa.fwd(q, k, v, causal=True, o_fp32=True, reverse_kv=True)
+    assert (r[0] - a[0]).abs().max().item() < 1e-3
+    assert (r[1] - a[1]).abs().max().item() < 1e-4
+
+
+def test_backward_dk_dv_deterministic():
+    x = W.random_case(1, 2, 500, 64, dtype="fp16", seed=10, causal=True)
+    q, k, v, do = (cuda(x[n]) for n in ("q", "k", "v", "do"))
+    o, lse = fa.fwd(q, k, v, causal=True)
+    g1 = fa.bwd(q, k, v, o, do, lse, causal=True)
+    g2 = fa.bwd(q, k, v, o, do, lse, causal=True)
+    assert torch.equal(g1[1], g2[1]) and torch.equal(g1[2], g2[2])
+    assert (g1[0].float() - g2[0].float()).abs().max().item() <= 1e-3 * g1[0].float().abs().max().item()
+
+
+def test_nan_propagates_without_hang():
+    x = W.random_case(1, 1, 300, 64, dtype="bf16", seed=12)
+    q = x["q"].clone()
+    q[0, 0, 5, 3] = float("nan")
+    o, lse = fa.fwd(cuda(q), cuda(x["k"]), cuda(x["v"]), o_fp32=True)
+    torch.cuda.synchronize()
+    o = o.cpu()
+    assert torch.isnan(o[0, 0, 5]).all()
+    rows = [i for i in range(300) if i != 5]
+    assert torch.isfinite(o[0, 0, rows]).all()
+
+
+def test_runs_on_a_non_default_stream():
+    x = W.random_case(2, 2, 640, 64, dtype="bf16", seed=13, causal=True)
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        q, k, v = (x[n].to("cuda", non_blocking=False) for n in ("q", "k", "v"))
+        q = q * 1.0          # producer work on the same stream
+        o, lse = fa.fwd(q, k, v, causal=True, o_fp32=True)
+        o2 = o * 2.0         # consumer on the same stream
+    s.synchronize()
+    O, L = oracle.attn_fwd(x["q"], x["k"], x["v"], x["scale"], causal=True)
+    check_o(o2 / 2.0, O, torch.bfloat16)
+
+
+def test_extra_memory_is_linear_in_n():
+    N, d = 16384, 128
+    q = torch.randn(1, 1, N, d, device="cuda", dtype=torch.bfloat16)
+    k, v = torch.randn_like(q), torch.randn_like(q)
+    do = torch.randn_like(q)
+    torch.cuda.synchronize()
+    torch.cuda.reset_peak_memory_stats()
+    base = torch.cuda.memory_allocated()
+    o, lse = fa.fwd(q, k, v, causal=True)
+    dq, dk, dv = fa.bwd(q, k, v, o, do, lse, causal=True)
+    torch.cuda.synchronize()
+    peak = torch.cuda.max_memory_allocated() - base
+    # outputs (O, dQ, dK, dV in bf16, LSE) + fp32 dQ workspace + D: all O(N d);
+    # a single N x N bf16 matrix would be 512 MiB
+    linear = 4 * N * d * 2 + N * 4 + N * d * 4 + N * 4 + (1 << 20)
+    assert peak <= linear, (peak, linear)

@@ -1,0 +1,72 @@
+"""GPU parity at the full sizes of the five workloads, through the C ABI and
+in the launch configuration bench.py times.  Where the fp64 oracle cannot
+cover every output in seconds (the 16K-token workloads) it checks sampled
+query rows (O, LSE, dQ: each needs only that row's full score row) and, for
+two heads, sampled key rows (dK, dV: each needs the full score column plus
+every row's LSE and D from a chunked fp64 pass)."""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads as W
+from helpers import check_grad, check_lse, check_o, cuda, f64, fa_kw, oracle_kw
+
+pytestmark = pytest.mark.gpu
+
+fa = pytest.importorskip("io_aware_exact_tiled_amd")
+
+
+def gpu_pass(x):
+    q, k, v, do = (cuda(x[n]) for n in ("q", "k", "v", "do"))
+    o32, lse = fa.fwd(q, k, v, o_fp32=True, **fa_kw(x))
+    o, _ = fa.fwd(q, k, v, **fa_kw(x))
+    dq, dk, dv = fa.bwd(q, k, v, o, do, lse, **fa_kw(x))
+    torch.cuda.synchronize()
+    return o32, o, lse, dq, dk, dv
+
+
+@pytest.mark.parametrize("name", ["gpt2", "bert"])
+def test_workload_full_oracle(name):
+    w = W.WORKLOADS[name]
+    print(f"[case] {name} full", flush=True)
+    x = W.make_inputs(w)
+    dtype = W.torch_dtype(w.dtype)
+    o32, o, lse, dq, dk, dv = gpu_pass(x)
+    okw = oracle_kw(x)
+    O, L = oracle.attn_fwd(x["q"], x["k"], x["v"], x["scale"], **okw)
+    res = dict(o=check_o(o32, O, dtype), o_stored=check_o(o, O, dtype, "O(stored)", stored=True),
+               lse=check_lse(lse, L, dtype))
+    rq, rk, rv, _ = oracle.attn_bwd(x["q"], x["k"], x["v"], x["do"], x["scale"], **okw)
+    res.update(dq=check_grad(dq, rq, dtype, "dQ"), dk=check_grad(dk, rk, dtype, "dK"),
+               dv=check_grad(dv, rv, dtype, "dV"))
+    print(f"[ok] {name} {res}", flush=True)
+
+
+@pytest.mark.parametrize("name", ["long", "sparse"])
+def test_workload_sampled_oracle(name):
+    w = W.WORKLOADS[name]
+    print(f"[case] {name} sampled", flush=True)
+    x = W.make_inputs(w)
+    dtype = W.torch_dtype(w.dtype)
+    o32, o, lse, dq, dk, dv = gpu_pass(x)
+    okw = oracle_kw(x)
+    rows = W.sample_rows(w.N, w.sample_rows, w.seed)
+    O, L = oracle.attn_fwd(x["q"], x["k"], x["v"], x["scale"], rows=rows, **okw)
+    res = dict(o=check_o(o32[:, :, rows], O, dtype), lse=check_lse(lse[:, :, rows], L, dtype),
+               o_stored=check_o(o[:, :, rows], O, dtype, "O(stored)", stored=True))
+    # dQ on the sampled rows of every head; dK, dV on sampled keys of two heads
+    heads = [(0, 0), (0, w.H - 1)]
+    cols = W.sample_rows(w.N, 128, w.seed + 1)
+    Ls, Ds = oracle.attn_stats(x["q"], x["k"], x["v"], x["do"], x["scale"], heads=heads, **okw)
+    rq, _, _ = oracle.attn_bwd_rows_cols(x["q"], x["k"], x["v"], x["do"], x["scale"], rows,
+                                         np.array([], dtype=np.int64), Ls, Ds, **okw)
+    res["dq"] = check_grad(dq[:, :, rows], rq, dtype, "dQ(rows)")
+    _, rk, rv = oracle.attn_bwd_rows_cols(x["q"], x["k"], x["v"], x["do"], x["scale"], rows[:1], cols,
+                                          Ls, Ds, pairs=heads, **okw)
+    for b, h in heads:
+        res[f"dk{h}"] = check_grad(dk[b:b + 1, h:h + 1, cols], rk[b:b + 1, h:h + 1], dtype, f"dK(h{h})")
+        res[f"dv{h}"] = check_grad(dv[b:b + 1, h:h + 1, cols], rv[b:b + 1, h:h + 1], dtype, f"dV(h{h})")
+    # the LSE and D the oracle used for the columns are its own, all rows
+    print(f"[ok] {name} {res}", flush=True)
