@@ -43,6 +43,9 @@ def parse():
     ap.add_argument("--cpu-rows", type=int, default=3072,
                     help="leading causal rows per head the oracle baseline computes")
     ap.add_argument("--sweep", action="store_true", help="also time the N sweep (extra JSON lines)")
+    ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
+                    help="first run one plain device-to-device copy of MIB MiB (a known-size kernel "
+                         "that hardware byte counters can be scaled by)")
     return ap.parse_args()
 
 
@@ -194,6 +197,14 @@ def main():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
     ev = HipEvents()
+    if args.calibrate_copy:
+        n = args.calibrate_copy * (1 << 20) // 4
+        src = torch.ones(n, dtype=torch.float32, device="cuda:0")
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
     w = W.WORKLOADS[args.workload]
     r = time_workload(w, args.steps, args.warmup, ev)
     fwd_flop = 4.0 * w.d * r["pairs"]
