@@ -92,14 +92,18 @@ __device__ inline f32x16 zero16() {
 // ---------------------------------------------------------------------------
 // Row-major LDS tile of ROWS x COLS elements of T, addressed in 16-byte units
 // with an XOR swizzle of the unit index by the row so that lanes reading the
-// same column of consecutive rows fall in different banks.
+// same column of consecutive rows fall in different banks.  Each swizzle is a
+// bijection on the units of 8 consecutive rows (a 128-byte bank window) and,
+// for rows of up to 256 bytes, also on the (window offset, unit) pairs of 16
+// consecutive rows (a 256-byte window).
 template <class T, int COLS>
 struct Swz {
     static constexpr int EPU = 16 / (int)sizeof(T);   // elements per 16-byte unit
     static constexpr int U = COLS / EPU;              // units per row
     static_assert(COLS % EPU == 0, "row must be a whole number of 16-byte units");
     __device__ static inline int f(int row) {
-        if constexpr (U >= 8) return (row ^ (row >> 3)) & 7;
+        if constexpr (U >= 16) return (row ^ (row >> 4)) & 15;
+        else if constexpr (U == 8) return (row ^ (row >> 3)) & 7;
         else if constexpr (U == 4) return ((row >> 1) ^ (row >> 3)) & 3;
         else if constexpr (U == 2) return ((row >> 2) ^ (row >> 3)) & 1;
         else return 0;
@@ -148,5 +152,11 @@ __device__ inline uint32_t keep4(uint32_t g, uint32_t i, uint32_t bh, uint32_t o
 __device__ inline float wave_xor32(float v) { return __shfl_xor(v, 32, WAVE); }
 
 __device__ inline float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// Map a linear workgroup id to a work item so that each of the 8 XCDs (which
+// receive workgroups round-robin and have their own L2) works on a contiguous
+// range of items.  `per` = ceil(total / 8); the grid has 8 * per workgroups
+// and ids whose item is >= total do nothing.
+__device__ inline int xcd_item(int wg, int per) { return (wg & 7) * per + (wg >> 3); }
 
 }  // namespace fa

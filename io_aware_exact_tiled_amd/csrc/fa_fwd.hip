@@ -79,37 +79,60 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdArgs a) {
     constexpr int DB = D / 32;          // 32-wide column blocks of O
     constexpr int PU = 16 / EV;         // P*V MFMAs per 32-key block
     constexpr int EPU = 16 / (int)sizeof(T);
+    constexpr int DC = D / EPU;         // 16-byte chunks per row of K / V
+    constexpr int KT = BC * DC;         // K staging: one 16-byte chunk per task
+    constexpr int KN = (KT + 255) / 256;
+    constexpr int VT = (BC / 4) * DC;   // V staging: 4 rows x one chunk per task
+    constexpr int VN = (VT + 255) / 256;
+    constexpr int TILE_K = BC * D;      // elements of one K (or V^T) buffer
+    constexpr float RESCALE = 8.0f;     // log2 headroom before the running max moves
     typedef Swz<T, D> LK;
     typedef Swz<TV, BC> LV;
 
-    __shared__ __attribute__((aligned(16))) T sK[BC * D];
-    __shared__ __attribute__((aligned(16))) TV sV[D * BC];
+    __shared__ __attribute__((aligned(16))) T sK[2 * TILE_K];
+    __shared__ __attribute__((aligned(16))) TV sV[2 * TILE_K];
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int hl = lane >> 5, ln = lane & 31;
     const int N = a.N, H = a.H;
     const int Tr = (N + BR - 1) / BR, Tc = (N + BC - 1) / BC;
-    const int b = blockIdx.z, h = blockIdx.y;
-    // causal: heaviest query tiles (most key tiles) are launched first
-    const int it = a.mask.causal ? (Tr - 1 - (int)blockIdx.x) : (int)blockIdx.x;
+    // work item: contiguous ranges per XCD; inside a head, heaviest tiles first
+    const int total = Tr * H * a.B;
+    const int item = xcd_item((int)blockIdx.x, (total + 7) / 8);
+    if (item >= total) return;
+    const int bhi = item / Tr, r_ = item % Tr;
+    const int it = a.mask.causal ? (Tr - 1 - r_) : r_;
+    const int b = bhi / H, h = bhi % H;
     const int q0 = it * BR, qw0 = q0 + wave * 32;
-    const size_t bh = (size_t)b * H + h;
+    const size_t bh = (size_t)bhi;
     const size_t hoff = bh * (size_t)N * D;
     const T* __restrict__ Qg = (const T*)a.q + hoff;
     const T* __restrict__ Kg = (const T*)a.k + hoff;
     const T* __restrict__ Vg = (const T*)a.v + hoff;
+    (void)b; (void)h;
 
     int kend = N;
     if (a.mask.key_lens) {
-        const int L = a.mask.key_lens[b];
+        const int L = a.mask.key_lens[bhi / H];
         kend = L < 0 ? 0 : (L > N ? N : L);
     }
     int j_end = min(Tc, (kend + BC - 1) / BC);
     if (a.mask.causal) j_end = min(j_end, (min(q0 + BR, N) - 1) / BC + 1);
+    const uint8_t* bmask = a.mask.block_mask ? a.mask.block_mask + (size_t)(q0 / MASK_TILE) * a.mask.mask_T
+                                             : nullptr;
+    const int rev = a.reverse_kv;
+    // next visited key tile after position jj of the walk (or -1)
+    auto tile_at = [&](int jj) -> int {
+        for (; jj < j_end; ++jj) {
+            const int j = rev ? (j_end - 1 - jj) : jj;
+            if (!bmask || bmask[(j * BC) / MASK_TILE]) return jj;
+        }
+        return -1;
+    };
 
     uint8_t* vis = a.tile_visits ? a.tile_visits + (bh * Tr + it) * (size_t)Tc : nullptr;
     if (vis)
-        for (int j = j_end + tid; j < Tc; j += 256) vis[j] = 0;
+        for (int j = tid; j < Tc; j += 256) vis[j] = 0;
 
     // Q_i^T as the B operand: lane column = query qw0 + ln, rows = d
     const int qrow = qw0 + ln;
@@ -119,6 +142,57 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdArgs a) {
         qf[ks] = (qrow < N) ? load_frag<T>(Qg + (size_t)qrow * D + ks * 2 * E + hl * E)
                             : zero_frag<T>();
 
+    // ---- staging: global -> registers (prefetch) -> LDS
+    u32x4 kreg[KN];
+    u32x4 vreg[VN][4];
+    auto load_tile = [&](int j) {
+        const int kv0 = j * BC;
+#pragma unroll
+        for (int n = 0; n < KN; ++n) {
+            const int t = tid + n * 256;
+            const int key = kv0 + t / DC;
+            u32x4 z = {0u, 0u, 0u, 0u};
+            kreg[n] = (t < KT && key < N) ? *reinterpret_cast<const u32x4*>(Kg + (size_t)key * D + (t % DC) * EPU)
+                                          : z;
+        }
+#pragma unroll
+        for (int n = 0; n < VN; ++n) {
+            const int t = tid + n * 256;
+#pragma unroll
+            for (int kk = 0; kk < 4; ++kk) {
+                const int key = kv0 + (t / DC) * 4 + kk;
+                u32x4 z = {0u, 0u, 0u, 0u};
+                vreg[n][kk] = (t < VT && key < N)
+                                  ? *reinterpret_cast<const u32x4*>(Vg + (size_t)key * D + (t % DC) * EPU)
+                                  : z;
+            }
+        }
+    };
+    auto store_tile = [&](int buf) {
+        T* k = sK + buf * TILE_K;
+        TV* v = sV + buf * TILE_K;
+#pragma unroll
+        for (int n = 0; n < KN; ++n) {
+            const int t = tid + n * 256;
+            if (t < KT) *reinterpret_cast<u32x4*>(k + LK::off(key_slot(t / DC), (t % DC) * EPU)) = kreg[n];
+        }
+#pragma unroll
+        for (int n = 0; n < VN; ++n) {
+            const int t = tid + n * 256;
+            if (t < VT) {
+                const int dc = t % DC, kg = t / DC;
+                const T* x0 = reinterpret_cast<const T*>(&vreg[n][0]);
+                const T* x1 = reinterpret_cast<const T*>(&vreg[n][1]);
+                const T* x2 = reinterpret_cast<const T*>(&vreg[n][2]);
+                const T* x3 = reinterpret_cast<const T*>(&vreg[n][3]);
+#pragma unroll
+                for (int dd = 0; dd < EPU; ++dd)
+                    store4<TV>(v + LV::off(dc * EPU + dd, kg * 4), to_f32(x0[dd]), to_f32(x1[dd]),
+                               to_f32(x2[dd]), to_f32(x3[dd]));
+            }
+        }
+    };
+
     float m_run = -INFINITY, l_run = 0.0f;
     f32x16 oacc[DB];
 #pragma unroll
@@ -126,123 +200,105 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdArgs a) {
 
     const float c = a.scale_log2;
     const int causal = a.mask.causal;
-    const uint8_t* bmask = a.mask.block_mask ? a.mask.block_mask + (size_t)(q0 / MASK_TILE) * a.mask.mask_T
-                                             : nullptr;
 
-    for (int jj = 0; jj < j_end; ++jj) {
-        const int j = a.reverse_kv ? (j_end - 1 - jj) : jj;
+    int jj = tile_at(0);
+    if (jj >= 0) {
+        load_tile(rev ? (j_end - 1 - jj) : jj);
+        store_tile(0);
+    }
+    __syncthreads();
+    int buf = 0;
+    while (jj >= 0) {
+        const int j = rev ? (j_end - 1 - jj) : jj;
         const int kv0 = j * BC;
-        if (bmask && bmask[kv0 / MASK_TILE] == 0) {
-            if (vis && tid == 0) vis[j] = 0;
-            continue;
-        }
         if (vis && tid == 0) vis[j] = 1;
+        const int jn = tile_at(jj + 1);
+        if (jn >= 0) load_tile(rev ? (j_end - 1 - jn) : jn);   // in flight during this tile's math
 
-        __syncthreads();   // previous tile fully consumed
-        // ---- stage K_j (MFMA row order) and V_j^T into LDS
-        {
-            constexpr int UPR = D / EPU;
-            for (int u = tid; u < BC * UPR; u += 256) {
-                const int r = u / UPR, cu = u % UPR;
-                const int key = kv0 + r;
-                u32x4 val = {0u, 0u, 0u, 0u};
-                if (key < N) val = *reinterpret_cast<const u32x4*>(Kg + (size_t)key * D + cu * EPU);
-                *reinterpret_cast<u32x4*>(sK + LK::off(key_slot(r), cu * EPU)) = val;
-            }
-            constexpr int DC = D / EPU;                 // 16-byte column chunks per row
-            for (int t = tid; t < (BC / 4) * DC; t += 256) {
-                const int dc = t % DC, kg = t / DC;
-                T x[4][EPU];
+        if (!(causal && kv0 > qw0 + 31)) {   // else: no valid key for this wave's rows
+            const T* k = sK + buf * TILE_K;
+            const TV* v = sV + buf * TILE_K;
+            // ---- S^T = K_j Q^T
+            f32x16 s[KB];
 #pragma unroll
-                for (int kk = 0; kk < 4; ++kk) {
-                    const int key = kv0 + kg * 4 + kk;
-                    u32x4 val = {0u, 0u, 0u, 0u};
-                    if (key < N) val = *reinterpret_cast<const u32x4*>(Vg + (size_t)key * D + dc * EPU);
-                    *reinterpret_cast<u32x4*>(&x[kk][0]) = val;
+            for (int kb = 0; kb < KB; ++kb) {
+                s[kb] = zero16();
+#pragma unroll
+                for (int ks = 0; ks < KS; ++ks) {
+                    const typename MS::frag ak = load_frag<T>(k + LK::off(kb * 32 + ln, ks * 2 * E + hl * E));
+                    s[kb] = MS::mma(ak, qf[ks], s[kb]);
                 }
-#pragma unroll
-                for (int dd = 0; dd < EPU; ++dd)
-                    store4<TV>(sV + LV::off(dc * EPU + dd, kg * 4), to_f32(x[0][dd]), to_f32(x[1][dd]),
-                               to_f32(x[2][dd]), to_f32(x[3][dd]));
             }
-        }
-        __syncthreads();
-
-        if (causal && kv0 > qw0 + 31) continue;   // no valid key for this wave's rows
-
-        // ---- S^T = K_j Q^T
-        f32x16 s[KB];
+            // ---- element masks on edge tiles
+            const bool edge = (kv0 + BC > kend) || (causal && kv0 + BC - 1 > qw0);
+            if (edge) {
 #pragma unroll
-        for (int kb = 0; kb < KB; ++kb) {
-            s[kb] = zero16();
+                for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
-            for (int ks = 0; ks < KS; ++ks) {
-                const typename MS::frag ak = load_frag<T>(sK + LK::off(kb * 32 + ln, ks * 2 * E + hl * E));
-                s[kb] = MS::mma(ak, qf[ks], s[kb]);
+                    for (int r = 0; r < 16; ++r) {
+                        const int key = kv0 + kb * 32 + hl * 16 + r;
+                        if (key >= kend || (causal && key > qrow)) s[kb][r] = -INFINITY;
+                    }
             }
-        }
-        // ---- element masks on edge tiles
-        const bool edge = (kv0 + BC > kend) || (causal && kv0 + BC - 1 > qw0);
-        if (edge) {
+            // ---- online softmax; the reference max only moves when some row's
+            // max exceeds it by more than 2^RESCALE, so P <= 2^RESCALE
+            float mx = -INFINITY;
+#pragma unroll
+            for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
+            mx = fmaxf(mx, wave_xor32(mx)) * c;
+            if (__any(mx > m_run + RESCALE)) {
+                const float m_new = fmaxf(m_run, mx);
+                const float alpha = (m_new == -INFINITY) ? 1.0f : fast_exp2(m_run - m_new);
+                m_run = m_new;
+                l_run *= alpha;
+#pragma unroll
+                for (int db = 0; db < DB; ++db)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
+            }
+            const float m_ref = (m_run == -INFINITY) ? 0.0f : m_run;
+
+            float p[KB][16];
 #pragma unroll
             for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
                 for (int r = 0; r < 16; ++r) {
-                    const int key = kv0 + kb * 32 + hl * 16 + r;
-                    if (key >= kend || (causal && key > qrow)) s[kb][r] = -INFINITY;
+                    p[kb][r] = fast_exp2(fmaf(s[kb][r], c, -m_ref));
+                    l_run += p[kb][r];
                 }
-        }
-        // ---- online softmax
-        float mx = -INFINITY;
+            if constexpr (DROP) {
+                const uint32_t g0 = (uint32_t)(kv0 + hl * 16) >> 2;
 #pragma unroll
-        for (int kb = 0; kb < KB; ++kb)
+                for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
-            for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
-        mx = fmaxf(mx, wave_xor32(mx));
-        const float m_new = fmaxf(m_run, mx * c);
-        const float m_ref = (m_new == -INFINITY) ? 0.0f : m_new;
-        const float alpha = fast_exp2(m_run - m_ref);
-        m_run = m_new;
-        l_run *= alpha;
+                    for (int g = 0; g < 4; ++g) {
+                        const uint32_t bits = keep4(g0 + kb * 8 + g, (uint32_t)qrow, (uint32_t)bh, a.drop.off,
+                                                    a.drop.k0, a.drop.k1, a.drop.thr);
 #pragma unroll
-        for (int db = 0; db < DB; ++db)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
-
-        float p[KB][16];
-#pragma unroll
-        for (int kb = 0; kb < KB; ++kb)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                p[kb][r] = fast_exp2(fmaf(s[kb][r], c, -m_ref));
-                l_run += p[kb][r];
+                        for (int e = 0; e < 4; ++e)
+                            if (!((bits >> e) & 1u)) p[kb][g * 4 + e] = 0.0f;
+                    }
             }
-        if constexpr (DROP) {
-            const uint32_t g0 = (uint32_t)(kv0 + hl * 16) >> 2;
+            // ---- O^T += V_j^T P^T
 #pragma unroll
             for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
-                for (int g = 0; g < 4; ++g) {
-                    const uint32_t bits = keep4(g0 + kb * 8 + g, (uint32_t)qrow, (uint32_t)bh, a.drop.off,
-                                                a.drop.k0, a.drop.k1, a.drop.thr);
+                for (int u = 0; u < PU; ++u) {
+                    const typename MV::frag bp = pack_p<TV>(&p[kb][u * EV]);
 #pragma unroll
-                    for (int e = 0; e < 4; ++e)
-                        if (!((bits >> e) & 1u)) p[kb][g * 4 + e] = 0.0f;
+                    for (int db = 0; db < DB; ++db) {
+                        const typename MV::frag av =
+                            load_frag<TV>(v + LV::off(db * 32 + ln, kb * 32 + hl * 16 + u * EV));
+                        oacc[db] = MV::mma(av, bp, oacc[db]);
+                    }
                 }
         }
-        // ---- O^T += V_j^T P^T
-#pragma unroll
-        for (int kb = 0; kb < KB; ++kb)
-#pragma unroll
-            for (int u = 0; u < PU; ++u) {
-                const typename MV::frag bp = pack_p<TV>(&p[kb][u * EV]);
-#pragma unroll
-                for (int db = 0; db < DB; ++db) {
-                    const typename MV::frag av =
-                        load_frag<TV>(sV + LV::off(db * 32 + ln, kb * 32 + hl * 16 + u * EV));
-                    oacc[db] = MV::mma(av, bp, oacc[db]);
-                }
-            }
+        if (jn >= 0) store_tile(buf ^ 1);   // that buffer was last read before the previous barrier
+        __syncthreads();
+        buf ^= 1;
+        jj = jn;
     }
 
     // ---- epilogue: O = O^T / l, LSE = m + ln l
@@ -270,7 +326,8 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdArgs a) {
 namespace {
 template <class T, int D, bool DROP>
 hipError_t launch_t(const FwdArgs& a, hipStream_t s) {
-    dim3 grid((a.N + FWD_BR - 1) / FWD_BR, a.H, a.B);
+    const int total = ((a.N + FWD_BR - 1) / FWD_BR) * a.H * a.B;
+    dim3 grid((unsigned)(8 * ((total + 7) / 8)));
     FwdArgs copy = a;
     void* args[] = {(void*)&copy};
     if (a.ev_begin) {
