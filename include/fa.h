@@ -97,14 +97,17 @@ typedef struct {
     uint64_t rng_offset;        /* Philox counter word 3 (low 32 bits used)      */
     uint32_t flags;             /* FA_FLAG_*                                      */
     uint8_t* tile_visits;       /* device uint8[B][H][ceil(N/Br)][ceil(N/Bc)] with
-                                   (Br, Bc) from fa_tile_shape for the pass; every
-                                   entry is written (1 = tile visited) when
-                                   FA_FLAG_RECORD_TILES is set                  */
+                                   (Br, Bc) = fa_tile_shape(pass 0) for fa_fwd and
+                                   fa_tile_shape(pass 1) (the dK/dV kernel) for
+                                   fa_bwd; every entry is written (1 = tile
+                                   visited) when FA_FLAG_RECORD_TILES is set     */
+    uint8_t* tile_visits2;      /* fa_bwd only: the dQ kernel's map, shape from
+                                   fa_tile_shape(pass 2); may be NULL            */
     hipEvent_t main_begin;      /* profiling: when both are non-NULL they are    */
     hipEvent_t main_end;        /* recorded on `stream` right before and right
-                                   after the pass's main kernel (the forward
-                                   kernel, or the backward's S/P-recomputing
-                                   kernel without its pre- and post-pass)       */
+                                   after the pass's main kernels (the forward
+                                   kernel; the backward's two S/P-recomputing
+                                   kernels, without the D pre-pass)             */
 } fa_opts;
 
 /* Forward pass.  Q, K, V: [B][H][N][d] of `dtype`.  O: [B][H][N][d] of
@@ -117,9 +120,8 @@ fa_status fa_fwd(const void* Q, const void* K, const void* V, void* O, float* LS
                  float scale, int32_t causal, float dropout_p, uint64_t seed,
                  const uint8_t* block_mask, const fa_opts* opts, hipStream_t stream);
 
-/* Bytes of device workspace fa_bwd needs: an fp32 dQ accumulator
- * [B][H][N][d] followed by D = rowsum(dO o O) float [B][H][N], each part
- * 256-byte aligned.  Returns 0 for invalid sizes. */
+/* Bytes of device workspace fa_bwd needs: D = rowsum(dO o O) as float
+ * [B][H][N], rounded up to 256 bytes.  Returns 0 for invalid sizes. */
 size_t fa_bwd_workspace_bytes(int32_t B, int32_t H, int32_t N, int32_t d);
 
 /* Backward pass.  Q, K, V, dO: [B][H][N][d] of `dtype`; O as the forward
@@ -144,10 +146,10 @@ fa_status fa_dropout_keep_mask(uint64_t seed, uint64_t rng_offset, float dropout
                                int32_t B, int32_t H, int32_t N, uint8_t* keep,
                                hipStream_t stream);
 
-/* Tile shape (rows Br of queries, columns Bc of keys) the given pass
- * (0 = forward, 1 = backward) uses for head dim d and dtype; these index
- * the tile-visit map.  Both divide 128, so a tile lies inside one block of
- * the 128 x 128 block mask. */
+/* Tile shape (rows Br of queries, columns Bc of keys) a kernel uses for head
+ * dim d and dtype: pass 0 = forward, 1 = backward dK/dV kernel, 2 = backward
+ * dQ kernel; these index the tile-visit maps.  Both divide 128, so a tile lies
+ * inside one block of the 128 x 128 block mask. */
 fa_status fa_tile_shape(int32_t d, fa_dtype dtype, int32_t pass, int32_t* Br, int32_t* Bc);
 
 /* Static description of a status code. */

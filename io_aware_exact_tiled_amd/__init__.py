@@ -64,9 +64,14 @@ def _opts(B, H, N, d, pass_, key_lens, rng_offset, o_fp32, record_tiles, reverse
     opts.rng_offset = int(rng_offset)
     tiles = None
     if record_tiles:
-        br, bc = tile_shape(d, dtype_code, pass_)
-        tiles = torch.full((B, H, -(-N // br), -(-N // bc)), 7, dtype=torch.uint8, device=device)
-        opts.tile_visits = tiles.data_ptr()
+        maps = []
+        for p in ((0,) if pass_ == 0 else (1, 2)):
+            br, bc = tile_shape(d, dtype_code, p)
+            maps.append(torch.full((B, H, -(-N // br), -(-N // bc)), 7, dtype=torch.uint8, device=device))
+        opts.tile_visits = maps[0].data_ptr()
+        if len(maps) > 1:
+            opts.tile_visits2 = maps[1].data_ptr()
+        tiles = maps[0] if pass_ == 0 else tuple(maps)
         opts.flags |= _lib.FA_FLAG_RECORD_TILES
     if reverse_kv:
         opts.flags |= _lib.FA_FLAG_REVERSE_KV
@@ -115,7 +120,8 @@ def bwd_workspace_bytes(B, H, N, d) -> int:
 def bwd(q, k, v, o, do, lse, *, causal=False, dropout_p=0.0, seed=0, rng_offset=0, key_lens=None,
         block_mask=None, scale: Optional[float] = None, record_tiles=False, workspace=None, grads=None,
         events=None):
-    """Backward pass.  Returns (dQ, dK, dV) [+ tile_visits], in q's dtype.
+    """Backward pass.  Returns (dQ, dK, dV) in q's dtype, plus, when
+    record_tiles is set, the (dK/dV kernel, dQ kernel) tile-visit maps.
     O may be fp32 (if the forward wrote it so) or q's dtype."""
     _check_qkv(q, k, v, do)
     B, H, N, d = q.shape

@@ -35,6 +35,7 @@ class FaOpts(ctypes.Structure):
         ("rng_offset", ctypes.c_uint64),
         ("flags", ctypes.c_uint32),
         ("tile_visits", ctypes.c_void_p),
+        ("tile_visits2", ctypes.c_void_p),
         ("main_begin", ctypes.c_void_p),
         ("main_end", ctypes.c_void_p),
     ]

@@ -105,7 +105,12 @@ fa_status fa_tile_shape(int32_t d, fa_dtype dtype, int32_t pass, int32_t* Br, in
     if (d != 64 && d != 128) return FA_ERR_HEAD_DIM;
     if (!valid_dtype(dtype)) return FA_ERR_DTYPE;
     if (pass == 0) { *Br = fa::FWD_BR; *Bc = fa::FWD_BC; return FA_OK; }
-    if (pass == 1) { *Br = fa::BWD_BR; *Bc = fa::BWD_BC; return FA_OK; }
+    if (pass == 1) {
+        *Br = dtype == FA_F32 ? fa::BWD_KV_BR32 : fa::BWD_KV_BR16;
+        *Bc = fa::BWD_KV_BC;
+        return FA_OK;
+    }
+    if (pass == 2) { *Br = fa::BWD_DQ_BR; *Bc = fa::BWD_DQ_BC; return FA_OK; }
     return FA_ERR_OPTS;
 }
 
@@ -135,7 +140,7 @@ fa_status fa_fwd(const void* Q, const void* K, const void* V, void* O, float* LS
 size_t fa_bwd_workspace_bytes(int32_t B, int32_t H, int32_t N, int32_t d) {
     if (check_shape(B, H, N, d) != FA_OK) return 0;
     const size_t rows = (size_t)B * H * N;
-    return align256(rows * d * sizeof(float)) + align256(rows * sizeof(float));
+    return align256(rows * sizeof(float));
 }
 
 fa_status fa_bwd(const void* Q, const void* K, const void* V, const void* O, const void* dO, const float* LSE,
@@ -152,19 +157,19 @@ fa_status fa_bwd(const void* Q, const void* K, const void* V, const void* O, con
     const size_t need = fa_bwd_workspace_bytes(B, H, N, d);
     if (!workspace || workspace_bytes < need || (reinterpret_cast<uintptr_t>(workspace) & 255u))
         return FA_ERR_WORKSPACE;
-    const size_t rows = (size_t)B * H * N;
     fa::BwdArgs a;
     a.q = Q; a.k = K; a.v = V; a.o = O; a.dout = dO; a.lse = LSE;
     a.dq = dQ; a.dk = dK; a.dv = dV;
-    a.dq_acc = static_cast<float*>(workspace);
-    a.delta = reinterpret_cast<float*>(static_cast<char*>(workspace) + align256(rows * d * sizeof(float)));
+    a.delta = static_cast<float*>(workspace);
     a.B = B; a.H = H; a.N = N;
     a.scale = scale;
     a.scale_log2 = scale * LOG2E;
     a.o_f32 = (opts && opts->o_fp32) ? 1 : 0;
     a.mask = mask_args(N, causal, block_mask, opts);
     a.drop = drop_args(dropout_p, seed, opts);
-    a.tile_visits = (opts && (opts->flags & FA_FLAG_RECORD_TILES)) ? opts->tile_visits : nullptr;
+    const bool rec = opts && (opts->flags & FA_FLAG_RECORD_TILES);
+    a.tile_visits = rec ? opts->tile_visits : nullptr;
+    a.tile_visits2 = rec ? opts->tile_visits2 : nullptr;
     a.ev_begin = (opts && opts->main_end) ? opts->main_begin : nullptr;
     a.ev_end = (opts && opts->main_begin) ? opts->main_end : nullptr;
     const hipError_t e = fa::launch_bwd(a, dtype, d, stream);

@@ -5,28 +5,36 @@
 // matrix (FlashAttention summary, xyznot.com, core ideas, recomputation;
 // azimuth.plus explainer, "three ideas in one kernel", recomputation).  The
 // gradients follow from the definition with the softmax Jacobian:
-//     D_i = sum_k dO_ik O_ik                (pre-pass)
-//     P   = exp(S - LSE_i)                  recomputed per tile
-//     dV_j += (P o Z / (1-p))^T dO_i
-//     dP   = (dO_i V_j^T) o Z / (1-p)
-//     dS   = P o (dP - D_i)
-//     dK_j += scale dS^T Q_i,   dQ_i += scale dS K_j
+//     D_i = sum_k dO_ik O_ik                          pre-pass
+//     P   = exp(S - LSE_i)                            recomputed per tile
+//     dV_j = sum_i (P o Z / (1-p))_ij dO_i
+//     dP   = (dO V^T) o Z / (1-p),   dS = P o (dP - D)
+//     dK_j = scale sum_i dS_ij Q_i,  dQ_i = scale sum_j dS_ij K_j
 //
 // Kernels, in launch order on the caller's stream:
-//   1. bwd_pre:   D = rowsum(dO o O) (fp32) and the fp32 dQ accumulator set to 0.
-//   2. bwd_main:  one workgroup (4 waves) per 128 keys of one (b, h); each wave
-//                 owns 32 keys and keeps K_j, V_j in registers and dK_j, dV_j
-//                 in fp32 accumulators.  It walks the query tiles of 32 rows
-//                 that hold a valid pair.  dQ contributions go through LDS
-//                 (dS) and fp32 atomic adds into the workspace.
-//   3. bwd_dq:    dQ = scale * accumulator, rounded to the input dtype.
+//   1. bwd_pre:  D = rowsum(dO o O) in fp32 (workspace).
+//   2. bwd_kv:   one workgroup (4 waves) per 128 keys of one (b, h); each wave
+//                owns 32 keys, keeps K_j, V_j as MFMA operands in registers and
+//                dK_j, dV_j in fp32 accumulators, and walks the query tiles of
+//                BR rows that hold a valid pair: S = Q K^T, dP = dO V^T,
+//                dV += P^T dO, dK += dS^T Q.
+//   3. bwd_dq:   one workgroup (4 waves) per 128 query rows; each wave owns 32
+//                rows (one per lane column, with its LSE_i and D_i in
+//                registers) and walks the key tiles of 32 that hold a valid
+//                pair: S^T = K Q^T, dP^T = V dO^T, dQ^T += K^T dS^T.
+// dQ is therefore produced without atomics and without a dS round trip
+// through memory, at the price of recomputing S and dP once more (seven
+// products per pair instead of five).  Both loops prefetch the next tile into
+// registers while the current one is computed and keep two LDS buffers (one
+// barrier per tile).
 //
-// Layout choices (MI355X-specific): S and dP are computed with queries on the
-// MFMA rows and keys on the columns, so each lane holds one key and 16
-// consecutive queries (query rows are staged in LDS in MFMA row order, as in
-// the forward kernel).  Those registers are directly the A operand of
-// dV += P^T dO and dK += dS^T Q; the B operands dO and Q are staged a second
-// time transposed (d rows, query columns).
+// Layouts (MI355X-specific): bwd_kv computes S with queries on the MFMA rows
+// and keys on the columns (query rows staged in LDS in MFMA row order so each
+// lane holds 16 consecutive queries of its key: these registers are directly
+// the A operand of dV += P^T dO and dK += dS^T Q; Q and dO are staged a second
+// time transposed for the B operands).  bwd_dq is the forward kernel's layout:
+// keys on the rows (K, V in MFMA row order), one query per lane, K staged a
+// second time transposed for dQ^T += K^T dS^T.
 #include "fa_device.hpp"
 #include "fa_internal.hpp"
 
@@ -59,14 +67,23 @@ template <class T> __device__ inline typename Mma<T>::frag pack_f(const float* p
     }
 }
 
+// MFMA row slot of row r within its 32-row block: slot m holds row
+// 16*((m/4)%2) + 4*(m/8) + m%4, so accumulator register r of lane half h is
+// row 16*h + r.
 __device__ inline int row_slot(int r) {
     return (r & ~31) | (((r >> 2) & 3) * 8 + ((r >> 4) & 1) * 4 + (r & 3));
+}
+
+__device__ inline int clamp_len(const int32_t* key_lens, int b, int N) {
+    if (!key_lens) return N;
+    const int L = key_lens[b];
+    return L < 0 ? 0 : (L > N ? N : L);
 }
 
 }  // namespace
 
 // ---------------------------------------------------------------------------
-// D = rowsum(dO o O); dQ accumulator = 0.  8 consecutive elements per lane.
+// D = rowsum(dO o O) in fp32.  8 consecutive elements per lane.
 template <class T, int D>
 __global__ __launch_bounds__(256) void bwd_pre_kernel(BwdArgs a) {
     constexpr int LPR = D / 8;                 // lanes per row
@@ -103,10 +120,6 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(BwdArgs a) {
         }
 #pragma unroll
         for (int e = 0; e < 8; ++e) acc = fmaf(g[e], o[e], acc);
-        float* dq = a.dq_acc + row * D + c0;
-        const f32x4 z = {0.f, 0.f, 0.f, 0.f};
-        *reinterpret_cast<f32x4*>(dq) = z;
-        *reinterpret_cast<f32x4*>(dq + 4) = z;
     }
 #pragma unroll
     for (int s = LPR / 2; s >= 1; s >>= 1) acc += __shfl_xor(acc, s, WAVE);
@@ -114,35 +127,43 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(BwdArgs a) {
 }
 
 // ---------------------------------------------------------------------------
+// dK, dV: key-stationary.
 template <class T, int D, bool DROP>
-__global__ __launch_bounds__(256, 1) void bwd_main_kernel(BwdArgs a) {
+__global__ __launch_bounds__(256, 1) void bwd_kv_kernel(BwdArgs a) {
     typedef Mma<T> MM;
     constexpr int E = MM::E;
-    constexpr int BR = BWD_BR, BC = BWD_BC;       // 32 queries per step, 128 keys per workgroup
+    constexpr int BR = BwdTiles<T>::KV_BR;        // query rows per step
+    constexpr int BC = BWD_KV_BC;                 // keys per workgroup
+    constexpr int QB = BR / 32;                   // 32-row query blocks per step
     constexpr int KS = D / (2 * E);               // MFMA steps over d
     constexpr int DB = D / 32;
-    constexpr int QU = 16 / E;                    // MFMA steps over the 32 queries
+    constexpr int QU = 16 / E;                    // MFMA steps over 16 queries of a lane half
     constexpr int EPU = 16 / (int)sizeof(T);
+    constexpr int DC = D / EPU;                   // 16-byte chunks per row
+    constexpr int NT = (BR / 4) * DC;             // staging tasks per tensor (4 rows x 1 chunk)
+    constexpr int NN = (NT + 255) / 256;
+    constexpr int TQ = BR * D;                    // elements per staged tensor
     typedef Swz<T, D> LQ;      // Q, dO natural: BR rows (MFMA row order) x D
     typedef Swz<T, BR> LT;     // Q^T, dO^T: D rows x BR queries
-    typedef Swz<T, BC> LS;     // dS: BR rows x BC keys;  K^T: D rows x BC keys
 
-    __shared__ __attribute__((aligned(16))) T sQ[BR * D];
-    __shared__ __attribute__((aligned(16))) T sdO[BR * D];
-    __shared__ __attribute__((aligned(16))) T sQt[D * BR];
-    __shared__ __attribute__((aligned(16))) T sdOt[D * BR];
-    __shared__ __attribute__((aligned(16))) T sdS[BR * BC];
-    __shared__ __attribute__((aligned(16))) T sKt[D * BC];
-    __shared__ float sLse[BR];
-    __shared__ float sDel[BR];
+    __shared__ __attribute__((aligned(16))) T sQ[2 * TQ];
+    __shared__ __attribute__((aligned(16))) T sdO[2 * TQ];
+    __shared__ __attribute__((aligned(16))) T sQt[2 * TQ];
+    __shared__ __attribute__((aligned(16))) T sdOt[2 * TQ];
+    __shared__ __attribute__((aligned(16))) float sLse[2 * BR];
+    __shared__ __attribute__((aligned(16))) float sDel[2 * BR];
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int hl = lane >> 5, ln = lane & 31;
     const int N = a.N, H = a.H;
     const int Tr = (N + BR - 1) / BR, Tc = (N + BC - 1) / BC;
-    const int jt = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+    const int total = Tc * H * a.B;
+    const int item = xcd_item((int)blockIdx.x, (total + 7) / 8);
+    if (item >= total) return;
+    const int bhi = item / Tc;
+    const int jt = item % Tc;                     // key tile of this workgroup
     const int kbase = jt * BC, kw0 = kbase + wave * 32;
-    const size_t bh = (size_t)b * H + h;
+    const size_t bh = (size_t)bhi;
     const size_t hoff = bh * (size_t)N * D;
     const T* __restrict__ Qg = (const T*)a.q + hoff;
     const T* __restrict__ Kg = (const T*)a.k + hoff;
@@ -150,23 +171,22 @@ __global__ __launch_bounds__(256, 1) void bwd_main_kernel(BwdArgs a) {
     const T* __restrict__ dOg = (const T*)a.dout + hoff;
     const float* __restrict__ lseg = a.lse + bh * N;
     const float* __restrict__ delg = a.delta + bh * N;
-    float* __restrict__ dqacc = a.dq_acc + hoff;
 
-    int kend = N;
-    if (a.mask.key_lens) {
-        const int L = a.mask.key_lens[b];
-        kend = L < 0 ? 0 : (L > N ? N : L);
-    }
+    const int kend = clamp_len(a.mask.key_lens, bhi / H, N);
     const int causal = a.mask.causal;
-    const int i_begin = (causal && kbase < kend) ? kbase / BR : 0;
-    const int i_end = (kbase < kend) ? Tr : 0;          // all keys padded: nothing to do
+    const bool live = kbase < kend;
+    const int i_begin = (causal && live) ? kbase / BR : 0;
+    const int i_end = live ? Tr : 0;
+    const uint8_t* bmcol = a.mask.block_mask ? a.mask.block_mask + (kbase / MASK_TILE) : nullptr;
+    auto tile_at = [&](int i) -> int {   // next visited query tile >= i, or -1
+        for (; i < i_end; ++i)
+            if (!bmcol || bmcol[(size_t)((i * BR) / MASK_TILE) * a.mask.mask_T]) return i;
+        return -1;
+    };
 
-    // tile-visit map: this workgroup owns column jt of the [Tr][Tc] map
     uint8_t* vis = a.tile_visits ? a.tile_visits + bh * Tr * (size_t)Tc + jt : nullptr;
-    if (vis) {
-        for (int i = tid; i < Tr; i += 256)
-            if (i < i_begin || i >= i_end) vis[(size_t)i * Tc] = 0;
-    }
+    if (vis)
+        for (int i = tid; i < Tr; i += 256) vis[(size_t)i * Tc] = 0;
 
     const int krow = kw0 + ln;           // this lane's key
     typename MM::frag kf[KS], vf[KS];
@@ -180,156 +200,139 @@ __global__ __launch_bounds__(256, 1) void bwd_main_kernel(BwdArgs a) {
 #pragma unroll
     for (int db = 0; db < DB; ++db) { dk[db] = zero16(); dv[db] = zero16(); }
 
-    // K^T for the dQ product: D rows x 128 keys
-    if (i_begin < i_end) {
-        constexpr int DC = D / EPU;
-        for (int t = tid; t < (BC / 4) * DC; t += 256) {
-            const int dc = t % DC, kg = t / DC;
-            T x[4][EPU];
+    // ---- staging of one query tile: Q, dO (4 rows x 16 bytes per task), LSE, D
+    u32x4 qreg[NN][4], oreg[NN][4];
+    float lreg = 0.0f;
+    auto load_tile = [&](int i) {
+        const int q0 = i * BR;
+#pragma unroll
+        for (int n = 0; n < NN; ++n) {
+            const int t = tid + n * 256;
+            const int dc = t % DC, rg = t / DC;
 #pragma unroll
             for (int kk = 0; kk < 4; ++kk) {
-                const int key = kbase + kg * 4 + kk;
-                u32x4 val = {0u, 0u, 0u, 0u};
-                if (key < N) val = *reinterpret_cast<const u32x4*>(Kg + (size_t)key * D + dc * EPU);
-                *reinterpret_cast<u32x4*>(&x[kk][0]) = val;
+                const int q = q0 + rg * 4 + kk;
+                const bool ok = t < NT && q < N;
+                const u32x4 z = {0u, 0u, 0u, 0u};
+                qreg[n][kk] = ok ? *reinterpret_cast<const u32x4*>(Qg + (size_t)q * D + dc * EPU) : z;
+                oreg[n][kk] = ok ? *reinterpret_cast<const u32x4*>(dOg + (size_t)q * D + dc * EPU) : z;
             }
+        }
+        if (tid < 2 * BR) {
+            const int q = q0 + (tid % BR);
+            lreg = (q < N) ? (tid < BR ? lseg[q] : delg[q]) : (tid < BR ? INFINITY : 0.0f);
+        }
+    };
+    auto store_tile = [&](int buf) {
+        T* q = sQ + buf * TQ;
+        T* o = sdO + buf * TQ;
+        T* qt = sQt + buf * TQ;
+        T* ot = sdOt + buf * TQ;
 #pragma unroll
-            for (int dd = 0; dd < EPU; ++dd)
-                store4g<T>(sKt + LS::off(dc * EPU + dd, kg * 4), to_f32(x[0][dd]), to_f32(x[1][dd]),
-                           to_f32(x[2][dd]), to_f32(x[3][dd]));
-        }
-    }
-
-    const float c = a.scale_log2;
-    const float LOG2E = 1.4426950408889634f;
-    const uint8_t* bmcol = a.mask.block_mask ? a.mask.block_mask + (kbase / MASK_TILE) : nullptr;
-
-    for (int i = i_begin; i < i_end; ++i) {
-        const int q0 = i * BR;
-        if (bmcol && bmcol[(size_t)(q0 / MASK_TILE) * a.mask.mask_T] == 0) {
-            if (vis && tid == 0) vis[(size_t)i * Tc] = 0;
-            continue;
-        }
-        if (vis && tid == 0) vis[(size_t)i * Tc] = 1;
-
-        __syncthreads();   // previous step's LDS readers are done
-        // ---- stage Q_i, dO_i (natural, MFMA row order) and transposed, plus LSE, D
-        {
-            constexpr int DC = D / EPU;
-            for (int t = tid; t < 2 * (BR / 4) * DC; t += 256) {
-                const int which = t / ((BR / 4) * DC);          // 0: Q, 1: dO
-                const int tt = t % ((BR / 4) * DC);
-                const int dc = tt % DC, qg = tt / DC;
-                const T* src = which ? dOg : Qg;
-                T* nat = which ? sdO : sQ;
-                T* tr = which ? sdOt : sQt;
-                T x[4][EPU];
+        for (int n = 0; n < NN; ++n) {
+            const int t = tid + n * 256;
+            if (t < NT) {
+                const int dc = t % DC, rg = t / DC;
 #pragma unroll
                 for (int kk = 0; kk < 4; ++kk) {
-                    const int r = qg * 4 + kk;
-                    const int q = q0 + r;
-                    u32x4 val = {0u, 0u, 0u, 0u};
-                    if (q < N) val = *reinterpret_cast<const u32x4*>(src + (size_t)q * D + dc * EPU);
-                    *reinterpret_cast<u32x4*>(&x[kk][0]) = val;
-                    *reinterpret_cast<u32x4*>(nat + LQ::off(row_slot(r), dc * EPU)) = val;
+                    *reinterpret_cast<u32x4*>(q + LQ::off(row_slot(rg * 4 + kk), dc * EPU)) = qreg[n][kk];
+                    *reinterpret_cast<u32x4*>(o + LQ::off(row_slot(rg * 4 + kk), dc * EPU)) = oreg[n][kk];
                 }
-#pragma unroll
-                for (int dd = 0; dd < EPU; ++dd)
-                    store4g<T>(tr + LT::off(dc * EPU + dd, qg * 4), to_f32(x[0][dd]), to_f32(x[1][dd]),
-                               to_f32(x[2][dd]), to_f32(x[3][dd]));
-            }
-            if (tid < BR) {
-                const int q = q0 + tid;
-                sLse[tid] = q < N ? lseg[q] * LOG2E : INFINITY;
-                sDel[tid] = q < N ? delg[q] : 0.0f;
+                store_transposed4<T>(qreg[n], [&](int c) { return qt + LT::off(dc * EPU + c, rg * 4); });
+                store_transposed4<T>(oreg[n], [&](int c) { return ot + LT::off(dc * EPU + c, rg * 4); });
             }
         }
-        __syncthreads();
+        if (tid < BR) sLse[buf * BR + tid] = lreg * 1.4426950408889634f;
+        else if (tid < 2 * BR) sDel[buf * BR + tid - BR] = lreg;
+    };
 
-        const bool wave_live = !(causal && kw0 > q0 + BR - 1) && kw0 < kend;
-        if (wave_live) {
-            // ---- S = Q_i K_j^T and dP_hat = dO_i V_j^T (queries on rows, keys on columns)
-            f32x16 s = zero16(), dp = zero16();
-#pragma unroll
-            for (int ks = 0; ks < KS; ++ks) {
-                const typename MM::frag aq = load_frag<T>(sQ + LQ::off(ln, ks * 2 * E + hl * E));
-                s = MM::mma(aq, kf[ks], s);
-                const typename MM::frag ao = load_frag<T>(sdO + LQ::off(ln, ks * 2 * E + hl * E));
-                dp = MM::mma(ao, vf[ks], dp);
-            }
-            // lane holds key krow and queries q0 + hl*16 + r
-            float lse2[16], del[16];
-#pragma unroll
-            for (int r = 0; r < 16; ++r) { lse2[r] = sLse[hl * 16 + r]; del[r] = sDel[hl * 16 + r]; }
-            float p[16], pd[16], ds[16];
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const int q = q0 + hl * 16 + r;
-                const bool valid = (q < N) && (krow < kend) && !(causal && krow > q);
-                p[r] = valid ? fast_exp2(fmaf(s[r], c, -lse2[r])) : 0.0f;
-            }
-            if constexpr (DROP) {
-#pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    const uint32_t q = (uint32_t)(q0 + hl * 16 + r);
-                    const uint32_t bits = keep4((uint32_t)krow >> 2, q, (uint32_t)bh, a.drop.off, a.drop.k0,
-                                                a.drop.k1, a.drop.thr);
-                    const float z = ((bits >> (krow & 3)) & 1u) ? a.drop.keep_scale : 0.0f;
-                    pd[r] = p[r] * z;
-                    ds[r] = p[r] * (dp[r] * z - del[r]);
-                }
-            } else {
-#pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    pd[r] = p[r];
-                    ds[r] = p[r] * (dp[r] - del[r]);
-                }
-            }
-            // ---- dV_j += Pd^T dO_i ;  dK_j += dS^T Q_i
-#pragma unroll
-            for (int u = 0; u < QU; ++u) {
-                const typename MM::frag ap = pack_f<T>(&pd[u * E]);
-                const typename MM::frag as = pack_f<T>(&ds[u * E]);
-#pragma unroll
-                for (int db = 0; db < DB; ++db) {
-                    const typename MM::frag bo = load_frag<T>(sdOt + LT::off(db * 32 + ln, hl * 16 + u * E));
-                    dv[db] = MM::mma(ap, bo, dv[db]);
-                    const typename MM::frag bq = load_frag<T>(sQt + LT::off(db * 32 + ln, hl * 16 + u * E));
-                    dk[db] = MM::mma(as, bq, dk[db]);
-                }
-            }
-            // ---- dS to LDS for the dQ product (rows = queries, cols = keys)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) sdS[LS::off(hl * 16 + r, wave * 32 + ln)] = (T)ds[r];
-        } else {
-#pragma unroll
-            for (int r = 0; r < 16; ++r) sdS[LS::off(hl * 16 + r, wave * 32 + ln)] = (T)0.0f;
-        }
-        __syncthreads();
+    const float c = a.scale_log2;
+    int i = tile_at(i_begin);
+    if (i >= 0) {
+        load_tile(i);
+        store_tile(0);
+    }
+    __syncthreads();
+    int buf = 0;
+    while (i >= 0) {
+        const int q0 = i * BR;
+        if (vis && tid == 0) vis[(size_t)i * Tc] = 1;
+        const int in = tile_at(i + 1);
+        if (in >= 0) load_tile(in);
 
-        // ---- dQ_i += dS K_j : output 32 x D split over the waves
-        {
-            constexpr int SPLIT = (DB >= 4) ? 1 : 4 / DB;      // waves sharing one column block
-            constexpr int KEYS = BC / SPLIT;
-            const int db = wave % DB;
-            const int kpart = (wave / DB) % SPLIT;
-            if (wave < DB * SPLIT) {
-                f32x16 acc = zero16();
+        {   // no per-wave skip: a wave whose keys all lie above this tile's rows (first
+            // causal step only) or past the key length runs the edge path with P = 0,
+            // which keeps dK, dV in the MFMA accumulators across the loop
+            const T* q = sQ + buf * TQ;
+            const T* o = sdO + buf * TQ;
+            const T* qt = sQt + buf * TQ;
+            const T* ot = sdOt + buf * TQ;
+            const float* ls = sLse + buf * BR;
+            const float* dl = sDel + buf * BR;
+            const bool edge = (causal && kw0 + 31 > q0) || (kw0 + 32 > kend) || (q0 + BR > N);
 #pragma unroll
-                for (int ks = 0; ks < KEYS / (2 * E); ++ks) {
-                    const int kc = kpart * KEYS + ks * 2 * E + hl * E;
-                    const typename MM::frag as = load_frag<T>(sdS + LS::off(ln, kc));
-                    const typename MM::frag bk = load_frag<T>(sKt + LS::off(db * 32 + ln, kc));
-                    acc = MM::mma(as, bk, acc);
+            for (int qb = 0; qb < QB; ++qb) {
+                // S = Q K^T, dP_hat = dO V^T: lane holds key krow, queries q0 + 32qb + 16hl + r
+                f32x16 s = zero16(), dp = zero16();
+#pragma unroll
+                for (int ks = 0; ks < KS; ++ks) {
+                    const typename MM::frag aq = load_frag<T>(q + LQ::off(qb * 32 + ln, ks * 2 * E + hl * E));
+                    s = MM::mma(aq, kf[ks], s);
+                    const typename MM::frag ao = load_frag<T>(o + LQ::off(qb * 32 + ln, ks * 2 * E + hl * E));
+                    dp = MM::mma(ao, vf[ks], dp);
                 }
-                const int dcol = db * 32 + ln;
+                const int qr0 = qb * 32 + hl * 16;     // first query of this lane half, tile-local
+                float lsv[16], dlv[16];
+#pragma unroll
+                for (int g = 0; g < 4; ++g) {
+                    const f32x4 l4 = *reinterpret_cast<const f32x4*>(ls + qr0 + 4 * g);
+                    const f32x4 d4 = *reinterpret_cast<const f32x4*>(dl + qr0 + 4 * g);
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) { lsv[4 * g + e] = l4[e]; dlv[4 * g + e] = d4[e]; }
+                }
+                float pd[16], ds[16], p[16];
+#pragma unroll
+                for (int r = 0; r < 16; ++r) p[r] = fast_exp2(fmaf(s[r], c, -lsv[r]));
+                if (__builtin_expect(edge, 0)) {
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) {
+                        const int qq = q0 + qr0 + r;
+                        if (qq >= N || krow >= kend || (causal && krow > qq)) p[r] = 0.0f;
+                    }
+                }
 #pragma unroll
                 for (int r = 0; r < 16; ++r) {
-                    const int q = q0 + 8 * (r / 4) + 4 * hl + (r % 4);
-                    if (q < N) unsafeAtomicAdd(dqacc + (size_t)q * D + dcol, acc[r]);
+                    float dpr = dp[r];
+                    if constexpr (DROP) {
+                        const uint32_t bits = keep4((uint32_t)krow >> 2, (uint32_t)(q0 + qr0 + r), (uint32_t)bh,
+                                                    a.drop.off, a.drop.k0, a.drop.k1, a.drop.thr);
+                        const float z = ((bits >> (krow & 3)) & 1u) ? a.drop.keep_scale : 0.0f;
+                        pd[r] = p[r] * z;
+                        dpr *= z;
+                    } else {
+                        pd[r] = p[r];
+                    }
+                    ds[r] = p[r] * (dpr - dlv[r]);
+                }
+                // dV_j += Pd^T dO_i ; dK_j += dS^T Q_i
+#pragma unroll
+                for (int u = 0; u < QU; ++u) {
+                    const typename MM::frag ap = pack_f<T>(&pd[u * E]);
+                    const typename MM::frag as = pack_f<T>(&ds[u * E]);
+#pragma unroll
+                    for (int db = 0; db < DB; ++db) {
+                        const typename MM::frag bo = load_frag<T>(ot + LT::off(db * 32 + ln, qr0 + u * E));
+                        dv[db] = MM::mma(ap, bo, dv[db]);
+                        const typename MM::frag bq = load_frag<T>(qt + LT::off(db * 32 + ln, qr0 + u * E));
+                        dk[db] = MM::mma(as, bq, dk[db]);
+                    }
                 }
             }
         }
+        if (in >= 0) store_tile(buf ^ 1);
+        __syncthreads();
+        buf ^= 1;
+        i = in;
     }
 
     // ---- dK_j = scale * acc, dV_j = acc (lane holds column db*32+ln, rows = keys)
@@ -348,12 +351,191 @@ __global__ __launch_bounds__(256, 1) void bwd_main_kernel(BwdArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-template <class T>
-__global__ __launch_bounds__(256) void bwd_dq_kernel(const float* __restrict__ acc, T* __restrict__ dq,
-                                                     size_t n, float scale) {
-    for (size_t i = ((size_t)blockIdx.x * 256 + threadIdx.x) * 4; i < n; i += (size_t)gridDim.x * 256 * 4) {
-        const f32x4 x = *reinterpret_cast<const f32x4*>(acc + i);
-        store4g<T>(dq + i, x[0] * scale, x[1] * scale, x[2] * scale, x[3] * scale);
+// dQ: query-stationary.
+template <class T, int D, bool DROP>
+__global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdArgs a) {
+    typedef Mma<T> MM;
+    constexpr int E = MM::E;
+    constexpr int BR = BWD_DQ_BR, BC = BWD_DQ_BC;   // 128 query rows, 32-key tiles
+    constexpr int KS = D / (2 * E);
+    constexpr int DB = D / 32;
+    constexpr int PU = 16 / E;
+    constexpr int EPU = 16 / (int)sizeof(T);
+    constexpr int DC = D / EPU;
+    constexpr int NT = (BC / 4) * DC;               // staging tasks per tensor
+    constexpr int NN = (NT + 255) / 256;
+    constexpr int TK = BC * D;
+    typedef Swz<T, D> LK;      // K, V: BC rows (MFMA row order) x D
+    typedef Swz<T, BC> LT;     // K^T: D rows x BC keys
+
+    __shared__ __attribute__((aligned(16))) T sK[2 * TK];
+    __shared__ __attribute__((aligned(16))) T sV[2 * TK];
+    __shared__ __attribute__((aligned(16))) T sKt[2 * TK];
+
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int hl = lane >> 5, ln = lane & 31;
+    const int N = a.N, H = a.H;
+    const int Tr = (N + BR - 1) / BR, Tc = (N + BC - 1) / BC;
+    const int total = Tr * H * a.B;
+    const int item = xcd_item((int)blockIdx.x, (total + 7) / 8);
+    if (item >= total) return;
+    const int bhi = item / Tr, r_ = item % Tr;
+    const int it = a.mask.causal ? (Tr - 1 - r_) : r_;
+    const int q0 = it * BR, qw0 = q0 + wave * 32;
+    const size_t bh = (size_t)bhi;
+    const size_t hoff = bh * (size_t)N * D;
+    const T* __restrict__ Qg = (const T*)a.q + hoff;
+    const T* __restrict__ Kg = (const T*)a.k + hoff;
+    const T* __restrict__ Vg = (const T*)a.v + hoff;
+    const T* __restrict__ dOg = (const T*)a.dout + hoff;
+
+    const int kend = clamp_len(a.mask.key_lens, bhi / H, N);
+    const int causal = a.mask.causal;
+    int j_end = min(Tc, (kend + BC - 1) / BC);
+    if (causal) j_end = min(j_end, (min(q0 + BR, N) - 1) / BC + 1);
+    const uint8_t* bmask = a.mask.block_mask ? a.mask.block_mask + (size_t)(q0 / MASK_TILE) * a.mask.mask_T
+                                             : nullptr;
+    auto tile_at = [&](int j) -> int {
+        for (; j < j_end; ++j)
+            if (!bmask || bmask[(j * BC) / MASK_TILE]) return j;
+        return -1;
+    };
+
+    uint8_t* vis = a.tile_visits2 ? a.tile_visits2 + (bh * Tr + it) * (size_t)Tc : nullptr;
+    if (vis)
+        for (int j = tid; j < Tc; j += 256) vis[j] = 0;
+
+    // this lane's query row: Q and dO rows as B operands, LSE and D as scalars
+    const int qrow = qw0 + ln;
+    const bool qok = qrow < N;
+    typename MM::frag qf[KS], of[KS];
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+        qf[ks] = qok ? load_frag<T>(Qg + (size_t)qrow * D + ks * 2 * E + hl * E) : zero_frag<T>();
+        of[ks] = qok ? load_frag<T>(dOg + (size_t)qrow * D + ks * 2 * E + hl * E) : zero_frag<T>();
+    }
+    const float lse2 = qok ? a.lse[bh * N + qrow] * 1.4426950408889634f : INFINITY;
+    const float del = qok ? a.delta[bh * N + qrow] : 0.0f;
+    f32x16 dq[DB];
+#pragma unroll
+    for (int db = 0; db < DB; ++db) dq[db] = zero16();
+
+    u32x4 kreg[NN][4], vreg[NN][4];
+    auto load_tile = [&](int j) {
+        const int kv0 = j * BC;
+#pragma unroll
+        for (int n = 0; n < NN; ++n) {
+            const int t = tid + n * 256;
+            const int dc = t % DC, rg = t / DC;
+#pragma unroll
+            for (int kk = 0; kk < 4; ++kk) {
+                const int key = kv0 + rg * 4 + kk;
+                const bool ok = t < NT && key < N;
+                const u32x4 z = {0u, 0u, 0u, 0u};
+                kreg[n][kk] = ok ? *reinterpret_cast<const u32x4*>(Kg + (size_t)key * D + dc * EPU) : z;
+                vreg[n][kk] = ok ? *reinterpret_cast<const u32x4*>(Vg + (size_t)key * D + dc * EPU) : z;
+            }
+        }
+    };
+    auto store_tile = [&](int buf) {
+        T* k = sK + buf * TK;
+        T* v = sV + buf * TK;
+        T* kt = sKt + buf * TK;
+#pragma unroll
+        for (int n = 0; n < NN; ++n) {
+            const int t = tid + n * 256;
+            if (t < NT) {
+                const int dc = t % DC, rg = t / DC;
+#pragma unroll
+                for (int kk = 0; kk < 4; ++kk) {
+                    *reinterpret_cast<u32x4*>(k + LK::off(row_slot(rg * 4 + kk), dc * EPU)) = kreg[n][kk];
+                    *reinterpret_cast<u32x4*>(v + LK::off(row_slot(rg * 4 + kk), dc * EPU)) = vreg[n][kk];
+                }
+                store_transposed4<T>(kreg[n], [&](int cc) { return kt + LT::off(dc * EPU + cc, rg * 4); });
+            }
+        }
+    };
+
+    const float c = a.scale_log2;
+    int j = tile_at(0);
+    if (j >= 0) {
+        load_tile(j);
+        store_tile(0);
+    }
+    __syncthreads();
+    int buf = 0;
+    while (j >= 0) {
+        const int kv0 = j * BC;
+        if (vis && tid == 0) vis[j] = 1;
+        const int jn = tile_at(j + 1);
+        if (jn >= 0) load_tile(jn);
+
+        if (!(causal && kv0 > qw0 + 31)) {
+            const T* k = sK + buf * TK;
+            const T* v = sV + buf * TK;
+            const T* kt = sKt + buf * TK;
+            // S^T = K Q^T, dP_hat^T = V dO^T: lane holds query qrow, keys kv0 + 16hl + r
+            f32x16 s = zero16(), dp = zero16();
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks) {
+                const typename MM::frag ak = load_frag<T>(k + LK::off(ln, ks * 2 * E + hl * E));
+                s = MM::mma(ak, qf[ks], s);
+                const typename MM::frag av = load_frag<T>(v + LK::off(ln, ks * 2 * E + hl * E));
+                dp = MM::mma(av, of[ks], dp);
+            }
+            const bool edge = (kv0 + BC > kend) || (causal && kv0 + BC - 1 > qw0);
+            float ds[16];
+            uint32_t keep = 0xFFFFu;
+            if constexpr (DROP) {
+                const uint32_t g0 = (uint32_t)(kv0 + hl * 16) >> 2;
+                keep = 0;
+#pragma unroll
+                for (int g = 0; g < 4; ++g)
+                    keep |= keep4(g0 + g, (uint32_t)qrow, (uint32_t)bh, a.drop.off, a.drop.k0, a.drop.k1,
+                                  a.drop.thr) << (4 * g);
+            }
+            float p[16];
+#pragma unroll
+            for (int r = 0; r < 16; ++r) p[r] = fast_exp2(fmaf(s[r], c, -lse2));
+            if (__builtin_expect(edge, 0)) {
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const int key = kv0 + hl * 16 + r;
+                    if (key >= kend || (causal && key > qrow)) p[r] = 0.0f;
+                }
+            }
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                float dpr = dp[r];
+                if constexpr (DROP) dpr *= ((keep >> r) & 1u) ? a.drop.keep_scale : 0.0f;
+                ds[r] = p[r] * (dpr - del);
+            }
+            // dQ^T += K^T dS^T
+#pragma unroll
+            for (int u = 0; u < PU; ++u) {
+                const typename MM::frag bs = pack_f<T>(&ds[u * E]);
+#pragma unroll
+                for (int db = 0; db < DB; ++db) {
+                    const typename MM::frag akt = load_frag<T>(kt + LT::off(db * 32 + ln, hl * 16 + u * E));
+                    dq[db] = MM::mma(akt, bs, dq[db]);
+                }
+            }
+        }
+        if (jn >= 0) store_tile(buf ^ 1);
+        __syncthreads();
+        buf ^= 1;
+        j = jn;
+    }
+
+    // ---- dQ = scale * dQ^T (lane holds query qrow, columns db*32 + 8(r/4) + 4hl + r%4)
+    if (qok) {
+        T* dQg = (T*)a.dq + hoff + (size_t)qrow * D;
+#pragma unroll
+        for (int db = 0; db < DB; ++db)
+#pragma unroll
+            for (int g = 0; g < 4; ++g)
+                store4g<T>(dQg + db * 32 + 8 * g + 4 * hl, dq[db][4 * g] * a.scale, dq[db][4 * g + 1] * a.scale,
+                           dq[db][4 * g + 2] * a.scale, dq[db][4 * g + 3] * a.scale);
     }
 }
 
@@ -367,19 +549,17 @@ hipError_t launch_t(const BwdArgs& a, hipStream_t s) {
     hipError_t e = hipLaunchKernel((const void*)&bwd_pre_kernel<T, D>, dim3((unsigned)((rows + RPB - 1) / RPB)),
                                    dim3(256), args, 0, s);
     if (e != hipSuccess) return e;
-    dim3 grid((a.N + BWD_BC - 1) / BWD_BC, a.H, a.B);
+    const int kv_total = ((a.N + BWD_KV_BC - 1) / BWD_KV_BC) * a.H * a.B;
+    const int dq_total = ((a.N + BWD_DQ_BR - 1) / BWD_DQ_BR) * a.H * a.B;
     if (a.ev_begin && (e = hipEventRecord(a.ev_begin, s)) != hipSuccess) return e;
-    e = hipLaunchKernel((const void*)&bwd_main_kernel<T, D, DROP>, grid, dim3(256), args, 0, s);
+    e = hipLaunchKernel((const void*)&bwd_kv_kernel<T, D, DROP>, dim3((unsigned)(8 * ((kv_total + 7) / 8))),
+                        dim3(256), args, 0, s);
+    if (e != hipSuccess) return e;
+    e = hipLaunchKernel((const void*)&bwd_dq_kernel<T, D, DROP>, dim3((unsigned)(8 * ((dq_total + 7) / 8))),
+                        dim3(256), args, 0, s);
     if (e != hipSuccess) return e;
     if (a.ev_end && (e = hipEventRecord(a.ev_end, s)) != hipSuccess) return e;
-    const float* acc = a.dq_acc;
-    T* dq = (T*)a.dq;
-    size_t n = rows * D;
-    float scale = a.scale;
-    size_t blocks = (n / 4 + 255) / 256;
-    if (blocks > 8192) blocks = 8192;
-    void* args2[] = {(void*)&acc, (void*)&dq, (void*)&n, (void*)&scale};
-    return hipLaunchKernel((const void*)&bwd_dq_kernel<T>, dim3((unsigned)blocks), dim3(256), args2, 0, s);
+    return hipSuccess;
 }
 
 template <class T>

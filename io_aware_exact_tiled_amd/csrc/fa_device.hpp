@@ -153,6 +153,34 @@ __device__ inline float wave_xor32(float v) { return __shfl_xor(v, 32, WAVE); }
 
 __device__ inline float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// Transpose-and-store helper for staging: `x` holds 4 consecutive rows of a
+// tile, each as one 16-byte chunk (EPU elements); column c of that 4 x EPU
+// block (4 elements, rows 0..3) is written to dst(c), a pointer into a
+// transposed LDS tile.  16-bit elements are paired with byte permutes, no
+// float round trip.
+template <class T, class F>
+__device__ inline void store_transposed4(const u32x4 (&x)[4], F dst) {
+    if constexpr (sizeof(T) == 2) {
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+            // column 2w: low halves; column 2w+1: high halves
+            const uint32_t lo01 = __builtin_amdgcn_perm(x[1][w], x[0][w], 0x05040100u);
+            const uint32_t lo23 = __builtin_amdgcn_perm(x[3][w], x[2][w], 0x05040100u);
+            const uint32_t hi01 = __builtin_amdgcn_perm(x[1][w], x[0][w], 0x07060302u);
+            const uint32_t hi23 = __builtin_amdgcn_perm(x[3][w], x[2][w], 0x07060302u);
+            u32x2 a = {lo01, lo23}, b = {hi01, hi23};
+            *reinterpret_cast<u32x2*>(dst(2 * w)) = a;
+            *reinterpret_cast<u32x2*>(dst(2 * w + 1)) = b;
+        }
+    } else {
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+            u32x4 col = {x[0][w], x[1][w], x[2][w], x[3][w]};
+            *reinterpret_cast<u32x4*>(dst(w)) = col;
+        }
+    }
+}
+
 // Map a linear workgroup id to a work item so that each of the 8 XCDs (which
 // receive workgroups round-robin and have their own L2) works on a contiguous
 // range of items.  `per` = ceil(total / 8); the grid has 8 * per workgroups

@@ -215,23 +215,21 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdArgs a) {
         const int jn = tile_at(jj + 1);
         if (jn >= 0) load_tile(rev ? (j_end - 1 - jn) : jn);   // in flight during this tile's math
 
-        if (!(causal && kv0 > qw0 + 31)) {   // else: no valid key for this wave's rows
+        // one tile of math; element masks only on tiles that straddle the
+        // diagonal, the padding boundary or the N tail
+        auto tile_math = [&](bool edge) {
             const T* k = sK + buf * TILE_K;
             const TV* v = sV + buf * TILE_K;
-            // ---- S^T = K_j Q^T
+            // ---- S^T = K_j Q^T (operands of one 32-key block loaded together)
             f32x16 s[KB];
 #pragma unroll
             for (int kb = 0; kb < KB; ++kb) {
                 s[kb] = zero16();
 #pragma unroll
-                for (int ks = 0; ks < KS; ++ks) {
-                    const typename MS::frag ak = load_frag<T>(k + LK::off(kb * 32 + ln, ks * 2 * E + hl * E));
-                    s[kb] = MS::mma(ak, qf[ks], s[kb]);
-                }
+                for (int ks = 0; ks < KS; ++ks)
+                    s[kb] = MS::mma(load_frag<T>(k + LK::off(kb * 32 + ln, ks * 2 * E + hl * E)), qf[ks], s[kb]);
             }
-            // ---- element masks on edge tiles
-            const bool edge = (kv0 + BC > kend) || (causal && kv0 + BC - 1 > qw0);
-            if (edge) {
+            if (__builtin_expect(edge, 0)) {
 #pragma unroll
                 for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
@@ -248,7 +246,7 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdArgs a) {
 #pragma unroll
                 for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
             mx = fmaxf(mx, wave_xor32(mx)) * c;
-            if (__any(mx > m_run + RESCALE)) {
+            if (__builtin_expect(__any(mx > m_run + RESCALE), 0)) {
                 const float m_new = fmaxf(m_run, mx);
                 const float alpha = (m_new == -INFINITY) ? 1.0f : fast_exp2(m_run - m_new);
                 m_run = m_new;
@@ -288,13 +286,13 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdArgs a) {
                 for (int u = 0; u < PU; ++u) {
                     const typename MV::frag bp = pack_p<TV>(&p[kb][u * EV]);
 #pragma unroll
-                    for (int db = 0; db < DB; ++db) {
-                        const typename MV::frag av =
-                            load_frag<TV>(v + LV::off(db * 32 + ln, kb * 32 + hl * 16 + u * EV));
-                        oacc[db] = MV::mma(av, bp, oacc[db]);
-                    }
+                    for (int db = 0; db < DB; ++db)
+                        oacc[db] = MV::mma(load_frag<TV>(v + LV::off(db * 32 + ln, kb * 32 + hl * 16 + u * EV)), bp,
+                                           oacc[db]);
                 }
-        }
+        };
+        if (!(causal && kv0 > qw0 + 31))   // else: no valid key for this wave's rows
+            tile_math((kv0 + BC > kend) || (causal && kv0 + BC - 1 > qw0));
         if (jn >= 0) store_tile(buf ^ 1);   // that buffer was last read before the previous barrier
         __syncthreads();
         buf ^= 1;

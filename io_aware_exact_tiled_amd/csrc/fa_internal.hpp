@@ -10,14 +10,23 @@
 
 namespace fa {
 
-// Tile shapes.  Forward: a workgroup owns BR query rows (4 waves x 32) and
-// walks key tiles of BC.  Backward: a workgroup owns BC_B keys (4 waves x 32)
-// and walks query tiles of BR_B.  All divide the 128-token block-mask tile.
+// Tile shapes (query rows x keys).  Forward: a workgroup owns FWD_BR query
+// rows (4 waves x 32) and walks key tiles of FWD_BC.  Backward dK/dV kernel: a
+// workgroup owns BWD_KV_BC keys (4 waves x 32) and walks query tiles of
+// BwdTiles<T>::KV_BR rows.  Backward dQ kernel: a workgroup owns BWD_DQ_BR
+// query rows and walks key tiles of BWD_DQ_BC.  All divide the 128-token
+// block-mask tile.
 constexpr int MASK_TILE = 128;   // block-mask granularity (tokens)
 constexpr int FWD_BR = 128;
 constexpr int FWD_BC = 64;
-constexpr int BWD_BR = 32;
-constexpr int BWD_BC = 128;
+constexpr int BWD_KV_BC = 128;
+constexpr int BWD_KV_BR16 = 64;  // 16-bit inputs
+constexpr int BWD_KV_BR32 = 32;  // fp32 inputs (LDS budget of the double buffer)
+constexpr int BWD_DQ_BR = 128;
+constexpr int BWD_DQ_BC = 32;
+template <class T> struct BwdTiles {
+    static constexpr int KV_BR = sizeof(T) == 4 ? BWD_KV_BR32 : BWD_KV_BR16;
+};
 
 struct MaskArgs {
     int causal;
@@ -59,7 +68,6 @@ struct BwdArgs {
     void* dq;
     void* dk;
     void* dv;
-    float* dq_acc;        // fp32 [B][H][N][d] workspace
     float* delta;         // fp32 [B][H][N] workspace: D = rowsum(dO o O)
     int B, H, N;
     float scale;
@@ -67,8 +75,9 @@ struct BwdArgs {
     int o_f32;
     MaskArgs mask;
     DropArgs drop;
-    uint8_t* tile_visits;
-    hipEvent_t ev_begin, ev_end;   // optional profiling events around bwd_main
+    uint8_t* tile_visits;          // dK/dV kernel's map (or null)
+    uint8_t* tile_visits2;         // dQ kernel's map (or null)
+    hipEvent_t ev_begin, ev_end;   // optional profiling events around the two main kernels
 };
 
 hipError_t launch_fwd(const FwdArgs& a, fa_dtype dt, int d, hipStream_t s);

@@ -47,13 +47,14 @@ def test_scalars():
     br, bc = ctypes.c_int32(), ctypes.c_int32()
     for d in (64, 128):
         for dt in (0, 1, 2):
-            for p in (0, 1):
+            for p in (0, 1, 2):
                 assert L.fa_tile_shape(d, dt, p, ctypes.byref(br), ctypes.byref(bc)) == 0
                 assert 128 % br.value == 0 and 128 % bc.value == 0
     assert L.fa_tile_shape(96, 2, 0, ctypes.byref(br), ctypes.byref(bc)) == -3
     assert L.fa_tile_shape(64, 7, 0, ctypes.byref(br), ctypes.byref(bc)) == -4
-    assert L.fa_bwd_workspace_bytes(1, 2, 256, 64) == 1 * 2 * 256 * 64 * 4 + 2048
-    assert L.fa_bwd_workspace_bytes(1, 1, 3, 64) == 768 + 256
+    assert L.fa_bwd_workspace_bytes(1, 2, 256, 64) == 2048
+    assert L.fa_bwd_workspace_bytes(1, 1, 3, 64) == 256
+    assert L.fa_tile_shape(64, 2, 3, ctypes.byref(br), ctypes.byref(bc)) == -10
     assert L.fa_bwd_workspace_bytes(0, 1, 3, 64) == 0
 
 
