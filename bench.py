@@ -126,6 +126,7 @@ def time_workload(w, steps, warmup, ev):
     f1 = [ev.create() for _ in range(n_ev)]
     b0 = [ev.create() for _ in range(n_ev)]
     b1 = [ev.create() for _ in range(n_ev)]
+    bm = [ev.create() for _ in range(n_ev)]
     s0 = [ev.create() for _ in range(n_ev)]
     s1 = [ev.create() for _ in range(n_ev)]
 
@@ -134,7 +135,7 @@ def time_workload(w, steps, warmup, ev):
             ev.record(s0[i], stream)
         fa.fwd(q, k, v, out=o, lse=lse, events=None if i is None else (f0[i], f1[i]), **kw)
         fa.bwd(q, k, v, o, do, lse, grads=grads, workspace=ws,
-               events=None if i is None else (b0[i], b1[i]), **kw)
+               events=None if i is None else (b0[i], b1[i], bm[i]), **kw)
         if i is not None:
             ev.record(s1[i], stream)
 
@@ -148,11 +149,14 @@ def time_workload(w, steps, warmup, ev):
     wall = time.perf_counter() - t0
     fwd_ms = [ev.ms(f0[i], f1[i]) for i in range(steps)]
     bwd_ms = [ev.ms(b0[i], b1[i]) for i in range(steps)]
+    kv_ms = [ev.ms(b0[i], bm[i]) for i in range(steps)]
+    dq_ms = [ev.ms(bm[i], b1[i]) for i in range(steps)]
     step_ms = [ev.ms(s0[i], s1[i]) for i in range(steps)]
-    for e in f0 + f1 + b0 + b1 + s0 + s1:
+    for e in f0 + f1 + b0 + b1 + bm + s0 + s1:
         ev.destroy(e)
     pairs = valid_pairs(x, w)
-    return dict(x=x, pairs=pairs, wall_s=wall, fwd_ms=fwd_ms, bwd_main_ms=bwd_ms, step_ms=step_ms)
+    return dict(x=x, pairs=pairs, wall_s=wall, fwd_ms=fwd_ms, bwd_main_ms=bwd_ms, kv_ms=kv_ms, dq_ms=dq_ms,
+                step_ms=step_ms)
 
 
 def cpu_baseline(w, rows):
@@ -216,13 +220,14 @@ def main():
     total_tflops = (fwd_flop + bwd_flop) / (step_ms * 1e-3) / 1e12
     fwd_tf = fwd_flop / (fwd_ms * 1e-3) / 1e12
     bwd_tf = bwd_flop / (bwd_ms * 1e-3) / 1e12
-    # dominant kernel: whichever main kernel takes longer per step
-    avg_fwd = float(np.mean(r["fwd_ms"]))
-    avg_bwd = float(np.mean(r["bwd_main_ms"]))
-    if avg_bwd >= avg_fwd:
-        dom, dom_ms, dom_flop = "bwd_main_kernel", avg_bwd, bwd_flop
-    else:
-        dom, dom_ms, dom_flop = "fwd_kernel", avg_fwd, fwd_flop
+    # dominant kernel: the one with the largest average launch time.  Algorithmic
+    # FLOPs per launch: fwd_kernel 4d per valid pair (S, PV); bwd_kv_kernel 8d
+    # (S, dP, dV, dK); bwd_dq_kernel 2d (dQ; its recomputed S and dP are extra work)
+    kern = {"fwd_kernel": (float(np.mean(r["fwd_ms"])), fwd_flop),
+            "bwd_kv_kernel": (float(np.mean(r["kv_ms"])), 8.0 * w.d * r["pairs"]),
+            "bwd_dq_kernel": (float(np.mean(r["dq_ms"])), 2.0 * w.d * r["pairs"])}
+    dom = max(kern, key=lambda k: kern[k][0])
+    dom_ms, dom_flop = kern[dom]
     achieved = dom_flop / (dom_ms * 1e-3) / 1e12
     out = {
         "metric": "attention fwd/bwd TFLOP/s (bf16, d=64/128, N 1K-16K), % of MFMA peak",
@@ -244,6 +249,7 @@ def main():
         "fwd_tflops": round(fwd_tf, 2), "fwd_pct_peak": round(100 * fwd_tf / peak, 2), "fwd_ms": round(fwd_ms, 4),
         "bwd_tflops": round(bwd_tf, 2), "bwd_pct_peak": round(100 * bwd_tf / peak, 2),
         "bwd_main_ms": round(bwd_ms, 4),
+        "bwd_kv_ms": round(med(r["kv_ms"]), 4), "bwd_dq_ms": round(med(r["dq_ms"]), 4),
         "roofline": {"bound": "mfma", "kernel": dom, "achieved": round(achieved, 2), "peak": peak,
                      "unit": "TFLOP/s", "frac": round(achieved / peak, 4), "traffic": None,
                      "avg_launch_ms": round(dom_ms, 4), "flop_per_launch": dom_flop},

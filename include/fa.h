@@ -108,6 +108,8 @@ typedef struct {
                                    after the pass's main kernels (the forward
                                    kernel; the backward's two S/P-recomputing
                                    kernels, without the D pre-pass)             */
+    hipEvent_t main_mid;        /* fa_bwd profiling, optional: recorded between
+                                   the dK/dV kernel and the dQ kernel            */
 } fa_opts;
 
 /* Forward pass.  Q, K, V: [B][H][N][d] of `dtype`.  O: [B][H][N][d] of

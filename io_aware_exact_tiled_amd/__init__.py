@@ -53,7 +53,9 @@ def _opts(B, H, N, d, pass_, key_lens, rng_offset, o_fp32, record_tiles, reverse
           events=None):
     opts = FaOpts()
     if events is not None:
-        opts.main_begin, opts.main_end = events
+        opts.main_begin, opts.main_end = events[0], events[1]
+        if len(events) > 2:
+            opts.main_mid = events[2]
     opts.struct_size = ctypes.sizeof(FaOpts)
     opts.o_fp32 = 1 if o_fp32 else 0
     keep = []

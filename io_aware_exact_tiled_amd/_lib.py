@@ -38,6 +38,7 @@ class FaOpts(ctypes.Structure):
         ("tile_visits2", ctypes.c_void_p),
         ("main_begin", ctypes.c_void_p),
         ("main_end", ctypes.c_void_p),
+        ("main_mid", ctypes.c_void_p),
     ]
 
 

@@ -172,6 +172,7 @@ fa_status fa_bwd(const void* Q, const void* K, const void* V, const void* O, con
     a.tile_visits2 = rec ? opts->tile_visits2 : nullptr;
     a.ev_begin = (opts && opts->main_end) ? opts->main_begin : nullptr;
     a.ev_end = (opts && opts->main_begin) ? opts->main_end : nullptr;
+    a.ev_mid = (a.ev_begin && a.ev_end) ? opts->main_mid : nullptr;
     const hipError_t e = fa::launch_bwd(a, dtype, d, stream);
     return e == hipSuccess ? FA_OK : hip_fail(e);
 }

@@ -25,16 +25,18 @@
 // dQ is therefore produced without atomics and without a dS round trip
 // through memory, at the price of recomputing S and dP once more (seven
 // products per pair instead of five).  Both loops prefetch the next tile into
-// registers while the current one is computed and keep two LDS buffers (one
-// barrier per tile).
+// the LDS buffer not in use while the current one is computed (one barrier
+// per tile).  Tiles are staged in their natural row-major layout with 16-byte
+// global-to-LDS loads; operands that are needed transposed are read with the
+// gfx950 LDS transpose read instead of being staged twice.
 //
 // Layouts (MI355X-specific): bwd_kv computes S with queries on the MFMA rows
 // and keys on the columns (query rows staged in LDS in MFMA row order so each
 // lane holds 16 consecutive queries of its key: these registers are directly
-// the A operand of dV += P^T dO and dK += dS^T Q; Q and dO are staged a second
-// time transposed for the B operands).  bwd_dq is the forward kernel's layout:
-// keys on the rows (K, V in MFMA row order), one query per lane, K staged a
-// second time transposed for dQ^T += K^T dS^T.
+// the A operand of dV += P^T dO and dK += dS^T Q, whose B operands are the
+// same Q and dO tiles read transposed).  bwd_dq is the forward kernel's
+// layout: keys on the rows (K, V in MFMA row order), one query per lane, and
+// the K tile read transposed for dQ^T += K^T dS^T.
 #include "fa_device.hpp"
 #include "fa_internal.hpp"
 
@@ -65,13 +67,6 @@ template <class T> __device__ inline typename Mma<T>::frag pack_f(const float* p
     } else {
         return p[0];
     }
-}
-
-// MFMA row slot of row r within its 32-row block: slot m holds row
-// 16*((m/4)%2) + 4*(m/8) + m%4, so accumulator register r of lane half h is
-// row 16*h + r.
-__device__ inline int row_slot(int r) {
-    return (r & ~31) | (((r >> 2) & 3) * 8 + ((r >> 4) & 1) * 4 + (r & 3));
 }
 
 __device__ inline int clamp_len(const int32_t* key_lens, int b, int N) {
@@ -138,18 +133,11 @@ __global__ __launch_bounds__(256, 1) void bwd_kv_kernel(BwdArgs a) {
     constexpr int KS = D / (2 * E);               // MFMA steps over d
     constexpr int DB = D / 32;
     constexpr int QU = 16 / E;                    // MFMA steps over 16 queries of a lane half
-    constexpr int EPU = 16 / (int)sizeof(T);
-    constexpr int DC = D / EPU;                   // 16-byte chunks per row
-    constexpr int NT = (BR / 4) * DC;             // staging tasks per tensor (4 rows x 1 chunk)
-    constexpr int NN = (NT + 255) / 256;
     constexpr int TQ = BR * D;                    // elements per staged tensor
-    typedef Swz<T, D> LQ;      // Q, dO natural: BR rows (MFMA row order) x D
-    typedef Swz<T, BR> LT;     // Q^T, dO^T: D rows x BR queries
+    typedef Swz<T, D> LQ;      // Q, dO: BR rows (MFMA row order) x D
 
     __shared__ __attribute__((aligned(16))) T sQ[2 * TQ];
     __shared__ __attribute__((aligned(16))) T sdO[2 * TQ];
-    __shared__ __attribute__((aligned(16))) T sQt[2 * TQ];
-    __shared__ __attribute__((aligned(16))) T sdOt[2 * TQ];
     __shared__ __attribute__((aligned(16))) float sLse[2 * BR];
     __shared__ __attribute__((aligned(16))) float sDel[2 * BR];
 
@@ -200,48 +188,18 @@ __global__ __launch_bounds__(256, 1) void bwd_kv_kernel(BwdArgs a) {
 #pragma unroll
     for (int db = 0; db < DB; ++db) { dk[db] = zero16(); dv[db] = zero16(); }
 
-    // ---- staging of one query tile: Q, dO (4 rows x 16 bytes per task), LSE, D
-    u32x4 qreg[NN][4], oreg[NN][4];
+    // ---- staging of one query tile: Q, dO by global->LDS DMA; LSE, D via registers
     float lreg = 0.0f;
-    auto load_tile = [&](int i) {
+    auto load_tile = [&](int i, int buf) {
         const int q0 = i * BR;
-#pragma unroll
-        for (int n = 0; n < NN; ++n) {
-            const int t = tid + n * 256;
-            const int dc = t % DC, rg = t / DC;
-#pragma unroll
-            for (int kk = 0; kk < 4; ++kk) {
-                const int q = q0 + rg * 4 + kk;
-                const bool ok = t < NT && q < N;
-                const u32x4 z = {0u, 0u, 0u, 0u};
-                qreg[n][kk] = ok ? *reinterpret_cast<const u32x4*>(Qg + (size_t)q * D + dc * EPU) : z;
-                oreg[n][kk] = ok ? *reinterpret_cast<const u32x4*>(dOg + (size_t)q * D + dc * EPU) : z;
-            }
-        }
+        dma_rows<T, BR, D>(sQ + buf * TQ, Qg, q0, N, wave, lane);
+        dma_rows<T, BR, D>(sdO + buf * TQ, dOg, q0, N, wave, lane);
         if (tid < 2 * BR) {
             const int q = q0 + (tid % BR);
             lreg = (q < N) ? (tid < BR ? lseg[q] : delg[q]) : (tid < BR ? INFINITY : 0.0f);
         }
     };
-    auto store_tile = [&](int buf) {
-        T* q = sQ + buf * TQ;
-        T* o = sdO + buf * TQ;
-        T* qt = sQt + buf * TQ;
-        T* ot = sdOt + buf * TQ;
-#pragma unroll
-        for (int n = 0; n < NN; ++n) {
-            const int t = tid + n * 256;
-            if (t < NT) {
-                const int dc = t % DC, rg = t / DC;
-#pragma unroll
-                for (int kk = 0; kk < 4; ++kk) {
-                    *reinterpret_cast<u32x4*>(q + LQ::off(row_slot(rg * 4 + kk), dc * EPU)) = qreg[n][kk];
-                    *reinterpret_cast<u32x4*>(o + LQ::off(row_slot(rg * 4 + kk), dc * EPU)) = oreg[n][kk];
-                }
-                store_transposed4<T>(qreg[n], [&](int c) { return qt + LT::off(dc * EPU + c, rg * 4); });
-                store_transposed4<T>(oreg[n], [&](int c) { return ot + LT::off(dc * EPU + c, rg * 4); });
-            }
-        }
+    auto publish_stats = [&](int buf) {
         if (tid < BR) sLse[buf * BR + tid] = lreg * 1.4426950408889634f;
         else if (tid < 2 * BR) sDel[buf * BR + tid - BR] = lreg;
     };
@@ -249,24 +207,23 @@ __global__ __launch_bounds__(256, 1) void bwd_kv_kernel(BwdArgs a) {
     const float c = a.scale_log2;
     int i = tile_at(i_begin);
     if (i >= 0) {
-        load_tile(i);
-        store_tile(0);
+        load_tile(i, 0);
+        publish_stats(0);
     }
+    __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
     int buf = 0;
     while (i >= 0) {
         const int q0 = i * BR;
         if (vis && tid == 0) vis[(size_t)i * Tc] = 1;
         const int in = tile_at(i + 1);
-        if (in >= 0) load_tile(in);
+        if (in >= 0) load_tile(in, buf ^ 1);   // lands in the other buffer during this step
 
         {   // no per-wave skip: a wave whose keys all lie above this tile's rows (first
             // causal step only) or past the key length runs the edge path with P = 0,
             // which keeps dK, dV in the MFMA accumulators across the loop
             const T* q = sQ + buf * TQ;
             const T* o = sdO + buf * TQ;
-            const T* qt = sQt + buf * TQ;
-            const T* ot = sdOt + buf * TQ;
             const float* ls = sLse + buf * BR;
             const float* dl = sDel + buf * BR;
             const bool edge = (causal && kw0 + 31 > q0) || (kw0 + 32 > kend) || (q0 + BR > N);
@@ -314,22 +271,26 @@ __global__ __launch_bounds__(256, 1) void bwd_kv_kernel(BwdArgs a) {
                     }
                     ds[r] = p[r] * (dpr - dlv[r]);
                 }
-                // dV_j += Pd^T dO_i ; dK_j += dS^T Q_i
+                // dV_j += Pd^T dO_i ; dK_j += dS^T Q_i.  B operands are the dO and Q
+                // tiles read transposed: k-slot kk of MFMA u is query row
+                // 32qb + 16(kk/E) + uE + kk%E of the tile.
 #pragma unroll
                 for (int u = 0; u < QU; ++u) {
                     const typename MM::frag ap = pack_f<T>(&pd[u * E]);
                     const typename MM::frag as = pack_f<T>(&ds[u * E]);
+                    auto rowof = [&](int kk) { return row_slot(qb * 32 + (kk / E) * 16 + u * E + kk % E); };
 #pragma unroll
                     for (int db = 0; db < DB; ++db) {
-                        const typename MM::frag bo = load_frag<T>(ot + LT::off(db * 32 + ln, qr0 + u * E));
+                        const typename MM::frag bo = load_frag_tr<T, D>(o, db * 32, rowof, lane);
                         dv[db] = MM::mma(ap, bo, dv[db]);
-                        const typename MM::frag bq = load_frag<T>(qt + LT::off(db * 32 + ln, qr0 + u * E));
+                        const typename MM::frag bq = load_frag_tr<T, D>(q, db * 32, rowof, lane);
                         dk[db] = MM::mma(as, bq, dk[db]);
                     }
                 }
             }
         }
-        if (in >= 0) store_tile(buf ^ 1);
+        if (in >= 0) publish_stats(buf ^ 1);
+        __builtin_amdgcn_s_waitcnt(0);   // this wave's DMA into the other buffer has landed
         __syncthreads();
         buf ^= 1;
         i = in;
@@ -353,24 +314,18 @@ __global__ __launch_bounds__(256, 1) void bwd_kv_kernel(BwdArgs a) {
 // ---------------------------------------------------------------------------
 // dQ: query-stationary.
 template <class T, int D, bool DROP>
-__global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdArgs a) {
+__global__ __launch_bounds__(256, sizeof(T) == 4 ? 1 : 2) void bwd_dq_kernel(BwdArgs a) {
     typedef Mma<T> MM;
     constexpr int E = MM::E;
     constexpr int BR = BWD_DQ_BR, BC = BWD_DQ_BC;   // 128 query rows, 32-key tiles
     constexpr int KS = D / (2 * E);
     constexpr int DB = D / 32;
     constexpr int PU = 16 / E;
-    constexpr int EPU = 16 / (int)sizeof(T);
-    constexpr int DC = D / EPU;
-    constexpr int NT = (BC / 4) * DC;               // staging tasks per tensor
-    constexpr int NN = (NT + 255) / 256;
     constexpr int TK = BC * D;
     typedef Swz<T, D> LK;      // K, V: BC rows (MFMA row order) x D
-    typedef Swz<T, BC> LT;     // K^T: D rows x BC keys
 
     __shared__ __attribute__((aligned(16))) T sK[2 * TK];
     __shared__ __attribute__((aligned(16))) T sV[2 * TK];
-    __shared__ __attribute__((aligned(16))) T sKt[2 * TK];
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int hl = lane >> 5, ln = lane & 31;
@@ -420,60 +375,26 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdArgs a) {
 #pragma unroll
     for (int db = 0; db < DB; ++db) dq[db] = zero16();
 
-    u32x4 kreg[NN][4], vreg[NN][4];
-    auto load_tile = [&](int j) {
-        const int kv0 = j * BC;
-#pragma unroll
-        for (int n = 0; n < NN; ++n) {
-            const int t = tid + n * 256;
-            const int dc = t % DC, rg = t / DC;
-#pragma unroll
-            for (int kk = 0; kk < 4; ++kk) {
-                const int key = kv0 + rg * 4 + kk;
-                const bool ok = t < NT && key < N;
-                const u32x4 z = {0u, 0u, 0u, 0u};
-                kreg[n][kk] = ok ? *reinterpret_cast<const u32x4*>(Kg + (size_t)key * D + dc * EPU) : z;
-                vreg[n][kk] = ok ? *reinterpret_cast<const u32x4*>(Vg + (size_t)key * D + dc * EPU) : z;
-            }
-        }
-    };
-    auto store_tile = [&](int buf) {
-        T* k = sK + buf * TK;
-        T* v = sV + buf * TK;
-        T* kt = sKt + buf * TK;
-#pragma unroll
-        for (int n = 0; n < NN; ++n) {
-            const int t = tid + n * 256;
-            if (t < NT) {
-                const int dc = t % DC, rg = t / DC;
-#pragma unroll
-                for (int kk = 0; kk < 4; ++kk) {
-                    *reinterpret_cast<u32x4*>(k + LK::off(row_slot(rg * 4 + kk), dc * EPU)) = kreg[n][kk];
-                    *reinterpret_cast<u32x4*>(v + LK::off(row_slot(rg * 4 + kk), dc * EPU)) = vreg[n][kk];
-                }
-                store_transposed4<T>(kreg[n], [&](int cc) { return kt + LT::off(dc * EPU + cc, rg * 4); });
-            }
-        }
+    auto load_tile = [&](int j, int buf) {
+        dma_rows<T, BC, D>(sK + buf * TK, Kg, j * BC, N, wave, lane);
+        dma_rows<T, BC, D>(sV + buf * TK, Vg, j * BC, N, wave, lane);
     };
 
     const float c = a.scale_log2;
     int j = tile_at(0);
-    if (j >= 0) {
-        load_tile(j);
-        store_tile(0);
-    }
+    if (j >= 0) load_tile(j, 0);
+    __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
     int buf = 0;
     while (j >= 0) {
         const int kv0 = j * BC;
         if (vis && tid == 0) vis[j] = 1;
         const int jn = tile_at(j + 1);
-        if (jn >= 0) load_tile(jn);
+        if (jn >= 0) load_tile(jn, buf ^ 1);
 
         if (!(causal && kv0 > qw0 + 31)) {
             const T* k = sK + buf * TK;
             const T* v = sV + buf * TK;
-            const T* kt = sKt + buf * TK;
             // S^T = K Q^T, dP_hat^T = V dO^T: lane holds query qrow, keys kv0 + 16hl + r
             f32x16 s = zero16(), dp = zero16();
 #pragma unroll
@@ -510,18 +431,20 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdArgs a) {
                 if constexpr (DROP) dpr *= ((keep >> r) & 1u) ? a.drop.keep_scale : 0.0f;
                 ds[r] = p[r] * (dpr - del);
             }
-            // dQ^T += K^T dS^T
+            // dQ^T += K^T dS^T: the A operand is the K tile read transposed; k-slot
+            // kk of MFMA u is key 16(kk/E) + uE + kk%E of the tile
 #pragma unroll
             for (int u = 0; u < PU; ++u) {
                 const typename MM::frag bs = pack_f<T>(&ds[u * E]);
+                auto rowof = [&](int kk) { return row_slot((kk / E) * 16 + u * E + kk % E); };
 #pragma unroll
                 for (int db = 0; db < DB; ++db) {
-                    const typename MM::frag akt = load_frag<T>(kt + LT::off(db * 32 + ln, hl * 16 + u * E));
+                    const typename MM::frag akt = load_frag_tr<T, D>(k, db * 32, rowof, lane);
                     dq[db] = MM::mma(akt, bs, dq[db]);
                 }
             }
         }
-        if (jn >= 0) store_tile(buf ^ 1);
+        __builtin_amdgcn_s_waitcnt(0);   // this wave's DMA into the other buffer has landed
         __syncthreads();
         buf ^= 1;
         j = jn;
@@ -555,6 +478,7 @@ hipError_t launch_t(const BwdArgs& a, hipStream_t s) {
     e = hipLaunchKernel((const void*)&bwd_kv_kernel<T, D, DROP>, dim3((unsigned)(8 * ((kv_total + 7) / 8))),
                         dim3(256), args, 0, s);
     if (e != hipSuccess) return e;
+    if (a.ev_mid && (e = hipEventRecord(a.ev_mid, s)) != hipSuccess) return e;
     e = hipLaunchKernel((const void*)&bwd_dq_kernel<T, D, DROP>, dim3((unsigned)(8 * ((dq_total + 7) / 8))),
                         dim3(256), args, 0, s);
     if (e != hipSuccess) return e;

@@ -181,6 +181,74 @@ __device__ inline void store_transposed4(const u32x4 (&x)[4], F dst) {
     }
 }
 
+// MFMA row order within a 32-row block: slot m holds row 16*((m/4)%2) +
+// 4*(m/8) + m%4, so accumulator register r of lane half h is row 16*h + r.
+__device__ inline int row_slot(int r) {
+    return (r & ~31) | (((r >> 2) & 3) * 8 + ((r >> 4) & 1) * 4 + (r & 3));
+}
+__device__ inline int slot_row(int m) {
+    return (m & ~31) | (((m >> 2) & 1) * 16 + ((m >> 3) & 3) * 4 + (m & 3));
+}
+
+typedef __attribute__((address_space(3))) void lds_void;
+typedef __attribute__((address_space(1))) void glb_void;
+
+// Stage ROWS x D elements (rows row0.. of a row-major [N][D] head slab) into
+// a swizzled LDS tile whose rows are in MFMA row order, with 16-byte
+// global-to-LDS loads.  One such load writes the 64 lanes' 16 bytes to 64
+// consecutive LDS units, so each lane fetches the global chunk that belongs
+// at its unit.  Rows past N read row N-1 (finite data; those rows are masked
+// by the caller).  Issued by all 4 waves of the workgroup; completion is
+// awaited with s_waitcnt before the barrier that publishes the tile.
+template <class T, int ROWS, int D>
+__device__ inline void dma_rows(T* tile, const T* head, int row0, int N, int wave, int lane) {
+    typedef Swz<T, D> L;
+    constexpr int EPU = 16 / (int)sizeof(T);
+    constexpr int UPR = D / EPU;
+    constexpr int UNITS = ROWS * UPR;
+    static_assert(UNITS % 256 == 0, "tile must be a whole number of workgroup-wide loads");
+#pragma unroll
+    for (int n = 0; n < UNITS / 256; ++n) {
+        const int blk = n * 4 + wave;                 // this wave's 64-unit block
+        const int P = blk * 64 + lane;                // LDS unit written by this lane
+        const int slot = P / UPR, pu = P % UPR;
+        const int u = pu ^ L::f(slot);
+        int row = row0 + slot_row(slot);
+        row = row < N ? row : N - 1;
+        const T* src = head + (size_t)row * D + u * EPU;
+        __builtin_amdgcn_global_load_lds((glb_void*)src, (lds_void*)(tile + blk * 64 * EPU), 16, 0, 0);
+    }
+}
+
+// Transposed MFMA operand from a natural (row-major, swizzled, MFMA row
+// order) 16-bit LDS tile, with the gfx950 LDS transpose read: the result is
+// the 8 values X[k][c] for k = k-slots 8*(lane/32) .. +7 and c = col0 +
+// lane%32, where k-slot q maps to tile row rowof(q).  Within each 16-lane
+// group the transpose read hands destination lane j, element e, element j%4
+// of the 8 bytes addressed by source lane j/4 + 4e; so source lane s of group
+// G addresses row k = 8*(G/2) + 4*h + s/4 (h = 0, 1: the two halves of the
+// fragment), columns col0 + 16*(G%2) + 4*(s%4) .. +3.
+template <class T, int D, class RowOf>
+__device__ inline typename Mma<T>::frag load_frag_tr(const T* tile, int col0, RowOf rowof, int lane) {
+    typedef Swz<T, D> L;
+    typedef short v4s __attribute__((ext_vector_type(4)));
+    typedef __attribute__((address_space(3))) v4s lds_v4s;
+    if constexpr (Mma<T>::E == 8) {
+        const int G = lane >> 4, s = lane & 15;
+        const int col = col0 + 16 * (G & 1) + 4 * (s & 3);
+        union { v4s h[2]; typename Mma<T>::frag f; } u;
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            const int k = 8 * (G >> 1) + 4 * h + (s >> 2);
+            u.h[h] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s*)(tile + L::off(rowof(k), col)));
+        }
+        return u.f;
+    } else {
+        // one element per lane (k-slot lane/32): a plain read
+        return tile[L::off(rowof(lane >> 5), col0 + (lane & 31))];
+    }
+}
+
 // Map a linear workgroup id to a work item so that each of the 8 XCDs (which
 // receive workgroups round-robin and have their own L2) works on a contiguous
 // range of items.  `per` = ceil(total / 8); the grid has 8 * per workgroups

@@ -60,9 +60,7 @@ template <class TV> __device__ inline typename Mma<TV>::frag pack_p(const float*
 }
 
 // MFMA row slot of key r within a 32-key block (see the file comment).
-__device__ inline int key_slot(int r) {
-    return (r & ~31) | (((r >> 2) & 3) * 8 + ((r >> 4) & 1) * 4 + (r & 3));
-}
+__device__ inline int key_slot(int r) { return row_slot(r); }
 
 }  // namespace
 

@@ -78,6 +78,7 @@ struct BwdArgs {
     uint8_t* tile_visits;          // dK/dV kernel's map (or null)
     uint8_t* tile_visits2;         // dQ kernel's map (or null)
     hipEvent_t ev_begin, ev_end;   // optional profiling events around the two main kernels
+    hipEvent_t ev_mid;             // optional: between the two main kernels
 };
 
 hipError_t launch_fwd(const FwdArgs& a, fa_dtype dt, int d, hipStream_t s);
