@@ -134,7 +134,7 @@ __global__ __launch_bounds__(256, 1) void bwd_kv_kernel(BwdArgs a) {
     constexpr int DB = D / 32;
     constexpr int QU = 16 / E;                    // MFMA steps over 16 queries of a lane half
     constexpr int TQ = BR * D;                    // elements per staged tensor
-    typedef Swz<T, D> LQ;      // Q, dO: BR rows (MFMA row order) x D
+    typedef SwzTr<T, D> LQ;    // Q, dO: BR rows (MFMA row order) x D
 
     __shared__ __attribute__((aligned(16))) T sQ[2 * TQ];
     __shared__ __attribute__((aligned(16))) T sdO[2 * TQ];
@@ -322,7 +322,7 @@ __global__ __launch_bounds__(256, sizeof(T) == 4 ? 1 : 2) void bwd_dq_kernel(Bwd
     constexpr int DB = D / 32;
     constexpr int PU = 16 / E;
     constexpr int TK = BC * D;
-    typedef Swz<T, D> LK;      // K, V: BC rows (MFMA row order) x D
+    typedef SwzTr<T, D> LK;    // K, V: BC rows (MFMA row order) x D
 
     __shared__ __attribute__((aligned(16))) T sK[2 * TK];
     __shared__ __attribute__((aligned(16))) T sV[2 * TK];
@@ -396,13 +396,23 @@ __global__ __launch_bounds__(256, sizeof(T) == 4 ? 1 : 2) void bwd_dq_kernel(Bwd
             const T* k = sK + buf * TK;
             const T* v = sV + buf * TK;
             // S^T = K Q^T, dP_hat^T = V dO^T: lane holds query qrow, keys kv0 + 16hl + r
+            // (operands of step ks+1 read before the MFMAs of step ks)
             f32x16 s = zero16(), dp = zero16();
+            {
+                typename MM::frag ak[2], av[2];
+                ak[0] = load_frag<T>(k + LK::off(ln, hl * E));
+                av[0] = load_frag<T>(v + LK::off(ln, hl * E));
 #pragma unroll
-            for (int ks = 0; ks < KS; ++ks) {
-                const typename MM::frag ak = load_frag<T>(k + LK::off(ln, ks * 2 * E + hl * E));
-                s = MM::mma(ak, qf[ks], s);
-                const typename MM::frag av = load_frag<T>(v + LK::off(ln, ks * 2 * E + hl * E));
-                dp = MM::mma(av, of[ks], dp);
+                for (int ks = 0; ks < KS; ++ks) {
+                    if (ks + 1 < KS) {
+                        ak[(ks + 1) & 1] = load_frag<T>(k + LK::off(ln, (ks + 1) * 2 * E + hl * E));
+                        av[(ks + 1) & 1] = load_frag<T>(v + LK::off(ln, (ks + 1) * 2 * E + hl * E));
+                    }
+                    __builtin_amdgcn_sched_barrier(0);
+                    s = MM::mma(ak[ks & 1], qf[ks], s);
+                    dp = MM::mma(av[ks & 1], of[ks], dp);
+                    __builtin_amdgcn_sched_barrier(0);
+                }
             }
             const bool edge = (kv0 + BC > kend) || (causal && kv0 + BC - 1 > qw0);
             float ds[16];
@@ -433,14 +443,24 @@ __global__ __launch_bounds__(256, sizeof(T) == 4 ? 1 : 2) void bwd_dq_kernel(Bwd
             }
             // dQ^T += K^T dS^T: the A operand is the K tile read transposed; k-slot
             // kk of MFMA u is key 16(kk/E) + uE + kk%E of the tile
+            {
+                typename MM::frag bs[PU];
 #pragma unroll
-            for (int u = 0; u < PU; ++u) {
-                const typename MM::frag bs = pack_f<T>(&ds[u * E]);
-                auto rowof = [&](int kk) { return row_slot((kk / E) * 16 + u * E + kk % E); };
+                for (int u = 0; u < PU; ++u) bs[u] = pack_f<T>(&ds[u * E]);
+                auto rowof_u = [&](int u) {
+                    return [=](int kk) { return row_slot((kk / E) * 16 + u * E + kk % E); };
+                };
+                constexpr int NI = PU * DB;
+                typename MM::frag akt[2];
+                akt[0] = load_frag_tr<T, D>(k, 0, rowof_u(0), lane);
 #pragma unroll
-                for (int db = 0; db < DB; ++db) {
-                    const typename MM::frag akt = load_frag_tr<T, D>(k, db * 32, rowof, lane);
-                    dq[db] = MM::mma(akt, bs, dq[db]);
+                for (int it2 = 0; it2 < NI; ++it2) {
+                    const int u = it2 / DB, db = it2 % DB;
+                    if (it2 + 1 < NI)
+                        akt[(it2 + 1) & 1] = load_frag_tr<T, D>(k, ((it2 + 1) % DB) * 32, rowof_u((it2 + 1) / DB), lane);
+                    __builtin_amdgcn_sched_barrier(0);
+                    dq[db] = MM::mma(akt[it2 & 1], bs[u], dq[db]);
+                    __builtin_amdgcn_sched_barrier(0);
                 }
             }
         }

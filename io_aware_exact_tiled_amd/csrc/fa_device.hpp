@@ -116,6 +116,29 @@ struct Swz {
     }
 };
 
+// Row-major tile read both row-wise (16 consecutive rows, one 16-byte unit
+// each) and with the LDS transpose read (4 consecutive rows x 4 consecutive
+// units per 32 lanes).  With 64 banks of 4 bytes, a 256-byte row puts every
+// row at the same bank offset, so the swizzle must make (row mod 16) -> unit
+// a bijection and also spread 4 consecutive rows over 4 different unit
+// quartets: unit bits 2-3 take the row's low two bits, unit bits 0-1 the next
+// two.  For 128-byte rows the row's low bit picks the half of the 256-byte
+// window, the next bit goes to unit bit 2, the two above to unit bits 0-1.
+template <class T, int COLS>
+struct SwzTr {
+    static constexpr int EPU = 16 / (int)sizeof(T);
+    static constexpr int U = COLS / EPU;
+    static_assert(COLS % EPU == 0 && U >= 8, "rows of at least 128 bytes");
+    __device__ static inline int f(int row) {
+        if constexpr (U >= 16) return ((row & 3) << 2) | ((row >> 2) & 3);
+        else return (((row >> 1) & 1) << 2) | ((row >> 2) & 3);
+    }
+    __device__ static inline int off(int row, int col) {
+        const int u = col / EPU;
+        return row * COLS + ((u ^ f(row)) * EPU) + (col % EPU);
+    }
+};
+
 // ---------------------------------------------------------------------------
 // Philox4x32-10 (Salmon, Moraes, Dror, Shaw, SC'11): ten rounds of two
 // 32x32->64-bit products on counter words 0 and 2, the key added into the
@@ -202,7 +225,7 @@ typedef __attribute__((address_space(1))) void glb_void;
 // awaited with s_waitcnt before the barrier that publishes the tile.
 template <class T, int ROWS, int D>
 __device__ inline void dma_rows(T* tile, const T* head, int row0, int N, int wave, int lane) {
-    typedef Swz<T, D> L;
+    typedef SwzTr<T, D> L;
     constexpr int EPU = 16 / (int)sizeof(T);
     constexpr int UPR = D / EPU;
     constexpr int UNITS = ROWS * UPR;
@@ -230,7 +253,7 @@ __device__ inline void dma_rows(T* tile, const T* head, int row0, int N, int wav
 // fragment), columns col0 + 16*(G%2) + 4*(s%4) .. +3.
 template <class T, int D, class RowOf>
 __device__ inline typename Mma<T>::frag load_frag_tr(const T* tile, int col0, RowOf rowof, int lane) {
-    typedef Swz<T, D> L;
+    typedef SwzTr<T, D> L;
     typedef short v4s __attribute__((ext_vector_type(4)));
     typedef __attribute__((address_space(3))) v4s lds_v4s;
     if constexpr (Mma<T>::E == 8) {
