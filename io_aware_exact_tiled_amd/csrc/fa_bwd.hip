@@ -183,6 +183,12 @@ __global__ __launch_bounds__(256, 1) void bwd_kv_kernel(BwdArgs a) {
         const bool ok = krow < N;
         kf[ks] = ok ? load_frag<T>(Kg + (size_t)krow * D + ks * 2 * E + hl * E) : zero_frag<T>();
         vf[ks] = ok ? load_frag<T>(Vg + (size_t)krow * D + ks * 2 * E + hl * E) : zero_frag<T>();
+        // K_j, V_j fragments are only ever MFMA operands: keep them in AGPRs
+        // (register-class constraint only, no instruction) so the VGPRs hold S, dP
+        if constexpr (E == 8) {
+            asm volatile("" : "+a"(kf[ks]));
+            asm volatile("" : "+a"(vf[ks]));
+        }
     }
     f32x16 dk[DB], dv[DB];
 #pragma unroll
@@ -398,6 +404,7 @@ __global__ __launch_bounds__(256, sizeof(T) == 4 ? 1 : 2) void bwd_dq_kernel(Bwd
             // S^T = K Q^T, dP_hat^T = V dO^T: lane holds query qrow, keys kv0 + 16hl + r
             // (operands of step ks+1 read before the MFMAs of step ks)
             f32x16 s = zero16(), dp = zero16();
+            __builtin_amdgcn_s_setprio(1);
             {
                 typename MM::frag ak[2], av[2];
                 ak[0] = load_frag<T>(k + LK::off(ln, hl * E));
@@ -414,6 +421,7 @@ __global__ __launch_bounds__(256, sizeof(T) == 4 ? 1 : 2) void bwd_dq_kernel(Bwd
                     __builtin_amdgcn_sched_barrier(0);
                 }
             }
+            __builtin_amdgcn_s_setprio(0);
             const bool edge = (kv0 + BC > kend) || (causal && kv0 + BC - 1 > qw0);
             float ds[16];
             uint32_t keep = 0xFFFFu;
@@ -451,6 +459,7 @@ __global__ __launch_bounds__(256, sizeof(T) == 4 ? 1 : 2) void bwd_dq_kernel(Bwd
                     return [=](int kk) { return row_slot((kk / E) * 16 + u * E + kk % E); };
                 };
                 constexpr int NI = PU * DB;
+                __builtin_amdgcn_s_setprio(1);
                 typename MM::frag akt[2];
                 akt[0] = load_frag_tr<T, D>(k, 0, rowof_u(0), lane);
 #pragma unroll
@@ -462,6 +471,7 @@ __global__ __launch_bounds__(256, sizeof(T) == 4 ? 1 : 2) void bwd_dq_kernel(Bwd
                     dq[db] = MM::mma(akt[it2 & 1], bs[u], dq[db]);
                     __builtin_amdgcn_sched_barrier(0);
                 }
+                __builtin_amdgcn_s_setprio(0);
             }
         }
         __builtin_amdgcn_s_waitcnt(0);   // this wave's DMA into the other buffer has landed

@@ -220,6 +220,7 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdArgs a) {
             const TV* v = sV + buf * TILE_K;
             // ---- S^T = K_j Q^T (operands of one 32-key block loaded together)
             f32x16 s[KB];
+            __builtin_amdgcn_s_setprio(1);
 #pragma unroll
             for (int kb = 0; kb < KB; ++kb) {
                 s[kb] = zero16();
@@ -227,6 +228,7 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdArgs a) {
                 for (int ks = 0; ks < KS; ++ks)
                     s[kb] = MS::mma(load_frag<T>(k + LK::off(kb * 32 + ln, ks * 2 * E + hl * E)), qf[ks], s[kb]);
             }
+            __builtin_amdgcn_s_setprio(0);
             if (__builtin_expect(edge, 0)) {
 #pragma unroll
                 for (int kb = 0; kb < KB; ++kb)
@@ -278,6 +280,7 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdArgs a) {
                     }
             }
             // ---- O^T += V_j^T P^T
+            __builtin_amdgcn_s_setprio(1);
 #pragma unroll
             for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
@@ -288,6 +291,7 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdArgs a) {
                         oacc[db] = MV::mma(load_frag<TV>(v + LV::off(db * 32 + ln, kb * 32 + hl * 16 + u * EV)), bp,
                                            oacc[db]);
                 }
+            __builtin_amdgcn_s_setprio(0);
         };
         if (!(causal && kv0 > qw0 + 31))   // else: no valid key for this wave's rows
             tile_math((kv0 + BC > kend) || (causal && kv0 + BC - 1 > qw0));
