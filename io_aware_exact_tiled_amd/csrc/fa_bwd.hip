@@ -13,11 +13,10 @@
 //
 // Kernels, in launch order on the caller's stream:
 //   1. bwd_pre:  D = rowsum(dO o O) in fp32 (workspace).
-//   2. bwd_kv:   one workgroup (4 waves) per 128 keys of one (b, h); each wave
-//                owns 32 keys, keeps K_j, V_j as MFMA operands in registers and
-//                dK_j, dV_j in fp32 accumulators, and walks the query tiles of
-//                BR rows that hold a valid pair: S = Q K^T, dP = dO V^T,
-//                dV += P^T dO, dK += dS^T Q.
+//   2. bwd_kv:   one workgroup (8 waves) per 128 keys of one (b, h); two waves
+//                per 32 keys, one holding K_j and dV_j, the other V_j and dK_j;
+//                it walks the query tiles of BR rows that hold a valid pair:
+//                S = Q K^T, dP = dO V^T, dV += P^T dO, dK += dS^T Q.
 //   3. bwd_dq:   one workgroup (4 waves) per 128 query rows; each wave owns 32
 //                rows (one per lane column, with its LSE_i and D_i in
 //                registers) and walks the key tiles of 32 that hold a valid
@@ -122,10 +121,20 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(BwdArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// dK, dV: key-stationary.
+// dK, dV: key-stationary, with specialised waves.  Eight waves per workgroup,
+// two per block of 32 keys (waves w and w+4 share a SIMD):
+//   A (w < 4):  holds K_j; S = Q K^T, P = exp(S - LSE) with the masks, hands P
+//               to its partner through LDS, dV_j += (P o Z/(1-p))^T dO.
+//   B (w >= 4): holds V_j; dP = dO V^T, then with P from its partner
+//               dS = P o (dP o Z/(1-p) - D), dK_j += dS^T Q.
+// Each wave keeps one operand block and one accumulator block, so two waves
+// fit on a SIMD and one's exponentials overlap the other's MFMAs.  A and B
+// hold the same (key, query) elements in the same lane and register, so the
+// hand-off is a plain per-lane copy.
 template <class T, int D, bool DROP>
-__global__ __launch_bounds__(256, 1) void bwd_kv_kernel(BwdArgs a) {
+__global__ __launch_bounds__(512, 1) void bwd_kv_kernel(BwdArgs a) {
     typedef Mma<T> MM;
+    constexpr int NW = 8;
     constexpr int E = MM::E;
     constexpr int BR = BwdTiles<T>::KV_BR;        // query rows per step
     constexpr int BC = BWD_KV_BC;                 // keys per workgroup
@@ -134,15 +143,20 @@ __global__ __launch_bounds__(256, 1) void bwd_kv_kernel(BwdArgs a) {
     constexpr int DB = D / 32;
     constexpr int QU = 16 / E;                    // MFMA steps over 16 queries of a lane half
     constexpr int TQ = BR * D;                    // elements per staged tensor
+    constexpr int NX = DROP ? 2 : 1;              // hand-off planes: P (and P o Z / (1-p))
     typedef SwzTr<T, D> LQ;    // Q, dO: BR rows (MFMA row order) x D
 
     __shared__ __attribute__((aligned(16))) T sQ[2 * TQ];
     __shared__ __attribute__((aligned(16))) T sdO[2 * TQ];
     __shared__ __attribute__((aligned(16))) float sLse[2 * BR];
     __shared__ __attribute__((aligned(16))) float sDel[2 * BR];
+    // hand-off [key block][plane][query block][4 chunks][64 lanes] x f32x4
+    __shared__ __attribute__((aligned(16))) f32x4 sX[4 * NX * QB * 4 * 64];
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int hl = lane >> 5, ln = lane & 31;
+    const int kb = wave & 3;                      // key block of this wave
+    const bool roleA = wave < 4;
     const int N = a.N, H = a.H;
     const int Tr = (N + BR - 1) / BR, Tc = (N + BC - 1) / BC;
     const int total = Tc * H * a.B;
@@ -150,7 +164,7 @@ __global__ __launch_bounds__(256, 1) void bwd_kv_kernel(BwdArgs a) {
     if (item >= total) return;
     const int bhi = item / Tc;
     const int jt = item % Tc;                     // key tile of this workgroup
-    const int kbase = jt * BC, kw0 = kbase + wave * 32;
+    const int kbase = jt * BC, kw0 = kbase + kb * 32;
     const size_t bh = (size_t)bhi;
     const size_t hoff = bh * (size_t)N * D;
     const T* __restrict__ Qg = (const T*)a.q + hoff;
@@ -174,32 +188,28 @@ __global__ __launch_bounds__(256, 1) void bwd_kv_kernel(BwdArgs a) {
 
     uint8_t* vis = a.tile_visits ? a.tile_visits + bh * Tr * (size_t)Tc + jt : nullptr;
     if (vis)
-        for (int i = tid; i < Tr; i += 256) vis[(size_t)i * Tc] = 0;
+        for (int i = tid; i < Tr; i += NW * 64) vis[(size_t)i * Tc] = 0;
 
     const int krow = kw0 + ln;           // this lane's key
-    typename MM::frag kf[KS], vf[KS];
+    // role A holds K_j, role B holds V_j (as the MFMA B operand of S / dP)
+    typename MM::frag kvf[KS];
+    {
+        const T* src = roleA ? Kg : Vg;
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-        const bool ok = krow < N;
-        kf[ks] = ok ? load_frag<T>(Kg + (size_t)krow * D + ks * 2 * E + hl * E) : zero_frag<T>();
-        vf[ks] = ok ? load_frag<T>(Vg + (size_t)krow * D + ks * 2 * E + hl * E) : zero_frag<T>();
-        // K_j, V_j fragments are only ever MFMA operands: keep them in AGPRs
-        // (register-class constraint only, no instruction) so the VGPRs hold S, dP
-        if constexpr (E == 8) {
-            asm volatile("" : "+a"(kf[ks]));
-            asm volatile("" : "+a"(vf[ks]));
+        for (int ks = 0; ks < KS; ++ks) {
+            kvf[ks] = krow < N ? load_frag<T>(src + (size_t)krow * D + ks * 2 * E + hl * E) : zero_frag<T>();
         }
     }
-    f32x16 dk[DB], dv[DB];
+    f32x16 acc[DB];                      // dV_j (A) or dK_j (B)
 #pragma unroll
-    for (int db = 0; db < DB; ++db) { dk[db] = zero16(); dv[db] = zero16(); }
+    for (int db = 0; db < DB; ++db) acc[db] = zero16();
 
     // ---- staging of one query tile: Q, dO by global->LDS DMA; LSE, D via registers
     float lreg = 0.0f;
     auto load_tile = [&](int i, int buf) {
         const int q0 = i * BR;
-        dma_rows<T, BR, D>(sQ + buf * TQ, Qg, q0, N, wave, lane);
-        dma_rows<T, BR, D>(sdO + buf * TQ, dOg, q0, N, wave, lane);
+        dma_rows<T, BR, D, NW>(sQ + buf * TQ, Qg, q0, N, wave, lane);
+        dma_rows<T, BR, D, NW>(sdO + buf * TQ, dOg, q0, N, wave, lane);
         if (tid < 2 * BR) {
             const int q = q0 + (tid % BR);
             lreg = (q < N) ? (tid < BR ? lseg[q] : delg[q]) : (tid < BR ? INFINITY : 0.0f);
@@ -208,6 +218,9 @@ __global__ __launch_bounds__(256, 1) void bwd_kv_kernel(BwdArgs a) {
     auto publish_stats = [&](int buf) {
         if (tid < BR) sLse[buf * BR + tid] = lreg * 1.4426950408889634f;
         else if (tid < 2 * BR) sDel[buf * BR + tid - BR] = lreg;
+    };
+    auto xslot = [&](int plane, int qb, int chunk) -> f32x4* {
+        return &sX[(((kb * NX + plane) * QB + qb) * 4 + chunk) * 64 + lane];
     };
 
     const float c = a.scale_log2;
@@ -225,37 +238,37 @@ __global__ __launch_bounds__(256, 1) void bwd_kv_kernel(BwdArgs a) {
         const int in = tile_at(i + 1);
         if (in >= 0) load_tile(in, buf ^ 1);   // lands in the other buffer during this step
 
-        {   // no per-wave skip: a wave whose keys all lie above this tile's rows (first
-            // causal step only) or past the key length runs the edge path with P = 0,
-            // which keeps dK, dV in the MFMA accumulators across the loop
-            const T* q = sQ + buf * TQ;
-            const T* o = sdO + buf * TQ;
-            const float* ls = sLse + buf * BR;
-            const float* dl = sDel + buf * BR;
+        const T* q = sQ + buf * TQ;
+        const T* o = sdO + buf * TQ;
+        const float* ls = sLse + buf * BR;
+        const float* dl = sDel + buf * BR;
+        // first product: S = Q K^T (A) or dP_hat = dO V^T (B); lane holds key krow,
+        // queries q0 + 32qb + 16hl + r
+        f32x16 sp[QB];
+        __builtin_amdgcn_s_setprio(1);
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb) {
+            const T* src = roleA ? q : o;
+            sp[qb] = zero16();
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks)
+                sp[qb] = MM::mma(load_frag<T>(src + LQ::off(qb * 32 + ln, ks * 2 * E + hl * E)), kvf[ks], sp[qb]);
+        }
+        __builtin_amdgcn_s_setprio(0);
+
+        if (roleA) {
+            // P = exp(S - LSE) with the masks, handed to B; then dV_j += Pd^T dO
             const bool edge = (causal && kw0 + 31 > q0) || (kw0 + 32 > kend) || (q0 + BR > N);
 #pragma unroll
             for (int qb = 0; qb < QB; ++qb) {
-                // S = Q K^T, dP_hat = dO V^T: lane holds key krow, queries q0 + 32qb + 16hl + r
-                f32x16 s = zero16(), dp = zero16();
-#pragma unroll
-                for (int ks = 0; ks < KS; ++ks) {
-                    const typename MM::frag aq = load_frag<T>(q + LQ::off(qb * 32 + ln, ks * 2 * E + hl * E));
-                    s = MM::mma(aq, kf[ks], s);
-                    const typename MM::frag ao = load_frag<T>(o + LQ::off(qb * 32 + ln, ks * 2 * E + hl * E));
-                    dp = MM::mma(ao, vf[ks], dp);
-                }
-                const int qr0 = qb * 32 + hl * 16;     // first query of this lane half, tile-local
-                float lsv[16], dlv[16];
+                const int qr0 = qb * 32 + hl * 16;
+                float p[16];
 #pragma unroll
                 for (int g = 0; g < 4; ++g) {
                     const f32x4 l4 = *reinterpret_cast<const f32x4*>(ls + qr0 + 4 * g);
-                    const f32x4 d4 = *reinterpret_cast<const f32x4*>(dl + qr0 + 4 * g);
 #pragma unroll
-                    for (int e = 0; e < 4; ++e) { lsv[4 * g + e] = l4[e]; dlv[4 * g + e] = d4[e]; }
+                    for (int e = 0; e < 4; ++e) p[4 * g + e] = fast_exp2(fmaf(sp[qb][4 * g + e], c, -l4[e]));
                 }
-                float pd[16], ds[16], p[16];
-#pragma unroll
-                for (int r = 0; r < 16; ++r) p[r] = fast_exp2(fmaf(s[r], c, -lsv[r]));
                 if (__builtin_expect(edge, 0)) {
 #pragma unroll
                     for (int r = 0; r < 16; ++r) {
@@ -264,56 +277,90 @@ __global__ __launch_bounds__(256, 1) void bwd_kv_kernel(BwdArgs a) {
                     }
                 }
 #pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    float dpr = dp[r];
-                    if constexpr (DROP) {
+                for (int g = 0; g < 4; ++g) {
+                    const f32x4 v4 = {p[4 * g], p[4 * g + 1], p[4 * g + 2], p[4 * g + 3]};
+                    *xslot(0, qb, g) = v4;
+                }
+                if constexpr (DROP) {
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) {
                         const uint32_t bits = keep4((uint32_t)krow >> 2, (uint32_t)(q0 + qr0 + r), (uint32_t)bh,
                                                     a.drop.off, a.drop.k0, a.drop.k1, a.drop.thr);
-                        const float z = ((bits >> (krow & 3)) & 1u) ? a.drop.keep_scale : 0.0f;
-                        pd[r] = p[r] * z;
-                        dpr *= z;
-                    } else {
-                        pd[r] = p[r];
+                        p[r] *= ((bits >> (krow & 3)) & 1u) ? a.drop.keep_scale : 0.0f;
                     }
-                    ds[r] = p[r] * (dpr - dlv[r]);
+#pragma unroll
+                    for (int g = 0; g < 4; ++g) {
+                        const f32x4 v4 = {p[4 * g], p[4 * g + 1], p[4 * g + 2], p[4 * g + 3]};
+                        *xslot(1, qb, g) = v4;
+                    }
                 }
-                // dV_j += Pd^T dO_i ; dK_j += dS^T Q_i.  B operands are the dO and Q
-                // tiles read transposed: k-slot kk of MFMA u is query row
-                // 32qb + 16(kk/E) + uE + kk%E of the tile.
+                sp[qb] = zero16();   // reuse as nothing; keeps the register set small
+#pragma unroll
+                for (int r = 0; r < 16; ++r) sp[qb][r] = p[r];
+            }
+        }
+        __syncthreads();   // P handed over
+        __builtin_amdgcn_s_setprio(1);
+        if (roleA) {
+#pragma unroll
+            for (int qb = 0; qb < QB; ++qb)
 #pragma unroll
                 for (int u = 0; u < QU; ++u) {
-                    const typename MM::frag ap = pack_f<T>(&pd[u * E]);
+                    float pr[E];
+#pragma unroll
+                    for (int e = 0; e < E; ++e) pr[e] = sp[qb][u * E + e];
+                    const typename MM::frag ap = pack_f<T>(pr);
+                    auto rowof = [&](int kk) { return row_slot(qb * 32 + (kk / E) * 16 + u * E + kk % E); };
+#pragma unroll
+                    for (int db = 0; db < DB; ++db)
+                        acc[db] = MM::mma(ap, load_frag_tr<T, D>(o, db * 32, rowof, lane), acc[db]);
+                }
+        } else {
+#pragma unroll
+            for (int qb = 0; qb < QB; ++qb) {
+                const int qr0 = qb * 32 + hl * 16;
+                float ds[16];
+#pragma unroll
+                for (int g = 0; g < 4; ++g) {
+                    const f32x4 p4 = *xslot(0, qb, g);
+                    const f32x4 d4 = *reinterpret_cast<const f32x4*>(dl + qr0 + 4 * g);
+                    if constexpr (DROP) {
+                        // dS = P dP_hat Z/(1-p) - P D = Pd dP_hat - P D
+                        const f32x4 pd4 = *xslot(1, qb, g);
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) ds[4 * g + e] = pd4[e] * sp[qb][4 * g + e] - p4[e] * d4[e];
+                    } else {
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) ds[4 * g + e] = p4[e] * (sp[qb][4 * g + e] - d4[e]);
+                    }
+                }
+#pragma unroll
+                for (int u = 0; u < QU; ++u) {
                     const typename MM::frag as = pack_f<T>(&ds[u * E]);
                     auto rowof = [&](int kk) { return row_slot(qb * 32 + (kk / E) * 16 + u * E + kk % E); };
 #pragma unroll
-                    for (int db = 0; db < DB; ++db) {
-                        const typename MM::frag bo = load_frag_tr<T, D>(o, db * 32, rowof, lane);
-                        dv[db] = MM::mma(ap, bo, dv[db]);
-                        const typename MM::frag bq = load_frag_tr<T, D>(q, db * 32, rowof, lane);
-                        dk[db] = MM::mma(as, bq, dk[db]);
-                    }
+                    for (int db = 0; db < DB; ++db)
+                        acc[db] = MM::mma(as, load_frag_tr<T, D>(q, db * 32, rowof, lane), acc[db]);
                 }
             }
         }
+        __builtin_amdgcn_s_setprio(0);
         if (in >= 0) publish_stats(buf ^ 1);
         __builtin_amdgcn_s_waitcnt(0);   // this wave's DMA into the other buffer has landed
-        __syncthreads();
+        __syncthreads();                 // also: the hand-off buffer may be overwritten
         buf ^= 1;
         i = in;
     }
 
-    // ---- dK_j = scale * acc, dV_j = acc (lane holds column db*32+ln, rows = keys)
-    T* dKg = (T*)a.dk + hoff;
-    T* dVg = (T*)a.dv + hoff;
+    // ---- dV_j = acc (A), dK_j = scale * acc (B); lane holds column db*32+ln, rows = keys
+    T* dst = (T*)(roleA ? a.dv : a.dk) + hoff;
+    const float sc = roleA ? 1.0f : a.scale;
 #pragma unroll
     for (int db = 0; db < DB; ++db)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
             const int key = kw0 + 8 * (r / 4) + 4 * hl + (r % 4);
-            if (key < N) {
-                dKg[(size_t)key * D + db * 32 + ln] = (T)(dk[db][r] * a.scale);
-                dVg[(size_t)key * D + db * 32 + ln] = (T)dv[db][r];
-            }
+            if (key < N) dst[(size_t)key * D + db * 32 + ln] = (T)(acc[db][r] * sc);
         }
 }
 
@@ -506,7 +553,7 @@ hipError_t launch_t(const BwdArgs& a, hipStream_t s) {
     const int dq_total = ((a.N + BWD_DQ_BR - 1) / BWD_DQ_BR) * a.H * a.B;
     if (a.ev_begin && (e = hipEventRecord(a.ev_begin, s)) != hipSuccess) return e;
     e = hipLaunchKernel((const void*)&bwd_kv_kernel<T, D, DROP>, dim3((unsigned)(8 * ((kv_total + 7) / 8))),
-                        dim3(256), args, 0, s);
+                        dim3(512), args, 0, s);
     if (e != hipSuccess) return e;
     if (a.ev_mid && (e = hipEventRecord(a.ev_mid, s)) != hipSuccess) return e;
     e = hipLaunchKernel((const void*)&bwd_dq_kernel<T, D, DROP>, dim3((unsigned)(8 * ((dq_total + 7) / 8))),

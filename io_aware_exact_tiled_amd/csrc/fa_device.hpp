@@ -221,18 +221,18 @@ typedef __attribute__((address_space(1))) void glb_void;
 // global-to-LDS loads.  One such load writes the 64 lanes' 16 bytes to 64
 // consecutive LDS units, so each lane fetches the global chunk that belongs
 // at its unit.  Rows past N read row N-1 (finite data; those rows are masked
-// by the caller).  Issued by all 4 waves of the workgroup; completion is
+// by the caller).  Issued by all NW waves of the workgroup; completion is
 // awaited with s_waitcnt before the barrier that publishes the tile.
-template <class T, int ROWS, int D>
+template <class T, int ROWS, int D, int NW = 4>
 __device__ inline void dma_rows(T* tile, const T* head, int row0, int N, int wave, int lane) {
     typedef SwzTr<T, D> L;
     constexpr int EPU = 16 / (int)sizeof(T);
     constexpr int UPR = D / EPU;
     constexpr int UNITS = ROWS * UPR;
-    static_assert(UNITS % 256 == 0, "tile must be a whole number of workgroup-wide loads");
+    static_assert(UNITS % (64 * NW) == 0, "tile must be a whole number of workgroup-wide loads");
 #pragma unroll
-    for (int n = 0; n < UNITS / 256; ++n) {
-        const int blk = n * 4 + wave;                 // this wave's 64-unit block
+    for (int n = 0; n < UNITS / (64 * NW); ++n) {
+        const int blk = n * NW + wave;                // this wave's 64-unit block
         const int P = blk * 64 + lane;                // LDS unit written by this lane
         const int slot = P / UPR, pu = P % UPR;
         const int u = pu ^ L::f(slot);
