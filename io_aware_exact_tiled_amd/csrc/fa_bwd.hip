@@ -244,15 +244,30 @@ __global__ __launch_bounds__(512, 1) void bwd_kv_kernel(BwdArgs a) {
         const float* dl = sDel + buf * BR;
         // first product: S = Q K^T (A) or dP_hat = dO V^T (B); lane holds key krow,
         // queries q0 + 32qb + 16hl + r
+        // (software-pipelined: the operands of step ks+1 are read before the
+        // MFMAs of step ks are issued)
         f32x16 sp[QB];
         __builtin_amdgcn_s_setprio(1);
-#pragma unroll
-        for (int qb = 0; qb < QB; ++qb) {
+        {
             const T* src = roleA ? q : o;
-            sp[qb] = zero16();
+            typename MM::frag fa[2][QB];
 #pragma unroll
-            for (int ks = 0; ks < KS; ++ks)
-                sp[qb] = MM::mma(load_frag<T>(src + LQ::off(qb * 32 + ln, ks * 2 * E + hl * E)), kvf[ks], sp[qb]);
+            for (int qb = 0; qb < QB; ++qb) {
+                sp[qb] = zero16();
+                fa[0][qb] = load_frag<T>(src + LQ::off(qb * 32 + ln, hl * E));
+            }
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks) {
+                if (ks + 1 < KS) {
+#pragma unroll
+                    for (int qb = 0; qb < QB; ++qb)
+                        fa[(ks + 1) & 1][qb] = load_frag<T>(src + LQ::off(qb * 32 + ln, (ks + 1) * 2 * E + hl * E));
+                }
+                __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+                for (int qb = 0; qb < QB; ++qb) sp[qb] = MM::mma(fa[ks & 1][qb], kvf[ks], sp[qb]);
+                __builtin_amdgcn_sched_barrier(0);
+            }
         }
         __builtin_amdgcn_s_setprio(0);
 
