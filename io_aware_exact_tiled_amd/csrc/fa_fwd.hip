@@ -219,14 +219,37 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdArgs a) {
             const T* k = sK + buf * TILE_K;
             const TV* v = sV + buf * TILE_K;
             // ---- S^T = K_j Q^T (operands of one 32-key block loaded together)
+            // (software-pipelined: the K operands of step ks+1 are read
+            // before the MFMAs of step ks are issued; not with dropout at
+            // d=128, where the registers are short)
+            constexpr bool PIPE = !(DROP && D == 128);
+            auto fence = [] { if constexpr (PIPE) __builtin_amdgcn_sched_barrier(0); };
             f32x16 s[KB];
             __builtin_amdgcn_s_setprio(1);
+            {
+                typename MS::frag kf[2][KB];
 #pragma unroll
-            for (int kb = 0; kb < KB; ++kb) {
-                s[kb] = zero16();
+                for (int kb = 0; kb < KB; ++kb) {
+                    s[kb] = zero16();
+                    kf[0][kb] = load_frag<T>(k + LK::off(kb * 32 + ln, hl * E));
+                }
 #pragma unroll
-                for (int ks = 0; ks < KS; ++ks)
-                    s[kb] = MS::mma(load_frag<T>(k + LK::off(kb * 32 + ln, ks * 2 * E + hl * E)), qf[ks], s[kb]);
+                for (int ks = 0; ks < KS; ++ks) {
+                    if (!PIPE && ks > 0) {
+#pragma unroll
+                        for (int kb = 0; kb < KB; ++kb)
+                            kf[ks & 1][kb] = load_frag<T>(k + LK::off(kb * 32 + ln, ks * 2 * E + hl * E));
+                    }
+                    if (PIPE && ks + 1 < KS) {
+#pragma unroll
+                        for (int kb = 0; kb < KB; ++kb)
+                            kf[(ks + 1) & 1][kb] = load_frag<T>(k + LK::off(kb * 32 + ln, (ks + 1) * 2 * E + hl * E));
+                    }
+                    fence();
+#pragma unroll
+                    for (int kb = 0; kb < KB; ++kb) s[kb] = MS::mma(kf[ks & 1][kb], qf[ks], s[kb]);
+                    fence();
+                }
             }
             __builtin_amdgcn_s_setprio(0);
             if (__builtin_expect(edge, 0)) {
@@ -280,17 +303,29 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdArgs a) {
                     }
             }
             // ---- O^T += V_j^T P^T
+            // (software-pipelined over the flattened (kb, u, db) steps, two
+            // V^T operands ahead)
             __builtin_amdgcn_s_setprio(1);
+            {
+                constexpr int NS = KB * PU * DB, PF = PIPE ? 2 : 1;
+                auto vfrag = [&](int st) {
+                    const int db = st % DB, u = (st / DB) % PU, kb = st / (DB * PU);
+                    return load_frag<TV>(v + LV::off(db * 32 + ln, kb * 32 + hl * 16 + u * EV));
+                };
+                typename MV::frag vf[PF + 1];
 #pragma unroll
-            for (int kb = 0; kb < KB; ++kb)
+                for (int st = 0; st < PF; ++st) vf[st] = vfrag(st);
+                typename MV::frag bp;
 #pragma unroll
-                for (int u = 0; u < PU; ++u) {
-                    const typename MV::frag bp = pack_p<TV>(&p[kb][u * EV]);
-#pragma unroll
-                    for (int db = 0; db < DB; ++db)
-                        oacc[db] = MV::mma(load_frag<TV>(v + LV::off(db * 32 + ln, kb * 32 + hl * 16 + u * EV)), bp,
-                                           oacc[db]);
+                for (int st = 0; st < NS; ++st) {
+                    if (st + PF < NS) vf[(st + PF) % (PF + 1)] = vfrag(st + PF);
+                    const int db = st % DB, u = (st / DB) % PU, kb = st / (DB * PU);
+                    if (db == 0) bp = pack_p<TV>(&p[kb][u * EV]);
+                    fence();
+                    oacc[db] = MV::mma(vf[st % (PF + 1)], bp, oacc[db]);
+                    fence();
                 }
+            }
             __builtin_amdgcn_s_setprio(0);
         };
         if (!(causal && kv0 > qw0 + 31))   // else: no valid key for this wave's rows
