@@ -120,6 +120,7 @@ def time_workload(w, steps, warmup, ev):
     lse = torch.empty(w.B, w.H, w.N, dtype=torch.float32, device=dev)
     grads = tuple(torch.empty_like(q) for _ in range(3))
     ws = torch.empty(fa.bwd_workspace_bytes(w.B, w.H, w.N, w.d), dtype=torch.uint8, device=dev)
+    fws = torch.empty(max(1, fa.fwd_workspace_bytes(w.B, w.H, w.N, w.d, q.dtype)), dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream(dev).cuda_stream
     n_ev = steps
     f0 = [ev.create() for _ in range(n_ev)]
@@ -133,7 +134,7 @@ def time_workload(w, steps, warmup, ev):
     def step(i=None):
         if i is not None:
             ev.record(s0[i], stream)
-        fa.fwd(q, k, v, out=o, lse=lse, events=None if i is None else (f0[i], f1[i]), **kw)
+        fa.fwd(q, k, v, out=o, lse=lse, workspace=fws, events=None if i is None else (f0[i], f1[i]), **kw)
         fa.bwd(q, k, v, o, do, lse, grads=grads, workspace=ws,
                events=None if i is None else (b0[i], b1[i], bm[i]), **kw)
         if i is not None:

@@ -29,9 +29,10 @@
  *
  * Conventions for every entry point:
  *  - Pointers are device memory owned by the caller (allocated by whatever
- *    allocator the caller uses).  The library never allocates or frees
- *    device memory and never synchronises; all work is enqueued on `stream`
- *    in order and the call returns before it completes.
+ *    allocator the caller uses), workspaces included.  The library never
+ *    allocates or frees device memory and never synchronises; all work is
+ *    enqueued on `stream` in order and the call returns before it completes.
+ *    A workspace must not be used by two calls whose work overlaps.
  *  - Q, K, V, O, dO, dQ, dK, dV are contiguous [B][H][N][d] row-major with
  *    16-byte aligned base addresses.  LSE and D are float [B][H][N].
  *    Outputs must not alias inputs.
@@ -60,7 +61,7 @@
 extern "C" {
 #endif
 
-#define FA_ABI_VERSION 1
+#define FA_ABI_VERSION 2
 
 typedef enum { FA_F32 = 0, FA_F16 = 1, FA_BF16 = 2 } fa_dtype;
 
@@ -106,21 +107,36 @@ typedef struct {
     hipEvent_t main_begin;      /* profiling: when both are non-NULL they are    */
     hipEvent_t main_end;        /* recorded on `stream` right before and right
                                    after the pass's main kernels (the forward
-                                   kernel; the backward's two S/P-recomputing
+                                   kernel, without the bf16 V pre-pass; the
+                                   backward's two S/P-recomputing
                                    kernels, without the D pre-pass)             */
     hipEvent_t main_mid;        /* fa_bwd profiling, optional: recorded between
                                    the dK/dV kernel and the dQ kernel            */
 } fa_opts;
 
+/* Bytes of device workspace fa_fwd needs.  bf16: the forward multiplies P
+ * (rounded to fp16, whose significand is 3 bits longer than bf16's) with an
+ * fp16 copy of V scaled by a power of two per (b, h), V * 2^-e_bh, with e_bh
+ * chosen from the largest finite |V| of that head so that it lands in
+ * [2^14, 2^15); every bf16 value of magnitude >= 2^(e_bh - 17) converts
+ * exactly.  The workspace holds that copy (B*H*N*d fp16) plus 4-byte
+ * per-head statistics, each part rounded up to 256 bytes.  fp16 and fp32
+ * need none: 0.  Returns 0 for invalid sizes or dtypes. */
+size_t fa_fwd_workspace_bytes(int32_t B, int32_t H, int32_t N, int32_t d, fa_dtype dtype);
+
 /* Forward pass.  Q, K, V: [B][H][N][d] of `dtype`.  O: [B][H][N][d] of
  * `dtype`, or fp32 when opts->o_fp32 is set.  LSE: float [B][H][N].
  * causal: nonzero for the lower-triangular mask.  dropout_p in [0, 1); seed
  * selects the Philox key.  block_mask: device uint8[ceil(N/128)][ceil(N/128)],
- * shared by all (b, h), nonzero = compute; NULL = dense. */
+ * shared by all (b, h), nonzero = compute; NULL = dense.  workspace: device
+ * memory of at least fa_fwd_workspace_bytes(B, H, N, d, dtype) bytes,
+ * 256-byte aligned (may be NULL when that is 0); its contents on return are
+ * unspecified. */
 fa_status fa_fwd(const void* Q, const void* K, const void* V, void* O, float* LSE,
                  int32_t B, int32_t H, int32_t N, int32_t d, fa_dtype dtype,
                  float scale, int32_t causal, float dropout_p, uint64_t seed,
-                 const uint8_t* block_mask, const fa_opts* opts, hipStream_t stream);
+                 const uint8_t* block_mask, const fa_opts* opts,
+                 void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /* Bytes of device workspace fa_bwd needs: D = rowsum(dO o O) as float
  * [B][H][N], rounded up to 256 bytes.  Returns 0 for invalid sizes. */

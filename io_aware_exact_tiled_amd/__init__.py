@@ -21,7 +21,8 @@ import torch
 from . import _lib
 from ._lib import FaOpts, check
 
-__all__ = ["fwd", "bwd", "dropout_keep_mask", "tile_shape", "bwd_workspace_bytes", "abi_version"]
+__all__ = ["fwd", "bwd", "dropout_keep_mask", "tile_shape", "fwd_workspace_bytes", "bwd_workspace_bytes",
+           "abi_version"]
 
 _DT = {torch.float32: _lib.FA_F32, torch.float16: _lib.FA_F16, torch.bfloat16: _lib.FA_BF16}
 
@@ -90,13 +91,18 @@ def _mask_ptr(block_mask, device, N):
     return bm, bm.data_ptr()
 
 
+def fwd_workspace_bytes(B, H, N, d, dtype: torch.dtype) -> int:
+    return int(_lib.lib().fa_fwd_workspace_bytes(B, H, N, d, _DT[dtype]))
+
+
 def fwd(q, k, v, *, causal=False, dropout_p=0.0, seed=0, rng_offset=0, key_lens=None, block_mask=None,
         scale: Optional[float] = None, o_fp32=False, record_tiles=False, reverse_kv=False,
-        out=None, lse=None, events=None):
+        out=None, lse=None, workspace=None, events=None):
     """Forward pass.  Returns (O, LSE) or (O, LSE, tile_visits) when
     record_tiles is set.  `events` = (hipEvent_t, hipEvent_t) raw handles
     recorded around the kernel (profiling).  O is fp32 when o_fp32, else q's dtype; LSE is fp32
-    [B, H, N]."""
+    [B, H, N].  `workspace`: a uint8 device tensor of fwd_workspace_bytes
+    (allocated here when None and needed)."""
     _check_qkv(q, k, v)
     B, H, N, d = q.shape
     scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
@@ -107,11 +113,16 @@ def fwd(q, k, v, *, causal=False, dropout_p=0.0, seed=0, rng_offset=0, key_lens=
     opts, keep, tiles = _opts(B, H, N, d, 0, key_lens, rng_offset, o_fp32, record_tiles, reverse_kv,
                               q.device, dt, events)
     bm, bmp = _mask_ptr(block_mask, q.device, N)
+    need = fwd_workspace_bytes(B, H, N, d, q.dtype)
+    ws = workspace
+    if ws is None and need:
+        ws = torch.empty(need, dtype=torch.uint8, device=q.device)
     code = _lib.lib().fa_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), l.data_ptr(),
                              B, H, N, d, dt, scale, 1 if causal else 0, float(dropout_p), int(seed),
-                             bmp, ctypes.byref(opts), _stream(q.device))
+                             bmp, ctypes.byref(opts), ws.data_ptr() if ws is not None else None,
+                             ws.numel() if ws is not None else 0, _stream(q.device))
     check(code, "fa_fwd")
-    del keep, bm
+    del keep, bm, ws
     return (o, l, tiles) if record_tiles else (o, l)
 
 

@@ -23,7 +23,7 @@ STATUS = {
 }
 
 # every symbol include/fa.h declares
-EXPORTS = ("fa_fwd", "fa_bwd", "fa_bwd_workspace_bytes", "fa_dropout_keep_mask", "fa_tile_shape",
+EXPORTS = ("fa_fwd", "fa_fwd_workspace_bytes", "fa_bwd", "fa_bwd_workspace_bytes", "fa_dropout_keep_mask", "fa_tile_shape",
            "fa_status_string", "fa_last_hip_error", "fa_abi_version")
 
 
@@ -61,8 +61,10 @@ def lib():
         L = ctypes.CDLL(LIB_PATH)
         vp, i32, u64, f32, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_uint64, ctypes.c_float, ctypes.c_size_t
         L.fa_fwd.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, f32, i32, f32, u64, vp,
-                             ctypes.POINTER(FaOpts), vp]
+                             ctypes.POINTER(FaOpts), vp, sz, vp]
         L.fa_fwd.restype = i32
+        L.fa_fwd_workspace_bytes.argtypes = [i32, i32, i32, i32, i32]
+        L.fa_fwd_workspace_bytes.restype = sz
         L.fa_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, f32, i32, f32, u64,
                              vp, ctypes.POINTER(FaOpts), vp, sz, vp]
         L.fa_bwd.restype = i32

@@ -73,7 +73,6 @@ fa::DropArgs drop_args(float p, uint64_t seed, const fa_opts* opts) {
 
 constexpr float LOG2E = 1.4426950408889634f;
 
-size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 }  // namespace
 
@@ -114,14 +113,23 @@ fa_status fa_tile_shape(int32_t d, fa_dtype dtype, int32_t pass, int32_t* Br, in
     return FA_ERR_OPTS;
 }
 
+size_t fa_fwd_workspace_bytes(int32_t B, int32_t H, int32_t N, int32_t d, fa_dtype dtype) {
+    if (check_shape(B, H, N, d) != FA_OK || !valid_dtype(dtype)) return 0;
+    return dtype == FA_BF16 ? fa::fwd_workspace_layout(B, H, N, d).bytes : 0;
+}
+
 fa_status fa_fwd(const void* Q, const void* K, const void* V, void* O, float* LSE, int32_t B, int32_t H,
                  int32_t N, int32_t d, fa_dtype dtype, float scale, int32_t causal, float dropout_p,
-                 uint64_t seed, const uint8_t* block_mask, const fa_opts* opts, hipStream_t stream) {
+                 uint64_t seed, const uint8_t* block_mask, const fa_opts* opts, void* workspace,
+                 size_t workspace_bytes, hipStream_t stream) {
     if (!Q || !K || !V || !O || !LSE) return FA_ERR_NULL;
     fa_status st = check_common(B, H, N, d, dtype, scale, dropout_p, opts);
     if (st != FA_OK) return st;
     if (!aligned16(Q) || !aligned16(K) || !aligned16(V) || !aligned16(O) || !aligned16(LSE))
         return FA_ERR_ALIGN;
+    const size_t need = fa_fwd_workspace_bytes(B, H, N, d, dtype);
+    if (need && (!workspace || workspace_bytes < need || (reinterpret_cast<uintptr_t>(workspace) & 255u)))
+        return FA_ERR_WORKSPACE;
     fa::FwdArgs a;
     a.q = Q; a.k = K; a.v = V; a.o = O; a.lse = LSE;
     a.B = B; a.H = H; a.N = N;
@@ -133,14 +141,14 @@ fa_status fa_fwd(const void* Q, const void* K, const void* V, void* O, float* LS
     a.reverse_kv = (opts && (opts->flags & FA_FLAG_REVERSE_KV)) ? 1 : 0;
     a.ev_begin = (opts && opts->main_end) ? opts->main_begin : nullptr;
     a.ev_end = (opts && opts->main_begin) ? opts->main_end : nullptr;
-    const hipError_t e = fa::launch_fwd(a, dtype, d, stream);
+    const hipError_t e = fa::launch_fwd(a, dtype, d, workspace, stream);
     return e == hipSuccess ? FA_OK : hip_fail(e);
 }
 
 size_t fa_bwd_workspace_bytes(int32_t B, int32_t H, int32_t N, int32_t d) {
     if (check_shape(B, H, N, d) != FA_OK) return 0;
     const size_t rows = (size_t)B * H * N;
-    return align256(rows * sizeof(float));
+    return fa::align256(rows * sizeof(float));
 }
 
 fa_status fa_bwd(const void* Q, const void* K, const void* V, const void* O, const void* dO, const float* LSE,

@@ -53,10 +53,10 @@ template <> struct Mma<float> {
     }
 };
 
-// Type used for the probability operand of P*V (and for V in LDS).  For bf16
-// inputs P is rounded to fp16 (11-bit significand) instead of bf16 (8 bits)
-// and V is converted bf16 -> fp16 while it is staged; the conversion is exact
-// for |v| in [2^-14, 65504] and loses at most 2^-25 absolute below.
+// Type used for the probability operand of the forward's P*V product (and
+// for V in LDS there).  For bf16 inputs P is rounded to fp16 (11-bit
+// significand) instead of bf16 (8 bits) and the product reads an fp16 copy
+// of V scaled by a power of two per (b, h) (see fa_fwd.hip).
 template <class T> struct PvType { typedef T type; };
 template <> struct PvType<bf16> { typedef f16 type; };
 

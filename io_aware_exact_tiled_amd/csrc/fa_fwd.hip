@@ -4,7 +4,7 @@
 // owns 32 of them.  The workgroup walks the key/value tiles of BC = 64 keys
 // that hold at least one valid pair (FlashAttention summary, xyznot.com,
 // "Method"; the query-outer / key-inner loop order of the tutorial's section
-// 12.2 pseudocode), staging K_j and V_j^T in LDS, and per tile:
+// 12.2 pseudocode), staging K_j and V_j in LDS, and per tile:
 //   S^T = K_j Q_i^T          MFMA, fp32 accumulation, one query per lane column
 //   masks on edge tiles      causal j > i, key padding j >= len_b, N tail
 //   m_new = max(m, rowmax)   lane-local max over 16 keys + one cross-half swap
@@ -20,13 +20,21 @@
 //    every lane holds one query row: the row max needs one cross-half swap,
 //    the row sum none until the epilogue, and the per-row rescale of O is a
 //    lane-local multiply.
-//  * K rows are stored in LDS in MFMA row order: MFMA row m takes key
-//    16*((m/4)%2) + 4*(m/8) + m%4, so that lane (l/32) of the accumulator
-//    holds 16 *consecutive* keys in registers r = 0..15.  Those 16 values are
-//    then exactly the B operand of the P*V product (8 consecutive keys per
-//    MFMA per lane half), with no register shuffles.
-//  * V is stored transposed (d rows, key columns) so the A operand of V^T P^T
-//    is one 16-byte LDS read per MFMA.
+//  * K and V tiles go global -> LDS with the 16-byte direct loads (no
+//    registers, no VALU), rows in MFMA row order: LDS row m of a 32-row block
+//    holds key 16*((m/4)%2) + 4*(m/8) + m%4, so that lane half h of the S^T
+//    accumulator holds the 16 *consecutive* keys 16h + r in registers r.
+//    Those 16 values are then exactly the B operand of the P*V product (8
+//    consecutive keys per MFMA per lane half), with no register shuffles.
+//  * The A operand V_j^T of that product is read from the row-major V tile
+//    with the gfx950 LDS transpose read.
+//  * bf16 inputs: P is rounded to fp16 (11-bit significand) rather than bf16
+//    (8 bits) for the P*V product, so V must be fp16 as well.  A pre-pass
+//    converts V once per call: it finds e_bh from the largest finite |V| of
+//    each (b, h) such that that value times 2^-e_bh lies in [2^14, 2^15),
+//    writes V * 2^-e_bh in fp16 to the workspace, and the epilogue multiplies
+//    O by 2^e_bh.  Every bf16 value of magnitude at least 2^(e_bh - 17)
+//    converts exactly; smaller ones are off by at most 2^(e_bh - 25).
 #include "fa_device.hpp"
 #include "fa_internal.hpp"
 
@@ -34,7 +42,7 @@ namespace fa {
 
 namespace {
 
-template <class TV> __device__ inline void store4(TV* p, float a, float b, float c, float d);
+template <class T> __device__ inline void store4(T* p, float a, float b, float c, float d);
 template <> __device__ inline void store4<f16>(f16* p, float a, float b, float c, float d) {
     f16x4 w = {(f16)a, (f16)b, (f16)c, (f16)d};
     *reinterpret_cast<f16x4*>(p) = w;
@@ -59,11 +67,68 @@ template <class TV> __device__ inline typename Mma<TV>::frag pack_p(const float*
     }
 }
 
-// MFMA row slot of key r within a 32-key block (see the file comment).
-__device__ inline int key_slot(int r) { return row_slot(r); }
+// maximum over a 256-thread workgroup (every thread gets it)
+__device__ inline uint32_t block_max256(uint32_t m) {
+    __shared__ uint32_t red[4];
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) m = max(m, (uint32_t)__shfl_xor((int)m, o));
+    if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = m;
+    __syncthreads();
+    return max(max(red[0], red[1]), max(red[2], red[3]));
+}
 
 }  // namespace
 
+// ---------------------------------------------------------------------------
+// bf16 V -> fp16 pre-pass.  Workgroup w handles chunk w % nch of (b, h) =
+// w / nch.  The first kernel writes each chunk's largest finite |V| as bf16
+// magnitude bits (monotone in the value); the second reduces the chunks of
+// its (b, h), picks the exponent and converts its chunk.
+__global__ __launch_bounds__(256) void v16_absmax_kernel(V16Args a) {
+    const int tid = threadIdx.x;
+    const size_t bh = blockIdx.x / a.nch, ch = blockIdx.x % a.nch;
+    const size_t beg = ch * a.chunk;
+    const size_t end = beg + a.chunk < a.per_head ? beg + a.chunk : a.per_head;
+    const uint16_t* src = static_cast<const uint16_t*>(a.v) + bh * a.per_head;
+    uint32_t m = 0;
+    for (size_t i = beg + (size_t)tid * 8; i < end; i += 256 * 8) {
+        const u32x4 w = *reinterpret_cast<const u32x4*>(src + i);
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            const uint32_t lo = w[k] & 0x7fffu, hi = (w[k] >> 16) & 0x7fffu;
+            if (lo < 0x7f80u) m = max(m, lo);   // exponent field all ones: inf or NaN
+            if (hi < 0x7f80u) m = max(m, hi);
+        }
+    }
+    m = block_max256(m);
+    if (tid == 0) a.part[bh * a.nch + ch] = m;
+}
+
+__global__ __launch_bounds__(256) void v16_convert_kernel(V16Args a) {
+    const int tid = threadIdx.x;
+    const size_t bh = blockIdx.x / a.nch, ch = blockIdx.x % a.nch;
+    const uint32_t M = block_max256(tid < a.nch ? a.part[bh * a.nch + tid] : 0u);
+    // the largest finite |V| lies in [2^(F-127), 2^(F-126)) for its bf16
+    // exponent field F (F = 0: a subnormal, below 2^-126 and at least 2^-133)
+    const int e = M == 0 ? 0 : (int)(M >> 7) - 141;
+    if (ch == 0 && tid == 0) a.vexp[bh] = e;
+    const size_t beg = ch * a.chunk;
+    const size_t end = beg + a.chunk < a.per_head ? beg + a.chunk : a.per_head;
+    const uint16_t* src = static_cast<const uint16_t*>(a.v) + bh * a.per_head;
+    f16* dst = a.v16 + bh * a.per_head;
+    for (size_t i = beg + (size_t)tid * 8; i < end; i += 256 * 8) {
+        const u32x4 w = *reinterpret_cast<const u32x4*>(src + i);
+        f16x8 h;
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            h[2 * k] = (f16)ldexpf(__uint_as_float(w[k] << 16), -e);
+            h[2 * k + 1] = (f16)ldexpf(__uint_as_float(w[k] & 0xffff0000u), -e);
+        }
+        *reinterpret_cast<f16x8*>(dst + i) = h;
+    }
+}
+
+// ---------------------------------------------------------------------------
 template <class T, int D, bool DROP>
 __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdArgs a) {
     typedef typename PvType<T>::type TV;
@@ -76,19 +141,12 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdArgs a) {
     constexpr int KB = BC / 32;         // 32-key blocks per tile
     constexpr int DB = D / 32;          // 32-wide column blocks of O
     constexpr int PU = 16 / EV;         // P*V MFMAs per 32-key block
-    constexpr int EPU = 16 / (int)sizeof(T);
-    constexpr int DC = D / EPU;         // 16-byte chunks per row of K / V
-    constexpr int KT = BC * DC;         // K staging: one 16-byte chunk per task
-    constexpr int KN = (KT + 255) / 256;
-    constexpr int VT = (BC / 4) * DC;   // V staging: 4 rows x one chunk per task
-    constexpr int VN = (VT + 255) / 256;
-    constexpr int TILE_K = BC * D;      // elements of one K (or V^T) buffer
+    constexpr int TILE = BC * D;        // elements of one K (or V) buffer
     constexpr float RESCALE = 8.0f;     // log2 headroom before the running max moves
-    typedef Swz<T, D> LK;
-    typedef Swz<TV, BC> LV;
+    typedef SwzTr<T, D> LK;
 
-    __shared__ __attribute__((aligned(16))) T sK[2 * TILE_K];
-    __shared__ __attribute__((aligned(16))) TV sV[2 * TILE_K];
+    __shared__ __attribute__((aligned(16))) T sK[2 * TILE];
+    __shared__ __attribute__((aligned(16))) TV sV[2 * TILE];
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int hl = lane >> 5, ln = lane & 31;
@@ -100,14 +158,12 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdArgs a) {
     if (item >= total) return;
     const int bhi = item / Tr, r_ = item % Tr;
     const int it = a.mask.causal ? (Tr - 1 - r_) : r_;
-    const int b = bhi / H, h = bhi % H;
     const int q0 = it * BR, qw0 = q0 + wave * 32;
     const size_t bh = (size_t)bhi;
     const size_t hoff = bh * (size_t)N * D;
     const T* __restrict__ Qg = (const T*)a.q + hoff;
     const T* __restrict__ Kg = (const T*)a.k + hoff;
-    const T* __restrict__ Vg = (const T*)a.v + hoff;
-    (void)b; (void)h;
+    const TV* __restrict__ Vg = (const TV*)a.v + hoff;   // the fp16 copy for bf16 inputs
 
     int kend = N;
     if (a.mask.key_lens) {
@@ -140,55 +196,10 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdArgs a) {
         qf[ks] = (qrow < N) ? load_frag<T>(Qg + (size_t)qrow * D + ks * 2 * E + hl * E)
                             : zero_frag<T>();
 
-    // ---- staging: global -> registers (prefetch) -> LDS
-    u32x4 kreg[KN];
-    u32x4 vreg[VN][4];
-    auto load_tile = [&](int j) {
-        const int kv0 = j * BC;
-#pragma unroll
-        for (int n = 0; n < KN; ++n) {
-            const int t = tid + n * 256;
-            const int key = kv0 + t / DC;
-            u32x4 z = {0u, 0u, 0u, 0u};
-            kreg[n] = (t < KT && key < N) ? *reinterpret_cast<const u32x4*>(Kg + (size_t)key * D + (t % DC) * EPU)
-                                          : z;
-        }
-#pragma unroll
-        for (int n = 0; n < VN; ++n) {
-            const int t = tid + n * 256;
-#pragma unroll
-            for (int kk = 0; kk < 4; ++kk) {
-                const int key = kv0 + (t / DC) * 4 + kk;
-                u32x4 z = {0u, 0u, 0u, 0u};
-                vreg[n][kk] = (t < VT && key < N)
-                                  ? *reinterpret_cast<const u32x4*>(Vg + (size_t)key * D + (t % DC) * EPU)
-                                  : z;
-            }
-        }
-    };
-    auto store_tile = [&](int buf) {
-        T* k = sK + buf * TILE_K;
-        TV* v = sV + buf * TILE_K;
-#pragma unroll
-        for (int n = 0; n < KN; ++n) {
-            const int t = tid + n * 256;
-            if (t < KT) *reinterpret_cast<u32x4*>(k + LK::off(key_slot(t / DC), (t % DC) * EPU)) = kreg[n];
-        }
-#pragma unroll
-        for (int n = 0; n < VN; ++n) {
-            const int t = tid + n * 256;
-            if (t < VT) {
-                const int dc = t % DC, kg = t / DC;
-                const T* x0 = reinterpret_cast<const T*>(&vreg[n][0]);
-                const T* x1 = reinterpret_cast<const T*>(&vreg[n][1]);
-                const T* x2 = reinterpret_cast<const T*>(&vreg[n][2]);
-                const T* x3 = reinterpret_cast<const T*>(&vreg[n][3]);
-#pragma unroll
-                for (int dd = 0; dd < EPU; ++dd)
-                    store4<TV>(v + LV::off(dc * EPU + dd, kg * 4), to_f32(x0[dd]), to_f32(x1[dd]),
-                               to_f32(x2[dd]), to_f32(x3[dd]));
-            }
-        }
+    // K_j, V_j: global -> LDS, rows past N repeat row N-1 (masked as keys >= kend)
+    auto load_tile = [&](int j, int buf) {
+        dma_rows<T, BC, D>(sK + buf * TILE, Kg, j * BC, N, wave, lane);
+        dma_rows<TV, BC, D>(sV + buf * TILE, Vg, j * BC, N, wave, lane);
     };
 
     float m_run = -INFINITY, l_run = 0.0f;
@@ -200,10 +211,8 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdArgs a) {
     const int causal = a.mask.causal;
 
     int jj = tile_at(0);
-    if (jj >= 0) {
-        load_tile(rev ? (j_end - 1 - jj) : jj);
-        store_tile(0);
-    }
+    if (jj >= 0) load_tile(rev ? (j_end - 1 - jj) : jj, 0);
+    __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
     int buf = 0;
     while (jj >= 0) {
@@ -211,19 +220,18 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdArgs a) {
         const int kv0 = j * BC;
         if (vis && tid == 0) vis[j] = 1;
         const int jn = tile_at(jj + 1);
-        if (jn >= 0) load_tile(rev ? (j_end - 1 - jn) : jn);   // in flight during this tile's math
+        // lands in the other buffer during this tile's math; that buffer was
+        // last read before the previous barrier
+        if (jn >= 0) load_tile(rev ? (j_end - 1 - jn) : jn, buf ^ 1);
 
         // one tile of math; element masks only on tiles that straddle the
         // diagonal, the padding boundary or the N tail
         auto tile_math = [&](bool edge) {
-            const T* k = sK + buf * TILE_K;
-            const TV* v = sV + buf * TILE_K;
-            // ---- S^T = K_j Q^T (operands of one 32-key block loaded together)
+            const T* k = sK + buf * TILE;
+            const TV* v = sV + buf * TILE;
+            // ---- S^T = K_j Q^T
             // (software-pipelined: the K operands of step ks+1 are read
-            // before the MFMAs of step ks are issued; not with dropout at
-            // d=128, where the registers are short)
-            constexpr bool PIPE = !(DROP && D == 128);
-            auto fence = [] { if constexpr (PIPE) __builtin_amdgcn_sched_barrier(0); };
+            // before the MFMAs of step ks are issued)
             f32x16 s[KB];
             __builtin_amdgcn_s_setprio(1);
             {
@@ -235,20 +243,15 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdArgs a) {
                 }
 #pragma unroll
                 for (int ks = 0; ks < KS; ++ks) {
-                    if (!PIPE && ks > 0) {
-#pragma unroll
-                        for (int kb = 0; kb < KB; ++kb)
-                            kf[ks & 1][kb] = load_frag<T>(k + LK::off(kb * 32 + ln, ks * 2 * E + hl * E));
-                    }
-                    if (PIPE && ks + 1 < KS) {
+                    if (ks + 1 < KS) {
 #pragma unroll
                         for (int kb = 0; kb < KB; ++kb)
                             kf[(ks + 1) & 1][kb] = load_frag<T>(k + LK::off(kb * 32 + ln, (ks + 1) * 2 * E + hl * E));
                     }
-                    fence();
+                    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
                     for (int kb = 0; kb < KB; ++kb) s[kb] = MS::mma(kf[ks & 1][kb], qf[ks], s[kb]);
-                    fence();
+                    __builtin_amdgcn_sched_barrier(0);
                 }
             }
             __builtin_amdgcn_s_setprio(0);
@@ -302,15 +305,18 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdArgs a) {
                             if (!((bits >> e) & 1u)) p[kb][g * 4 + e] = 0.0f;
                     }
             }
-            // ---- O^T += V_j^T P^T
+            // ---- O^T += V_j^T P^T.  k-slot kk of step (kb, u) is key
+            // 32kb + 16(kk/EV) + u*EV + kk%EV, which sits in LDS row
+            // 32kb + row_slot(16(kk/EV) + u*EV + kk%EV).
             // (software-pipelined over the flattened (kb, u, db) steps, two
             // V^T operands ahead)
             __builtin_amdgcn_s_setprio(1);
             {
-                constexpr int NS = KB * PU * DB, PF = PIPE ? 2 : 1;
+                constexpr int NS = KB * PU * DB, PF = 2;
                 auto vfrag = [&](int st) {
                     const int db = st % DB, u = (st / DB) % PU, kb = st / (DB * PU);
-                    return load_frag<TV>(v + LV::off(db * 32 + ln, kb * 32 + hl * 16 + u * EV));
+                    auto rowof = [=](int kk) { return kb * 32 + row_slot(16 * (kk / EV) + u * EV + kk % EV); };
+                    return load_frag_tr<TV, D>(v, db * 32, rowof, lane);
                 };
                 typename MV::frag vf[PF + 1];
 #pragma unroll
@@ -321,25 +327,26 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdArgs a) {
                     if (st + PF < NS) vf[(st + PF) % (PF + 1)] = vfrag(st + PF);
                     const int db = st % DB, u = (st / DB) % PU, kb = st / (DB * PU);
                     if (db == 0) bp = pack_p<TV>(&p[kb][u * EV]);
-                    fence();
+                    __builtin_amdgcn_sched_barrier(0);
                     oacc[db] = MV::mma(vf[st % (PF + 1)], bp, oacc[db]);
-                    fence();
+                    __builtin_amdgcn_sched_barrier(0);
                 }
             }
             __builtin_amdgcn_s_setprio(0);
         };
         if (!(causal && kv0 > qw0 + 31))   // else: no valid key for this wave's rows
             tile_math((kv0 + BC > kend) || (causal && kv0 + BC - 1 > qw0));
-        if (jn >= 0) store_tile(buf ^ 1);   // that buffer was last read before the previous barrier
+        __builtin_amdgcn_s_waitcnt(0);   // this wave's loads into the other buffer have landed
         __syncthreads();
         buf ^= 1;
         jj = jn;
     }
 
-    // ---- epilogue: O = O^T / l, LSE = m + ln l
+    // ---- epilogue: O = 2^e_bh O^T / l, LSE = m + ln l
     const float l_tot = l_run + wave_xor32(l_run);
     float inv = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
     if constexpr (DROP) inv *= a.drop.keep_scale;
+    const int vx = a.vexp ? a.vexp[bhi] : 0;
     if (qrow < N) {
         const size_t orow = hoff + (size_t)qrow * D;
 #pragma unroll
@@ -347,10 +354,11 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdArgs a) {
 #pragma unroll
             for (int g = 0; g < 4; ++g) {
                 const int dcol = db * 32 + 8 * g + 4 * hl;
-                const float v0 = oacc[db][4 * g] * inv, v1 = oacc[db][4 * g + 1] * inv;
-                const float v2 = oacc[db][4 * g + 2] * inv, v3 = oacc[db][4 * g + 3] * inv;
-                if (a.o_f32) store4<float>((float*)a.o + orow + dcol, v0, v1, v2, v3);
-                else store4<T>((T*)a.o + orow + dcol, v0, v1, v2, v3);
+                float w[4];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) w[e] = ldexpf(oacc[db][4 * g + e] * inv, vx);
+                if (a.o_f32) store4<float>((float*)a.o + orow + dcol, w[0], w[1], w[2], w[3]);
+                else store4<T>((T*)a.o + orow + dcol, w[0], w[1], w[2], w[3]);
             }
         if (hl == 0)
             a.lse[bh * N + qrow] = l_tot > 0.0f ? (m_run + log2f(l_tot)) * 0.69314718055994530942f
@@ -382,7 +390,28 @@ hipError_t launch_d(const FwdArgs& a, int d, hipStream_t s) {
 }
 }  // namespace
 
-hipError_t launch_fwd(const FwdArgs& a, fa_dtype dt, int d, hipStream_t s) {
+hipError_t launch_fwd(FwdArgs a, fa_dtype dt, int d, void* workspace, hipStream_t s) {
+    a.vexp = nullptr;
+    if (dt == FA_BF16) {
+        const FwdWorkspace L = fwd_workspace_layout(a.B, a.H, a.N, d);
+        char* ws = static_cast<char*>(workspace);
+        V16Args p;
+        p.v = a.v;
+        p.v16 = reinterpret_cast<f16*>(ws + L.v16);
+        p.part = reinterpret_cast<uint32_t*>(ws + L.part);
+        p.vexp = reinterpret_cast<int32_t*>(ws + L.vexp);
+        p.per_head = (size_t)a.N * d;
+        p.nch = L.nch;
+        p.chunk = L.chunk;
+        void* args[] = {(void*)&p};
+        const dim3 grid((unsigned)((size_t)a.B * a.H * L.nch));
+        hipError_t e = hipLaunchKernel((const void*)&v16_absmax_kernel, grid, dim3(256), args, 0, s);
+        if (e != hipSuccess) return e;
+        e = hipLaunchKernel((const void*)&v16_convert_kernel, grid, dim3(256), args, 0, s);
+        if (e != hipSuccess) return e;
+        a.v = p.v16;
+        a.vexp = p.vexp;
+    }
     switch (dt) {
         case FA_BF16: return launch_d<bf16>(a, d, s);
         case FA_F16: return launch_d<f16>(a, d, s);

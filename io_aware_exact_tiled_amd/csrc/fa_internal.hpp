@@ -56,6 +56,44 @@ struct FwdArgs {
     uint8_t* tile_visits; // null unless recording
     int reverse_kv;
     hipEvent_t ev_begin, ev_end;   // optional profiling events around the kernel
+    const int32_t* vexp;  // bf16: per-(b, h) exponent e, V operand = V * 2^-e in fp16
+};
+
+inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+// Forward workspace (bf16 inputs only): V * 2^-e_bh as fp16 [B][H][N][d],
+// then the per-chunk maxima of |V| and the exponents e_bh.  Each (b, h) is
+// cut into nch chunks of `chunk` elements (a multiple of one 256-thread x
+// 8-element pass) for the pre-pass kernels.
+constexpr int V16_MAX_CHUNKS = 64;
+struct FwdWorkspace {
+    size_t v16, part, vexp, bytes;   // byte offsets, total
+    int nch;
+    size_t chunk;
+};
+inline FwdWorkspace fwd_workspace_layout(int B, int H, int N, int d) {
+    FwdWorkspace w;
+    const size_t bh = (size_t)B * H, per_head = (size_t)N * d;
+    constexpr size_t GRAIN = 256 * 8;
+    const size_t passes = (per_head + GRAIN - 1) / GRAIN;
+    const size_t want = passes < (size_t)V16_MAX_CHUNKS ? passes : (size_t)V16_MAX_CHUNKS;
+    w.chunk = ((passes + want - 1) / want) * GRAIN;
+    w.nch = (int)((per_head + w.chunk - 1) / w.chunk);
+    w.v16 = 0;
+    w.part = align256(bh * per_head * 2);
+    w.vexp = w.part + align256(bh * (size_t)w.nch * 4);
+    w.bytes = w.vexp + align256(bh * 4);
+    return w;
+}
+
+struct V16Args {
+    const void* v;        // bf16 [B][H][N][d]
+    _Float16* v16;        // fp16 [B][H][N][d]
+    uint32_t* part;       // [B*H][nch] largest finite |V| per chunk (bf16 magnitude bits)
+    int32_t* vexp;        // [B*H]
+    size_t per_head;      // N * d
+    int nch;
+    size_t chunk;
 };
 
 struct BwdArgs {
@@ -81,7 +119,7 @@ struct BwdArgs {
     hipEvent_t ev_mid;             // optional: between the two main kernels
 };
 
-hipError_t launch_fwd(const FwdArgs& a, fa_dtype dt, int d, hipStream_t s);
+hipError_t launch_fwd(FwdArgs a, fa_dtype dt, int d, void* workspace, hipStream_t s);
 hipError_t launch_bwd(const BwdArgs& a, fa_dtype dt, int d, hipStream_t s);
 hipError_t launch_keep_mask(uint32_t k0, uint32_t k1, uint32_t off, uint32_t thr,
                             int B, int H, int N, uint8_t* keep, hipStream_t s);

@@ -41,7 +41,7 @@ def test_library_exports_every_declared_symbol():
 
 def test_scalars():
     L = _lib()
-    assert L.fa_abi_version() == 1
+    assert L.fa_abi_version() == 2
     for code in list(lib_mod.STATUS) + [-99]:
         assert isinstance(L.fa_status_string(code), bytes)
     br, bc = ctypes.c_int32(), ctypes.c_int32()
@@ -62,8 +62,8 @@ P = 0x10000  # a 256-byte aligned fake device address: never dereferenced on the
 
 
 def fwd(L, q=P, k=P, v=P, o=P, lse=P, B=1, H=1, N=8, d=64, dt=2, scale=0.125, causal=0, p=0.0, seed=0,
-        mask=None, opts=None):
-    return L.fa_fwd(q, k, v, o, lse, B, H, N, d, dt, scale, causal, p, seed, mask, opts, None)
+        mask=None, opts=None, ws=P, ws_bytes=1 << 20):
+    return L.fa_fwd(q, k, v, o, lse, B, H, N, d, dt, scale, causal, p, seed, mask, opts, ws, ws_bytes, None)
 
 
 def bwd(L, B=1, H=1, N=8, d=64, dt=2, scale=0.125, p=0.0, opts=None, ws=P, ws_bytes=1 << 20, ptrs=None):
@@ -97,6 +97,35 @@ def test_opts_validation():
     assert fwd(L, opts=ctypes.byref(o)) == -1
     o.flags = lib_mod.FA_FLAG_REVERSE_KV
     assert bwd(L, opts=ctypes.byref(o)) == -10      # forward-only flag
+
+
+def align256(x):
+    return (x + 255) // 256 * 256
+
+
+@pytest.mark.parametrize("B,H,N,d", [(1, 2, 256, 64), (1, 1, 3, 64), (2, 3, 1000, 128), (1, 16, 16384, 128)])
+def test_fwd_workspace_bytes(B, H, N, d):
+    """bf16 needs the fp16 copy of V (B*H*N*d halves, rounded to 256 bytes)
+    plus 4-byte per-head statistics (at most 64 chunk maxima and one exponent
+    per head, each part rounded to 256); fp16 and fp32 need none."""
+    L = _lib()
+    n = L.fa_fwd_workspace_bytes(B, H, N, d, 2)
+    v16 = align256(B * H * N * d * 2)
+    assert v16 + 2 * 256 <= n <= v16 + align256(B * H * 64 * 4) + align256(B * H * 4)
+    assert n % 256 == 0
+    assert L.fa_fwd_workspace_bytes(B, H, N, d, 1) == 0
+    assert L.fa_fwd_workspace_bytes(B, H, N, d, 0) == 0
+    assert L.fa_fwd_workspace_bytes(B, H, N, 96, 2) == 0
+    assert L.fa_fwd_workspace_bytes(0, H, N, d, 2) == 0
+    assert L.fa_fwd_workspace_bytes(B, H, N, d, 9) == 0
+
+
+def test_fwd_workspace_validation():
+    L = _lib()
+    need = L.fa_fwd_workspace_bytes(1, 1, 8, 64, 2)
+    assert fwd(L, ws=None) == -8
+    assert fwd(L, ws_bytes=need - 1) == -8
+    assert fwd(L, ws=P + 16) == -8                  # not 256-byte aligned
 
 
 def test_bwd_validation():

@@ -147,6 +147,35 @@ def test_backward_dk_dv_deterministic():
     assert (g1[0].float() - g2[0].float()).abs().max().item() <= 1e-3 * g1[0].float().abs().max().item()
 
 
+@pytest.mark.parametrize("vscale_log2", [0, 60, -60, 100])
+def test_bf16_v_outside_fp16_range(vscale_log2):
+    """bf16 forward: P*V runs in fp16 on a copy of V scaled by a power of two
+    per (b, h).  Heads whose V lies far above fp16's range (2^60, 2^100), far
+    below its normal range (2^-60), spans 2^20 within the head, or is all
+    zero give O equal to the oracle's to the usual bound, relative to the
+    head's own scale."""
+    N = 300
+    x = W.random_case(1, 4, N, 64, dtype="bf16", seed=21, causal=True)
+    s = 2.0 ** vscale_log2
+    v = x["v"].to(torch.float64)
+    v[0, 0] *= s
+    v[0, 1] = 0.0
+    v[0, 2, ::7] *= 2.0 ** 20         # one key in seven is 2^20 times larger
+    v[0, 2] *= s
+    x["v"] = v.to(torch.bfloat16)     # exact: powers of two within bf16's range
+    assert torch.equal(x["v"].to(torch.float64), v)
+    print(f"[case] bf16 V scaled by 2^{vscale_log2}", flush=True)
+    q, k, vv = (cuda(x[n]) for n in ("q", "k", "v"))
+    o, lse = fa.fwd(q, k, vv, causal=True, o_fp32=True)
+    torch.cuda.synchronize()
+    O, L = oracle.attn_fwd(x["q"], x["k"], x["v"], x["scale"], causal=True)
+    check_lse(lse, L, torch.bfloat16)
+    got = f64(o)
+    for h, unit in ((0, s), (2, s * 2.0 ** 20), (3, 1.0)):
+        check_o(torch.from_numpy(got[:, h] / unit), O[:, h] / unit, torch.bfloat16, f"O head {h}")
+    assert (got[:, 1] == 0).all()
+
+
 def test_nan_propagates_without_hang():
     x = W.random_case(1, 1, 300, 64, dtype="bf16", seed=12)
     q = x["q"].clone()
@@ -184,7 +213,7 @@ def test_extra_memory_is_linear_in_n():
     dq, dk, dv = fa.bwd(q, k, v, o, do, lse, causal=True)
     torch.cuda.synchronize()
     peak = torch.cuda.max_memory_allocated() - base
-    # outputs (O, dQ, dK, dV in bf16, LSE) + fp32 dQ workspace + D: all O(N d);
-    # a single N x N bf16 matrix would be 512 MiB
+    # outputs (O, dQ, dK, dV in bf16, LSE) + the forward's fp16 copy of V + D:
+    # all O(N d); a single N x N bf16 matrix would be 512 MiB
     linear = 4 * N * d * 2 + N * 4 + N * d * 4 + N * 4 + (1 << 20)
     assert peak <= linear, (peak, linear)
