@@ -395,7 +395,8 @@ __global__ __launch_bounds__(256, sizeof(T) == 4 ? 1 : 2) void bwd_dq_kernel(Bwd
     __shared__ __attribute__((aligned(16))) T sK[2 * TK];
     __shared__ __attribute__((aligned(16))) T sV[2 * TK];
 
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int hl = lane >> 5, ln = lane & 31;
     const int N = a.N, H = a.H;
     const int Tr = (N + BR - 1) / BR, Tc = (N + BC - 1) / BC;

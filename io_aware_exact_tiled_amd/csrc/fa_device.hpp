@@ -172,37 +172,20 @@ __device__ inline uint32_t keep4(uint32_t g, uint32_t i, uint32_t bh, uint32_t o
 }
 
 // ---------------------------------------------------------------------------
-__device__ inline float wave_xor32(float v) { return __shfl_xor(v, 32, WAVE); }
+// Reductions over the lane pair (l, l ^ 32) with the gfx950 half-swap: the
+// two results of v_permlane32_swap hold, between them, v of lane l and of
+// lane l ^ 32 in every lane (which one is where depends on the half, but
+// max and sum do not care).
+__device__ inline float pair_max(float v) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ inline float pair_sum(float v) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
 
 __device__ inline float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
-
-// Transpose-and-store helper for staging: `x` holds 4 consecutive rows of a
-// tile, each as one 16-byte chunk (EPU elements); column c of that 4 x EPU
-// block (4 elements, rows 0..3) is written to dst(c), a pointer into a
-// transposed LDS tile.  16-bit elements are paired with byte permutes, no
-// float round trip.
-template <class T, class F>
-__device__ inline void store_transposed4(const u32x4 (&x)[4], F dst) {
-    if constexpr (sizeof(T) == 2) {
-#pragma unroll
-        for (int w = 0; w < 4; ++w) {
-            // column 2w: low halves; column 2w+1: high halves
-            const uint32_t lo01 = __builtin_amdgcn_perm(x[1][w], x[0][w], 0x05040100u);
-            const uint32_t lo23 = __builtin_amdgcn_perm(x[3][w], x[2][w], 0x05040100u);
-            const uint32_t hi01 = __builtin_amdgcn_perm(x[1][w], x[0][w], 0x07060302u);
-            const uint32_t hi23 = __builtin_amdgcn_perm(x[3][w], x[2][w], 0x07060302u);
-            u32x2 a = {lo01, lo23}, b = {hi01, hi23};
-            *reinterpret_cast<u32x2*>(dst(2 * w)) = a;
-            *reinterpret_cast<u32x2*>(dst(2 * w + 1)) = b;
-        }
-    } else {
-#pragma unroll
-        for (int w = 0; w < 4; ++w) {
-            u32x4 col = {x[0][w], x[1][w], x[2][w], x[3][w]};
-            *reinterpret_cast<u32x4*>(dst(w)) = col;
-        }
-    }
-}
 
 // MFMA row order within a 32-row block: slot m holds row 16*((m/4)%2) +
 // 4*(m/8) + m%4, so accumulator register r of lane half h is row 16*h + r.
@@ -221,8 +204,10 @@ typedef __attribute__((address_space(1))) void glb_void;
 // global-to-LDS loads.  One such load writes the 64 lanes' 16 bytes to 64
 // consecutive LDS units, so each lane fetches the global chunk that belongs
 // at its unit.  Rows past N read row N-1 (finite data; those rows are masked
-// by the caller).  Issued by all NW waves of the workgroup; completion is
-// awaited with s_waitcnt before the barrier that publishes the tile.
+// by the caller).  Issued by all NW waves of the workgroup (`wave` must be
+// wave-uniform); completion is awaited with s_waitcnt before the barrier that
+// publishes the tile.  The address is a uniform row base plus a 32-bit lane
+// offset, so the loads take the scalar-base form.
 template <class T, int ROWS, int D, int NW = 4>
 __device__ inline void dma_rows(T* tile, const T* head, int row0, int N, int wave, int lane) {
     typedef SwzTr<T, D> L;
@@ -230,16 +215,19 @@ __device__ inline void dma_rows(T* tile, const T* head, int row0, int N, int wav
     constexpr int UPR = D / EPU;
     constexpr int UNITS = ROWS * UPR;
     static_assert(UNITS % (64 * NW) == 0, "tile must be a whole number of workgroup-wide loads");
+    const char* base = reinterpret_cast<const char*>(head + (size_t)row0 * D);
+    const int last = N - 1 - row0;                    // rows r > last repeat row `last`
+    const bool full = row0 + ROWS <= N;
 #pragma unroll
     for (int n = 0; n < UNITS / (64 * NW); ++n) {
         const int blk = n * NW + wave;                // this wave's 64-unit block
         const int P = blk * 64 + lane;                // LDS unit written by this lane
         const int slot = P / UPR, pu = P % UPR;
         const int u = pu ^ L::f(slot);
-        int row = row0 + slot_row(slot);
-        row = row < N ? row : N - 1;
-        const T* src = head + (size_t)row * D + u * EPU;
-        __builtin_amdgcn_global_load_lds((glb_void*)src, (lds_void*)(tile + blk * 64 * EPU), 16, 0, 0);
+        int r = slot_row(slot);
+        if (!full) r = r < last ? r : last;
+        const uint32_t off = (uint32_t)((r * D + u * EPU) * (int)sizeof(T));
+        __builtin_amdgcn_global_load_lds((glb_void*)(base + off), (lds_void*)(tile + blk * 64 * EPU), 16, 0, 0);
     }
 }
 
@@ -250,22 +238,35 @@ __device__ inline void dma_rows(T* tile, const T* head, int row0, int N, int wav
 // group the transpose read hands destination lane j, element e, element j%4
 // of the 8 bytes addressed by source lane j/4 + 4e; so source lane s of group
 // G addresses row k = 8*(G/2) + 4*h + s/4 (h = 0, 1: the two halves of the
-// fragment), columns col0 + 16*(G%2) + 4*(s%4) .. +3.
+// fragment), columns col0 + 16*(G%2) + 4*(s%4) .. +3.  frag_tr_off gives
+// the element offset of half h for this lane.
+template <class T, int D, class RowOf>
+__device__ inline int frag_tr_off(int col0, RowOf rowof, int lane, int h) {
+    typedef SwzTr<T, D> L;
+    const int G = lane >> 4, s = lane & 15;
+    const int col = col0 + 16 * (G & 1) + 4 * (s & 3);
+    const int k = 8 * (G >> 1) + 4 * h + (s >> 2);
+    return L::off(rowof(k), col);
+}
+
+// The two transpose reads of a 16-bit fragment at given addresses (halves
+// h = 0, 1 as frag_tr_off computes them).
+template <class T>
+__device__ inline typename Mma<T>::frag frag_tr_at(const T* p0, const T* p1) {
+    typedef short v4s __attribute__((ext_vector_type(4)));
+    typedef __attribute__((address_space(3))) v4s lds_v4s;
+    union { v4s h[2]; typename Mma<T>::frag f; } u;
+    u.h[0] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s*)p0);
+    u.h[1] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s*)p1);
+    return u.f;
+}
+
 template <class T, int D, class RowOf>
 __device__ inline typename Mma<T>::frag load_frag_tr(const T* tile, int col0, RowOf rowof, int lane) {
     typedef SwzTr<T, D> L;
-    typedef short v4s __attribute__((ext_vector_type(4)));
-    typedef __attribute__((address_space(3))) v4s lds_v4s;
     if constexpr (Mma<T>::E == 8) {
-        const int G = lane >> 4, s = lane & 15;
-        const int col = col0 + 16 * (G & 1) + 4 * (s & 3);
-        union { v4s h[2]; typename Mma<T>::frag f; } u;
-#pragma unroll
-        for (int h = 0; h < 2; ++h) {
-            const int k = 8 * (G >> 1) + 4 * h + (s >> 2);
-            u.h[h] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s*)(tile + L::off(rowof(k), col)));
-        }
-        return u.f;
+        return frag_tr_at<T>(tile + frag_tr_off<T, D>(col0, rowof, lane, 0),
+                             tile + frag_tr_off<T, D>(col0, rowof, lane, 1));
     } else {
         // one element per lane (k-slot lane/32): a plain read
         return tile[L::off(rowof(lane >> 5), col0 + (lane & 31))];

@@ -148,7 +148,8 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdArgs a) {
     __shared__ __attribute__((aligned(16))) T sK[2 * TILE];
     __shared__ __attribute__((aligned(16))) TV sV[2 * TILE];
 
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int hl = lane >> 5, ln = lane & 31;
     const int N = a.N, H = a.H;
     const int Tr = (N + BR - 1) / BR, Tc = (N + BC - 1) / BC;
@@ -201,6 +202,19 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdArgs a) {
         dma_rows<T, BC, D>(sK + buf * TILE, Kg, j * BC, N, wave, lane);
         dma_rows<TV, BC, D>(sV + buf * TILE, Vg, j * BC, N, wave, lane);
     };
+
+    // 16-bit V: element offsets of the transpose reads of column block db at
+    // kb = u = 0.  Step (kb, u) reads 32kb + 16u rows further down, since
+    // row_slot(16a + 8u + b) = 16u + row_slot(16a + b) for b < 8 and the
+    // swizzle depends on a row's low 4 bits only.
+    int vto[DB][2];
+    if constexpr (EV == 8) {
+        auto rowof = [](int kk) { return row_slot(16 * (kk / 8) + kk % 8); };
+#pragma unroll
+        for (int db = 0; db < DB; ++db)
+#pragma unroll
+            for (int h = 0; h < 2; ++h) vto[db][h] = frag_tr_off<TV, D>(db * 32, rowof, lane, h);
+    }
 
     float m_run = -INFINITY, l_run = 0.0f;
     f32x16 oacc[DB];
@@ -271,7 +285,7 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdArgs a) {
             for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
                 for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
-            mx = fmaxf(mx, wave_xor32(mx)) * c;
+            mx = pair_max(mx) * c;
             if (__builtin_expect(__any(mx > m_run + RESCALE), 0)) {
                 const float m_new = fmaxf(m_run, mx);
                 const float alpha = (m_new == -INFINITY) ? 1.0f : fast_exp2(m_run - m_new);
@@ -315,8 +329,13 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdArgs a) {
                 constexpr int NS = KB * PU * DB, PF = 2;
                 auto vfrag = [&](int st) {
                     const int db = st % DB, u = (st / DB) % PU, kb = st / (DB * PU);
-                    auto rowof = [=](int kk) { return kb * 32 + row_slot(16 * (kk / EV) + u * EV + kk % EV); };
-                    return load_frag_tr<TV, D>(v, db * 32, rowof, lane);
+                    if constexpr (EV == 8) {
+                        const TV* vs = v + (kb * 32 + u * 16) * D;
+                        return frag_tr_at<TV>(vs + vto[db][0], vs + vto[db][1]);
+                    } else {
+                        auto rowof = [=](int kk) { return kb * 32 + row_slot(16 * kk + u); };
+                        return load_frag_tr<TV, D>(v, db * 32, rowof, lane);
+                    }
                 };
                 typename MV::frag vf[PF + 1];
 #pragma unroll
@@ -343,7 +362,7 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdArgs a) {
     }
 
     // ---- epilogue: O = 2^e_bh O^T / l, LSE = m + ln l
-    const float l_tot = l_run + wave_xor32(l_run);
+    const float l_tot = pair_sum(l_run);
     float inv = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
     if constexpr (DROP) inv *= a.drop.keep_scale;
     const int vx = a.vexp ? a.vexp[bhi] : 0;
