@@ -36,6 +36,8 @@
 // same Q and dO tiles read transposed).  bwd_dq is the forward kernel's
 // layout: keys on the rows (K, V in MFMA row order), one query per lane, and
 // the K tile read transposed for dQ^T += K^T dS^T.
+#include <type_traits>
+
 #include "fa_device.hpp"
 #include "fa_internal.hpp"
 
@@ -128,9 +130,15 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(BwdArgs a) {
 //   B (w >= 4): holds V_j; dP = dO V^T, then with P from its partner
 //               dS = P o (dP o Z/(1-p) - D), dK_j += dS^T Q.
 // Each wave keeps one operand block and one accumulator block, so two waves
-// fit on a SIMD and one's exponentials overlap the other's MFMAs.  A and B
-// hold the same (key, query) elements in the same lane and register, so the
-// hand-off is a plain per-lane copy.
+// fit on a SIMD.  A and B hold the same (key, query) elements in the same
+// lane and register, so the hand-off is a plain per-lane copy.
+//
+// B runs one query tile behind A so that the SIMD always has MFMA work:
+// per step n (barriers marked |)
+//   A:  S(n) MFMA     P(n) exp, hand-off      |  dV += P(n)^T dO(n) MFMA      |
+//   B:  dP(n) MFMA    dK += dS(n-1)^T Q(n-1)  |  dS(n) from P(n), in regs    |
+// so B's dK product overlaps A's exponentials and A's dV product overlaps
+// B's dS arithmetic.  Q tiles stay in LDS one step longer (three buffers).
 template <class T, int D, bool DROP>
 __global__ __launch_bounds__(512, 1) void bwd_kv_kernel(BwdArgs a) {
     typedef Mma<T> MM;
@@ -146,7 +154,7 @@ __global__ __launch_bounds__(512, 1) void bwd_kv_kernel(BwdArgs a) {
     constexpr int NX = DROP ? 2 : 1;              // hand-off planes: P (and P o Z / (1-p))
     typedef SwzTr<T, D> LQ;    // Q, dO: BR rows (MFMA row order) x D
 
-    __shared__ __attribute__((aligned(16))) T sQ[2 * TQ];
+    __shared__ __attribute__((aligned(16))) T sQ[3 * TQ];
     __shared__ __attribute__((aligned(16))) T sdO[2 * TQ];
     __shared__ __attribute__((aligned(16))) float sLse[2 * BR];
     __shared__ __attribute__((aligned(16))) float sDel[2 * BR];
@@ -206,42 +214,65 @@ __global__ __launch_bounds__(512, 1) void bwd_kv_kernel(BwdArgs a) {
 
     // ---- staging of one query tile: Q, dO by global->LDS DMA; LSE, D via registers
     float lreg = 0.0f;
-    auto load_tile = [&](int i, int buf) {
+    auto load_tile = [&](int i, int qbuf, int obuf) {
         const int q0 = i * BR;
-        dma_rows<T, BR, D, NW>(sQ + buf * TQ, Qg, q0, N, wave, lane);
-        dma_rows<T, BR, D, NW>(sdO + buf * TQ, dOg, q0, N, wave, lane);
+        dma_rows<T, BR, D, NW>(sQ + qbuf * TQ, Qg, q0, N, wave, lane);
+        dma_rows<T, BR, D, NW>(sdO + obuf * TQ, dOg, q0, N, wave, lane);
         if (tid < 2 * BR) {
             const int q = q0 + (tid % BR);
             lreg = (q < N) ? (tid < BR ? lseg[q] : delg[q]) : (tid < BR ? INFINITY : 0.0f);
         }
     };
-    auto publish_stats = [&](int buf) {
-        if (tid < BR) sLse[buf * BR + tid] = lreg * 1.4426950408889634f;
-        else if (tid < 2 * BR) sDel[buf * BR + tid - BR] = lreg;
+    auto publish_stats = [&](int obuf) {
+        if (tid < BR) sLse[obuf * BR + tid] = lreg * 1.4426950408889634f;
+        else if (tid < 2 * BR) sDel[obuf * BR + tid - BR] = lreg;
     };
     auto xslot = [&](int plane, int qb, int chunk) -> f32x4* {
         return &sX[(((kb * NX + plane) * QB + qb) * 4 + chunk) * 64 + lane];
     };
+    // B: dK_j += dS^T Q over one query tile; dS as packed A operands (query
+    // block qb, 16-query step u), Q read transposed from its LDS buffer
+    typename MM::frag dsf[QB][QU];
+    auto dk_product = [&](const T* q) __attribute__((always_inline)) {
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb)
+#pragma unroll
+            for (int u = 0; u < QU; ++u) {
+                auto rowof = [&](int kk) { return row_slot(qb * 32 + (kk / E) * 16 + u * E + kk % E); };
+#pragma unroll
+                for (int db = 0; db < DB; ++db)
+                    acc[db] = MM::mma(dsf[qb][u], load_frag_tr<T, D>(q, db * 32, rowof, lane), acc[db]);
+            }
+    };
 
     const float c = a.scale_log2;
+    // One loop per role (the role is fixed per wave), so that each is
+    // register-allocated on its own; both pass the same barriers.
+    auto run = [&](auto role) __attribute__((always_inline)) {
+    constexpr bool RA = decltype(role)::value;
     int i = tile_at(i_begin);
     if (i >= 0) {
-        load_tile(i, 0);
+        load_tile(i, 0, 0);
         publish_stats(0);
     }
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
-    int buf = 0;
+    int qbuf = 0, obuf = 0, qprev = 0;
+    bool have_prev = false;              // B holds dS of the previous step in dsf
     while (i >= 0) {
         const int q0 = i * BR;
         if (vis && tid == 0) vis[(size_t)i * Tc] = 1;
         const int in = tile_at(i + 1);
-        if (in >= 0) load_tile(in, buf ^ 1);   // lands in the other buffer during this step
+        const int qnext = qbuf == 2 ? 0 : qbuf + 1;
+        // lands in the other buffers during this step; the Q buffer last held
+        // step n-2 (read by B before the previous step's first barrier), the
+        // dO buffer step n-1 (read before the previous step's second barrier)
+        if (in >= 0) load_tile(in, qnext, obuf ^ 1);
 
-        const T* q = sQ + buf * TQ;
-        const T* o = sdO + buf * TQ;
-        const float* ls = sLse + buf * BR;
-        const float* dl = sDel + buf * BR;
+        const T* q = sQ + qbuf * TQ;
+        const T* o = sdO + obuf * TQ;
+        const float* ls = sLse + obuf * BR;
+        const float* dl = sDel + obuf * BR;
         // first product: S = Q K^T (A) or dP_hat = dO V^T (B); lane holds key krow,
         // queries q0 + 32qb + 16hl + r
         // (software-pipelined: the operands of step ks+1 are read before the
@@ -249,7 +280,7 @@ __global__ __launch_bounds__(512, 1) void bwd_kv_kernel(BwdArgs a) {
         f32x16 sp[QB];
         __builtin_amdgcn_s_setprio(1);
         {
-            const T* src = roleA ? q : o;
+            const T* src = RA ? q : o;
             typename MM::frag fa[2][QB];
 #pragma unroll
             for (int qb = 0; qb < QB; ++qb) {
@@ -271,8 +302,8 @@ __global__ __launch_bounds__(512, 1) void bwd_kv_kernel(BwdArgs a) {
         }
         __builtin_amdgcn_s_setprio(0);
 
-        if (roleA) {
-            // P = exp(S - LSE) with the masks, handed to B; then dV_j += Pd^T dO
+        if constexpr (RA) {
+            // P = exp(S - LSE) with the masks, handed to B (kept for dV)
             const bool edge = (causal && kw0 + 31 > q0) || (kw0 + 32 > kend) || (q0 + BR > N);
 #pragma unroll
             for (int qb = 0; qb < QB; ++qb) {
@@ -309,14 +340,19 @@ __global__ __launch_bounds__(512, 1) void bwd_kv_kernel(BwdArgs a) {
                         *xslot(1, qb, g) = v4;
                     }
                 }
-                sp[qb] = zero16();   // reuse as nothing; keeps the register set small
 #pragma unroll
                 for (int r = 0; r < 16; ++r) sp[qb][r] = p[r];
             }
+        } else if (have_prev) {
+            // the previous step's dK product, while A computes P
+            __builtin_amdgcn_s_setprio(1);
+            dk_product(sQ + qprev * TQ);
+            __builtin_amdgcn_s_setprio(0);
         }
         __syncthreads();   // P handed over
-        __builtin_amdgcn_s_setprio(1);
-        if (roleA) {
+        if constexpr (RA) {
+            // dV_j += Pd^T dO
+            __builtin_amdgcn_s_setprio(1);
 #pragma unroll
             for (int qb = 0; qb < QB; ++qb)
 #pragma unroll
@@ -330,7 +366,9 @@ __global__ __launch_bounds__(512, 1) void bwd_kv_kernel(BwdArgs a) {
                     for (int db = 0; db < DB; ++db)
                         acc[db] = MM::mma(ap, load_frag_tr<T, D>(o, db * 32, rowof, lane), acc[db]);
                 }
+            __builtin_amdgcn_s_setprio(0);
         } else {
+            // dS = P o (dP - D), kept as packed operands for the next step
 #pragma unroll
             for (int qb = 0; qb < QB; ++qb) {
                 const int qr0 = qb * 32 + hl * 16;
@@ -350,22 +388,25 @@ __global__ __launch_bounds__(512, 1) void bwd_kv_kernel(BwdArgs a) {
                     }
                 }
 #pragma unroll
-                for (int u = 0; u < QU; ++u) {
-                    const typename MM::frag as = pack_f<T>(&ds[u * E]);
-                    auto rowof = [&](int kk) { return row_slot(qb * 32 + (kk / E) * 16 + u * E + kk % E); };
-#pragma unroll
-                    for (int db = 0; db < DB; ++db)
-                        acc[db] = MM::mma(as, load_frag_tr<T, D>(q, db * 32, rowof, lane), acc[db]);
-                }
+                for (int u = 0; u < QU; ++u) dsf[qb][u] = pack_f<T>(&ds[u * E]);
             }
+            have_prev = true;
         }
-        __builtin_amdgcn_s_setprio(0);
-        if (in >= 0) publish_stats(buf ^ 1);
-        __builtin_amdgcn_s_waitcnt(0);   // this wave's DMA into the other buffer has landed
+        if (in >= 0) publish_stats(obuf ^ 1);
+        __builtin_amdgcn_s_waitcnt(0);   // this wave's DMA into the other buffers has landed
         __syncthreads();                 // also: the hand-off buffer may be overwritten
-        buf ^= 1;
+        qprev = qbuf;
+        qbuf = qnext;
+        obuf ^= 1;
         i = in;
     }
+    // B: the last step's dK product (its Q tile is still in place: no DMA follows)
+    if constexpr (!RA) {
+        if (have_prev) dk_product(sQ + qprev * TQ);
+    }
+    };
+    if (roleA) run(std::true_type{});
+    else run(std::false_type{});
 
     // ---- dV_j = acc (A), dK_j = scale * acc (B); lane holds column db*32+ln, rows = keys
     T* dst = (T*)(roleA ? a.dv : a.dk) + hoff;
