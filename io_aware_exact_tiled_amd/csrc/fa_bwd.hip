@@ -232,17 +232,10 @@ __global__ __launch_bounds__(512, 1) void bwd_kv_kernel(BwdArgs a) {
     };
     // B: dK_j += dS^T Q over one query tile; dS as packed A operands (query
     // block qb, 16-query step u), Q read transposed from its LDS buffer
+    const TrOffsets<T, D> tro(lane);
     typename MM::frag dsf[QB][QU];
     auto dk_product = [&](const T* q) __attribute__((always_inline)) {
-#pragma unroll
-        for (int qb = 0; qb < QB; ++qb)
-#pragma unroll
-            for (int u = 0; u < QU; ++u) {
-                auto rowof = [&](int kk) { return row_slot(qb * 32 + (kk / E) * 16 + u * E + kk % E); };
-#pragma unroll
-                for (int db = 0; db < DB; ++db)
-                    acc[db] = MM::mma(dsf[qb][u], load_frag_tr<T, D>(q, db * 32, rowof, lane), acc[db]);
-            }
+        tr_chain<T, D, QB, false, 2>(acc, q, tro, [&](int qb, int u) { return dsf[qb][u]; }, lane);
     };
 
     const float c = a.scale_log2;
@@ -353,19 +346,12 @@ __global__ __launch_bounds__(512, 1) void bwd_kv_kernel(BwdArgs a) {
         if constexpr (RA) {
             // dV_j += Pd^T dO
             __builtin_amdgcn_s_setprio(1);
+            tr_chain<T, D, QB, false, 2>(acc, o, tro, [&](int qb, int u) {
+                float pr[E];
 #pragma unroll
-            for (int qb = 0; qb < QB; ++qb)
-#pragma unroll
-                for (int u = 0; u < QU; ++u) {
-                    float pr[E];
-#pragma unroll
-                    for (int e = 0; e < E; ++e) pr[e] = sp[qb][u * E + e];
-                    const typename MM::frag ap = pack_f<T>(pr);
-                    auto rowof = [&](int kk) { return row_slot(qb * 32 + (kk / E) * 16 + u * E + kk % E); };
-#pragma unroll
-                    for (int db = 0; db < DB; ++db)
-                        acc[db] = MM::mma(ap, load_frag_tr<T, D>(o, db * 32, rowof, lane), acc[db]);
-                }
+                for (int e = 0; e < E; ++e) pr[e] = sp[qb][u * E + e];
+                return pack_f<T>(pr);
+            }, lane);
             __builtin_amdgcn_s_setprio(0);
         } else {
             // dS = P o (dP - D), kept as packed operands for the next step
@@ -484,6 +470,7 @@ __global__ __launch_bounds__(256, sizeof(T) == 4 ? 1 : 2) void bwd_dq_kernel(Bwd
     f32x16 dq[DB];
 #pragma unroll
     for (int db = 0; db < DB; ++db) dq[db] = zero16();
+    const TrOffsets<T, D> tro(lane);   // transpose reads of K_j^T
 
     auto load_tile = [&](int j, int buf) {
         dma_rows<T, BC, D>(sK + buf * TK, Kg, j * BC, N, wave, lane);
@@ -559,22 +546,8 @@ __global__ __launch_bounds__(256, sizeof(T) == 4 ? 1 : 2) void bwd_dq_kernel(Bwd
                 typename MM::frag bs[PU];
 #pragma unroll
                 for (int u = 0; u < PU; ++u) bs[u] = pack_f<T>(&ds[u * E]);
-                auto rowof_u = [&](int u) {
-                    return [=](int kk) { return row_slot((kk / E) * 16 + u * E + kk % E); };
-                };
-                constexpr int NI = PU * DB;
                 __builtin_amdgcn_s_setprio(1);
-                typename MM::frag akt[2];
-                akt[0] = load_frag_tr<T, D>(k, 0, rowof_u(0), lane);
-#pragma unroll
-                for (int it2 = 0; it2 < NI; ++it2) {
-                    const int u = it2 / DB, db = it2 % DB;
-                    if (it2 + 1 < NI)
-                        akt[(it2 + 1) & 1] = load_frag_tr<T, D>(k, ((it2 + 1) % DB) * 32, rowof_u((it2 + 1) / DB), lane);
-                    __builtin_amdgcn_sched_barrier(0);
-                    dq[db] = MM::mma(akt[it2 & 1], bs[u], dq[db]);
-                    __builtin_amdgcn_sched_barrier(0);
-                }
+                tr_chain<T, D, 1, true, 2>(dq, k, tro, [&](int, int u) { return bs[u]; }, lane);
                 __builtin_amdgcn_s_setprio(0);
             }
         }

@@ -273,6 +273,63 @@ __device__ inline typename Mma<T>::frag load_frag_tr(const T* tile, int col0, Ro
     }
 }
 
+// Chains of MFMAs acc[db] += R(s) x X(s, db) (or X x R) whose one operand
+// is read from a natural 16-row-group tile with the transpose read and whose
+// other operand R(s) is in registers.  Step s = (blk, u) covers 16 k-slots:
+// k-slot kk is tile row 32*blk + row_slot(16*(kk/E) + u*E + kk%E), i.e. 16
+// consecutive keys (or queries) of the register operand's lane half.  For
+// 16-bit tiles row_slot(16a + 8u + b) = 16u + row_slot(16a + b) (b < 8) and
+// the swizzle depends on a row's low 4 bits only, so the lane's read
+// addresses are per-lane offsets fixed for the kernel plus a constant per
+// step: TrOffsets holds the former.
+template <class T, int D>
+struct TrOffsets {
+    int v[D / 32][2];
+    __device__ explicit TrOffsets(int lane) {
+        if constexpr (Mma<T>::E == 8) {
+            auto rowof = [](int kk) { return row_slot(16 * (kk / 8) + kk % 8); };
+#pragma unroll
+            for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+                for (int h = 0; h < 2; ++h) v[db][h] = frag_tr_off<T, D>(db * 32, rowof, lane, h);
+        }
+    }
+};
+
+// Steps run over (blk < NBLK, u < 16/E, db < D/32) with db fastest; the
+// transposed operands are read PF steps ahead of their MFMA.  reg(blk, u)
+// gives the register operand; TR_A puts the transposed operand first.
+template <class T, int D, int NBLK, bool TR_A, int PF, class Reg>
+__device__ inline void tr_chain(f32x16 (&acc)[D / 32], const T* tile, const TrOffsets<T, D>& to, Reg reg,
+                                int lane) {
+    typedef Mma<T> MM;
+    constexpr int E = MM::E, QU = 16 / E, DB = D / 32, NS = NBLK * QU * DB;
+    auto xfrag = [&](int st) {
+        const int db = st % DB, u = (st / DB) % QU, blk = st / (DB * QU);
+        if constexpr (E == 8) {
+            const T* p = tile + (blk * 32 + u * 16) * D;
+            return frag_tr_at<T>(p + to.v[db][0], p + to.v[db][1]);
+        } else {
+            auto rowof = [=](int kk) { return blk * 32 + row_slot(16 * kk + u); };
+            return load_frag_tr<T, D>(tile, db * 32, rowof, lane);
+        }
+    };
+    typename MM::frag xf[PF + 1];
+#pragma unroll
+    for (int st = 0; st < PF; ++st) xf[st] = xfrag(st);
+    typename MM::frag r;
+#pragma unroll
+    for (int st = 0; st < NS; ++st) {
+        if (st + PF < NS) xf[(st + PF) % (PF + 1)] = xfrag(st + PF);
+        const int db = st % DB, u = (st / DB) % QU, blk = st / (DB * QU);
+        if (db == 0) r = reg(blk, u);
+        __builtin_amdgcn_sched_barrier(0);
+        if constexpr (TR_A) acc[db] = MM::mma(xf[st % (PF + 1)], r, acc[db]);
+        else acc[db] = MM::mma(r, xf[st % (PF + 1)], acc[db]);
+        __builtin_amdgcn_sched_barrier(0);
+    }
+}
+
 // Map a linear workgroup id to a work item so that each of the 8 XCDs (which
 // receive workgroups round-robin and have their own L2) works on a contiguous
 // range of items.  `per` = ceil(total / 8); the grid has 8 * per workgroups

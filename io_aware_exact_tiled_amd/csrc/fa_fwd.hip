@@ -130,7 +130,7 @@ __global__ __launch_bounds__(256) void v16_convert_kernel(V16Args a) {
 
 // ---------------------------------------------------------------------------
 template <class T, int D, bool DROP>
-__global__ __launch_bounds__(256, 2) void fwd_kernel(FwdArgs a) {
+__global__ __launch_bounds__(256, sizeof(T) == 4 ? 1 : 2) void fwd_kernel(FwdArgs a) {
     typedef typename PvType<T>::type TV;
     typedef Mma<T> MS;
     typedef Mma<TV> MV;
@@ -140,7 +140,6 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdArgs a) {
     constexpr int KS = D / (2 * E);     // MFMA steps over d in S^T
     constexpr int KB = BC / 32;         // 32-key blocks per tile
     constexpr int DB = D / 32;          // 32-wide column blocks of O
-    constexpr int PU = 16 / EV;         // P*V MFMAs per 32-key block
     constexpr int TILE = BC * D;        // elements of one K (or V) buffer
     constexpr float RESCALE = 8.0f;     // log2 headroom before the running max moves
     typedef SwzTr<T, D> LK;
@@ -203,18 +202,7 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdArgs a) {
         dma_rows<TV, BC, D>(sV + buf * TILE, Vg, j * BC, N, wave, lane);
     };
 
-    // 16-bit V: element offsets of the transpose reads of column block db at
-    // kb = u = 0.  Step (kb, u) reads 32kb + 16u rows further down, since
-    // row_slot(16a + 8u + b) = 16u + row_slot(16a + b) for b < 8 and the
-    // swizzle depends on a row's low 4 bits only.
-    int vto[DB][2];
-    if constexpr (EV == 8) {
-        auto rowof = [](int kk) { return row_slot(16 * (kk / 8) + kk % 8); };
-#pragma unroll
-        for (int db = 0; db < DB; ++db)
-#pragma unroll
-            for (int h = 0; h < 2; ++h) vto[db][h] = frag_tr_off<TV, D>(db * 32, rowof, lane, h);
-    }
+    const TrOffsets<TV, D> vto(lane);   // transpose reads of V_j^T
 
     float m_run = -INFINITY, l_run = 0.0f;
     f32x16 oacc[DB];
@@ -319,38 +307,11 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdArgs a) {
                             if (!((bits >> e) & 1u)) p[kb][g * 4 + e] = 0.0f;
                     }
             }
-            // ---- O^T += V_j^T P^T.  k-slot kk of step (kb, u) is key
-            // 32kb + 16(kk/EV) + u*EV + kk%EV, which sits in LDS row
-            // 32kb + row_slot(16(kk/EV) + u*EV + kk%EV).
-            // (software-pipelined over the flattened (kb, u, db) steps, two
-            // V^T operands ahead)
+            // ---- O^T += V_j^T P^T: k-slot kk of step (kb, u) is key
+            // 32kb + 16(kk/EV) + u*EV + kk%EV, the lane half's own keys
             __builtin_amdgcn_s_setprio(1);
-            {
-                constexpr int NS = KB * PU * DB, PF = 2;
-                auto vfrag = [&](int st) {
-                    const int db = st % DB, u = (st / DB) % PU, kb = st / (DB * PU);
-                    if constexpr (EV == 8) {
-                        const TV* vs = v + (kb * 32 + u * 16) * D;
-                        return frag_tr_at<TV>(vs + vto[db][0], vs + vto[db][1]);
-                    } else {
-                        auto rowof = [=](int kk) { return kb * 32 + row_slot(16 * kk + u); };
-                        return load_frag_tr<TV, D>(v, db * 32, rowof, lane);
-                    }
-                };
-                typename MV::frag vf[PF + 1];
-#pragma unroll
-                for (int st = 0; st < PF; ++st) vf[st] = vfrag(st);
-                typename MV::frag bp;
-#pragma unroll
-                for (int st = 0; st < NS; ++st) {
-                    if (st + PF < NS) vf[(st + PF) % (PF + 1)] = vfrag(st + PF);
-                    const int db = st % DB, u = (st / DB) % PU, kb = st / (DB * PU);
-                    if (db == 0) bp = pack_p<TV>(&p[kb][u * EV]);
-                    __builtin_amdgcn_sched_barrier(0);
-                    oacc[db] = MV::mma(vf[st % (PF + 1)], bp, oacc[db]);
-                    __builtin_amdgcn_sched_barrier(0);
-                }
-            }
+            tr_chain<TV, D, KB, true, 2>(oacc, v, vto, [&](int kb, int u) { return pack_p<TV>(&p[kb][u * EV]); },
+                                         lane);
             __builtin_amdgcn_s_setprio(0);
         };
         if (!(causal && kv0 > qw0 + 31))   // else: no valid key for this wave's rows
