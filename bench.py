@@ -3,9 +3,10 @@
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload long]
 
-A step is one full pass of the hot path on one batch: the forward kernel
-(O, LSE) followed by the backward (D pre-pass, the S/P-recomputing kernel,
-dQ conversion), on inputs already resident in device memory.  The default
+A step is one full pass of the hot path on one batch: the forward (for bf16
+the V pre-pass, then the forward kernel: O, LSE) followed by the backward
+(D pre-pass, the dK/dV kernel, the dQ kernel), on inputs already resident
+in device memory.  The default
 workload is the long-context causal case (B=1, H=16, N=16384, d=128, bf16),
 the d=128, N>=4K configuration the fraction-of-peak target is stated for.
 
@@ -14,8 +15,13 @@ Algorithmic work counts valid (query, key) pairs only: the forward does
 dV, dK, dQ).  Peak: MI355X dense bf16/fp16 MFMA, 2.5 PFLOP/s.
 
 Prints one JSON line (rank 0).  Timing uses HIP events on the stream the
-kernels run on; the backward's main kernel is bracketed by events the
-library records around that one launch.
+kernels run on; the forward kernel and the backward's two main kernels are
+bracketed by events the library records around those launches.
+
+roofline.traffic is the dominant kernel's HBM traffic per launch in bytes
+(FETCH_SIZE + WRITE_SIZE counters, scaled by a plain copy of known size),
+read from the counter summary under profiles/ when that summary was taken
+on this workload from the kernel's current sources (else null).
 """
 
 from __future__ import annotations
@@ -31,6 +37,35 @@ import numpy as np
 
 PEAK_TFLOPS = {"bf16": 2500.0, "fp16": 2500.0, "fp32": 157.3}
 HBM_GBPS = 8000.0
+ROOT = os.path.dirname(os.path.abspath(__file__))
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.json")
+CSRC = os.path.join(ROOT, "io_aware_exact_tiled_amd", "csrc")
+KERNEL_SOURCES = {"fwd_kernel": "fa_fwd.hip", "bwd_kv_kernel": "fa_bwd.hip", "bwd_dq_kernel": "fa_bwd.hip"}
+
+
+def kernel_sources_sha256(kernel: str) -> str:
+    """SHA-256 over the sources a kernel is compiled from (its file, then the
+    two shared headers)."""
+    import hashlib
+    h = hashlib.sha256()
+    for f in (KERNEL_SOURCES[kernel], "fa_device.hpp", "fa_internal.hpp"):
+        with open(os.path.join(CSRC, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def measured_traffic(kernel: str, workload: str):
+    """HBM bytes per launch from the committed counter summary, or None when
+    it is missing, was taken on another workload, or predates the kernel's
+    current sources."""
+    try:
+        with open(TRAFFIC_FILE) as fh:
+            e = json.load(fh)["kernels"][kernel]
+    except (OSError, KeyError, ValueError):
+        return None
+    if e.get("workload") != workload or e.get("sources_sha256") != kernel_sources_sha256(kernel):
+        return None
+    return int(e["fetch_bytes"] + e["write_bytes"])
 
 
 def parse():
@@ -40,7 +75,7 @@ def parse():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="long")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-rows", type=int, default=3072,
+    ap.add_argument("--cpu-rows", type=int, default=6144,
                     help="leading causal rows per head the oracle baseline computes")
     ap.add_argument("--sweep", action="store_true", help="also time the N sweep (extra JSON lines)")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
@@ -252,7 +287,8 @@ def main():
         "bwd_main_ms": round(bwd_ms, 4),
         "bwd_kv_ms": round(med(r["kv_ms"]), 4), "bwd_dq_ms": round(med(r["dq_ms"]), 4),
         "roofline": {"bound": "mfma", "kernel": dom, "achieved": round(achieved, 2), "peak": peak,
-                     "unit": "TFLOP/s", "frac": round(achieved / peak, 4), "traffic": None,
+                     "unit": "TFLOP/s", "frac": round(achieved / peak, 4),
+                     "traffic": measured_traffic(dom, w.name),
                      "avg_launch_ms": round(dom_ms, 4), "flop_per_launch": dom_flop},
         "wall_s": round(r["wall_s"], 3),
     }
