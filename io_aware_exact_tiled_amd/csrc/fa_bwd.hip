@@ -321,12 +321,10 @@ __global__ __launch_bounds__(512, 1) void bwd_kv_kernel(BwdArgs a) {
                     *xslot(0, qb, g) = v4;
                 }
                 if constexpr (DROP) {
+                    const uint32_t keep = keep16_quad((uint32_t)krow, (uint32_t)(q0 + qr0), (uint32_t)bh, a.drop.off,
+                                                      a.drop.k0, a.drop.k1, a.drop.thr, lane);
 #pragma unroll
-                    for (int r = 0; r < 16; ++r) {
-                        const uint32_t bits = keep4((uint32_t)krow >> 2, (uint32_t)(q0 + qr0 + r), (uint32_t)bh,
-                                                    a.drop.off, a.drop.k0, a.drop.k1, a.drop.thr);
-                        p[r] *= ((bits >> (krow & 3)) & 1u) ? a.drop.keep_scale : 0.0f;
-                    }
+                    for (int r = 0; r < 16; ++r) p[r] *= ((keep >> r) & 1u) ? a.drop.keep_scale : 0.0f;
 #pragma unroll
                     for (int g = 0; g < 4; ++g) {
                         const f32x4 v4 = {p[4 * g], p[4 * g + 1], p[4 * g + 2], p[4 * g + 3]};

@@ -171,6 +171,31 @@ __device__ inline uint32_t keep4(uint32_t g, uint32_t i, uint32_t bh, uint32_t o
            ((uint32_t)(r.z >= thr) << 2) | ((uint32_t)(r.w >= thr) << 3);
 }
 
+// Keep bits of this lane's key for 16 consecutive queries i0 .. i0+15 (bit r
+// = query i0 + r), where the 4 lanes of each quad hold the 4 keys of one
+// Philox group (lane % 4 == key % 4).  One generator call covers 4 keys, so
+// lane t of the quad runs the calls of queries i0 + t + 4m (m = 0..3) and the
+// quad shares those 16-bit results with DPP quad broadcasts: 4 calls per
+// lane instead of 16.  All 4 lanes of every quad must be active.
+template <int TP> __device__ inline uint32_t quad_bcast(uint32_t w) {
+    return (uint32_t)__builtin_amdgcn_mov_dpp((int)w, TP * 0x55, 0xF, 0xF, false);   // quad_perm [TP,TP,TP,TP]
+}
+__device__ inline uint32_t keep16_quad(uint32_t key, uint32_t i0, uint32_t bh, uint32_t off, uint32_t k0,
+                                       uint32_t k1, uint32_t thr, int lane) {
+    const uint32_t t = (uint32_t)lane & 3u;
+    uint32_t w = 0;
+#pragma unroll
+    for (int m = 0; m < 4; ++m) w |= keep4(key >> 2, i0 + t + 4 * m, bh, off, k0, k1, thr) << (4 * m);
+    const uint32_t W[4] = {quad_bcast<0>(w), quad_bcast<1>(w), quad_bcast<2>(w), quad_bcast<3>(w)};
+    const uint32_t ks = key & 3u;
+    uint32_t out = 0;
+#pragma unroll
+    for (int tp = 0; tp < 4; ++tp)
+#pragma unroll
+        for (int m = 0; m < 4; ++m) out |= ((W[tp] >> (4 * m + ks)) & 1u) << (4 * m + tp);
+    return out;
+}
+
 // ---------------------------------------------------------------------------
 // Reductions over the lane pair (l, l ^ 32) with the gfx950 half-swap: the
 // two results of v_permlane32_swap hold, between them, v of lane l and of
