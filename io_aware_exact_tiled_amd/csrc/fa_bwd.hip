@@ -267,31 +267,16 @@ __global__ __launch_bounds__(512, 1) void bwd_kv_kernel(BwdArgs a) {
         const float* ls = sLse + obuf * BR;
         const float* dl = sDel + obuf * BR;
         // first product: S = Q K^T (A) or dP_hat = dO V^T (B); lane holds key krow,
-        // queries q0 + 32qb + 16hl + r
-        // (software-pipelined: the operands of step ks+1 are read before the
-        // MFMAs of step ks are issued)
+        // queries q0 + 32qb + 16hl + r (operands read ahead)
         f32x16 sp[QB];
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb) sp[qb] = zero16();
         __builtin_amdgcn_s_setprio(1);
         {
             const T* src = RA ? q : o;
-            typename MM::frag fa[2][QB];
-#pragma unroll
-            for (int qb = 0; qb < QB; ++qb) {
-                sp[qb] = zero16();
-                fa[0][qb] = load_frag<T>(src + LQ::off(qb * 32 + ln, hl * E));
-            }
-#pragma unroll
-            for (int ks = 0; ks < KS; ++ks) {
-                if (ks + 1 < KS) {
-#pragma unroll
-                    for (int qb = 0; qb < QB; ++qb)
-                        fa[(ks + 1) & 1][qb] = load_frag<T>(src + LQ::off(qb * 32 + ln, (ks + 1) * 2 * E + hl * E));
-                }
-                __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-                for (int qb = 0; qb < QB; ++qb) sp[qb] = MM::mma(fa[ks & 1][qb], kvf[ks], sp[qb]);
-                __builtin_amdgcn_sched_barrier(0);
-            }
+            lds_chain<T, QB, KS, BWD_PF>(
+                sp, [&](int qb, int ks) { return load_frag<T>(src + LQ::off(qb * 32 + ln, ks * 2 * E + hl * E)); },
+                [&](int, int ks) { return kvf[ks]; });
         }
         __builtin_amdgcn_s_setprio(0);
 
@@ -491,26 +476,14 @@ __global__ __launch_bounds__(256, sizeof(T) == 4 ? 1 : 2) void bwd_dq_kernel(Bwd
             const T* k = sK + buf * TK;
             const T* v = sV + buf * TK;
             // S^T = K Q^T, dP_hat^T = V dO^T: lane holds query qrow, keys kv0 + 16hl + r
-            // (operands of step ks+1 read before the MFMAs of step ks)
-            f32x16 s = zero16(), dp = zero16();
+            // (chain 0: S, chain 1: dP; operands read ahead)
+            f32x16 sd[2] = {zero16(), zero16()};
             __builtin_amdgcn_s_setprio(1);
-            {
-                typename MM::frag ak[2], av[2];
-                ak[0] = load_frag<T>(k + LK::off(ln, hl * E));
-                av[0] = load_frag<T>(v + LK::off(ln, hl * E));
-#pragma unroll
-                for (int ks = 0; ks < KS; ++ks) {
-                    if (ks + 1 < KS) {
-                        ak[(ks + 1) & 1] = load_frag<T>(k + LK::off(ln, (ks + 1) * 2 * E + hl * E));
-                        av[(ks + 1) & 1] = load_frag<T>(v + LK::off(ln, (ks + 1) * 2 * E + hl * E));
-                    }
-                    __builtin_amdgcn_sched_barrier(0);
-                    s = MM::mma(ak[ks & 1], qf[ks], s);
-                    dp = MM::mma(av[ks & 1], of[ks], dp);
-                    __builtin_amdgcn_sched_barrier(0);
-                }
-            }
+            lds_chain<T, 2, KS, BWD_PF>(
+                sd, [&](int c, int ks) { return load_frag<T>((c ? v : k) + LK::off(ln, ks * 2 * E + hl * E)); },
+                [&](int c, int ks) { return c ? of[ks] : qf[ks]; });
             __builtin_amdgcn_s_setprio(0);
+            const f32x16 s = sd[0], dp = sd[1];
             const bool edge = (kv0 + BC > kend) || (causal && kv0 + BC - 1 > qw0);
             float ds[16];
             uint32_t keep = 0xFFFFu;

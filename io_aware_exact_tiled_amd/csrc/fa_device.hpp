@@ -227,13 +227,14 @@ typedef __attribute__((address_space(1))) void glb_void;
 
 // Stage ROWS x D elements (rows row0.. of a row-major [N][D] head slab) into
 // a swizzled LDS tile whose rows are in MFMA row order, with 16-byte
-// global-to-LDS loads.  One such load writes the 64 lanes' 16 bytes to 64
+// buffer-to-LDS loads.  One such load writes the 64 lanes' 16 bytes to 64
 // consecutive LDS units, so each lane fetches the global chunk that belongs
-// at its unit.  Rows past N read row N-1 (finite data; those rows are masked
-// by the caller).  Issued by all NW waves of the workgroup (`wave` must be
-// wave-uniform); completion is awaited with s_waitcnt before the barrier that
-// publishes the tile.  The address is a uniform row base plus a 32-bit lane
-// offset, so the loads take the scalar-base form.
+// at its unit.  The buffer descriptor covers only the rows that exist, so
+// rows past N read as zeros (the hardware range check).  Issued by all NW
+// waves of the workgroup (`wave` must be wave-uniform); completion is awaited
+// with s_waitcnt before the barrier that publishes the tile.  (The buffer
+// form rather than the global one: with a global load to LDS in flight the
+// compiler turns every wait on an LDS read into a full drain.)
 template <class T, int ROWS, int D, int NW = 4>
 __device__ inline void dma_rows(T* tile, const T* head, int row0, int N, int wave, int lane) {
     typedef SwzTr<T, D> L;
@@ -241,19 +242,17 @@ __device__ inline void dma_rows(T* tile, const T* head, int row0, int N, int wav
     constexpr int UPR = D / EPU;
     constexpr int UNITS = ROWS * UPR;
     static_assert(UNITS % (64 * NW) == 0, "tile must be a whole number of workgroup-wide loads");
-    const char* base = reinterpret_cast<const char*>(head + (size_t)row0 * D);
-    const int last = N - 1 - row0;                    // rows r > last repeat row `last`
-    const bool full = row0 + ROWS <= N;
+    const int rows = N - row0 < ROWS ? N - row0 : ROWS;
+    const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<T*>(head + (size_t)row0 * D), (short)0, rows * D * (int)sizeof(T), 0x00020000);
 #pragma unroll
     for (int n = 0; n < UNITS / (64 * NW); ++n) {
         const int blk = n * NW + wave;                // this wave's 64-unit block
         const int P = blk * 64 + lane;                // LDS unit written by this lane
         const int slot = P / UPR, pu = P % UPR;
         const int u = pu ^ L::f(slot);
-        int r = slot_row(slot);
-        if (!full) r = r < last ? r : last;
-        const uint32_t off = (uint32_t)((r * D + u * EPU) * (int)sizeof(T));
-        __builtin_amdgcn_global_load_lds((glb_void*)(base + off), (lds_void*)(tile + blk * 64 * EPU), 16, 0, 0);
+        const uint32_t off = (uint32_t)((slot_row(slot) * D + u * EPU) * (int)sizeof(T));
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_void*)(tile + blk * 64 * EPU), 16, off, 0, 0, 0);
     }
 }
 
@@ -296,6 +295,32 @@ __device__ inline typename Mma<T>::frag load_frag_tr(const T* tile, int col0, Ro
     } else {
         // one element per lane (k-slot lane/32): a plain read
         return tile[L::off(rowof(lane >> 5), col0 + (lane & 31))];
+    }
+}
+
+// NC independent chains acc[c] += A(c, ks) x B(c, ks) over KS steps, with
+// the A operands read from LDS by afrag(c, ks) PF steps ahead of their MFMA
+// (LDS latency under load is several MFMA issue times) and the B operands
+// in registers.  The fences keep the compiler from sinking the reads.
+template <class T, int NC, int KS, int PF, class AFrag, class BFrag>
+__device__ inline void lds_chain(f32x16 (&acc)[NC], AFrag afrag, BFrag bfrag) {
+    typedef Mma<T> MM;
+    constexpr int P = PF < KS ? PF : KS - 1;
+    typename MM::frag af[P + 1][NC];
+#pragma unroll
+    for (int st = 0; st < P; ++st)
+#pragma unroll
+        for (int c = 0; c < NC; ++c) af[st][c] = afrag(c, st);
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+        if (ks + P < KS) {
+#pragma unroll
+            for (int c = 0; c < NC; ++c) af[(ks + P) % (P + 1)][c] = afrag(c, ks + P);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int c = 0; c < NC; ++c) acc[c] = MM::mma(af[ks % (P + 1)][c], bfrag(c, ks), acc[c]);
+        __builtin_amdgcn_sched_barrier(0);
     }
 }
 

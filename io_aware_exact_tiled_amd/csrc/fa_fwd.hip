@@ -196,7 +196,7 @@ __global__ __launch_bounds__(256, sizeof(T) == 4 ? 1 : 2) void fwd_kernel(FwdArg
         qf[ks] = (qrow < N) ? load_frag<T>(Qg + (size_t)qrow * D + ks * 2 * E + hl * E)
                             : zero_frag<T>();
 
-    // K_j, V_j: global -> LDS, rows past N repeat row N-1 (masked as keys >= kend)
+    // K_j, V_j: global -> LDS, rows past N read as zeros (masked as keys >= kend)
     auto load_tile = [&](int j, int buf) {
         dma_rows<T, BC, D>(sK + buf * TILE, Kg, j * BC, N, wave, lane);
         dma_rows<TV, BC, D>(sV + buf * TILE, Vg, j * BC, N, wave, lane);
@@ -231,31 +231,14 @@ __global__ __launch_bounds__(256, sizeof(T) == 4 ? 1 : 2) void fwd_kernel(FwdArg
         auto tile_math = [&](bool edge) {
             const T* k = sK + buf * TILE;
             const TV* v = sV + buf * TILE;
-            // ---- S^T = K_j Q^T
-            // (software-pipelined: the K operands of step ks+1 are read
-            // before the MFMAs of step ks are issued)
+            // ---- S^T = K_j Q^T (K operands read ahead)
             f32x16 s[KB];
+#pragma unroll
+            for (int kb = 0; kb < KB; ++kb) s[kb] = zero16();
             __builtin_amdgcn_s_setprio(1);
-            {
-                typename MS::frag kf[2][KB];
-#pragma unroll
-                for (int kb = 0; kb < KB; ++kb) {
-                    s[kb] = zero16();
-                    kf[0][kb] = load_frag<T>(k + LK::off(kb * 32 + ln, hl * E));
-                }
-#pragma unroll
-                for (int ks = 0; ks < KS; ++ks) {
-                    if (ks + 1 < KS) {
-#pragma unroll
-                        for (int kb = 0; kb < KB; ++kb)
-                            kf[(ks + 1) & 1][kb] = load_frag<T>(k + LK::off(kb * 32 + ln, (ks + 1) * 2 * E + hl * E));
-                    }
-                    __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-                    for (int kb = 0; kb < KB; ++kb) s[kb] = MS::mma(kf[ks & 1][kb], qf[ks], s[kb]);
-                    __builtin_amdgcn_sched_barrier(0);
-                }
-            }
+            lds_chain<T, KB, KS, FWD_PF>(
+                s, [&](int kb, int ks) { return load_frag<T>(k + LK::off(kb * 32 + ln, ks * 2 * E + hl * E)); },
+                [&](int, int ks) { return qf[ks]; });
             __builtin_amdgcn_s_setprio(0);
             if (__builtin_expect(edge, 0)) {
 #pragma unroll

@@ -24,6 +24,16 @@ constexpr int BWD_KV_BR16 = 64;  // 16-bit inputs
 constexpr int BWD_KV_BR32 = 32;  // fp32 inputs (LDS budget of the double buffer)
 constexpr int BWD_DQ_BR = 128;
 constexpr int BWD_DQ_BC = 32;
+// How many MFMA steps ahead the LDS operands of the S (and dP) products are
+// read: forward and backward.
+#ifndef FWD_PF_STEPS
+#define FWD_PF_STEPS 3
+#endif
+#ifndef BWD_PF_STEPS
+#define BWD_PF_STEPS 3
+#endif
+constexpr int FWD_PF = FWD_PF_STEPS;
+constexpr int BWD_PF = BWD_PF_STEPS;
 template <class T> struct BwdTiles {
     static constexpr int KV_BR = sizeof(T) == 4 ? BWD_KV_BR32 : BWD_KV_BR16;
 };
