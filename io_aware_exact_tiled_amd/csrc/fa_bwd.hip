@@ -274,7 +274,7 @@ __global__ __launch_bounds__(512, 1) void bwd_kv_kernel(BwdArgs a) {
         __builtin_amdgcn_s_setprio(1);
         {
             const T* src = RA ? q : o;
-            lds_chain<T, QB, KS, BWD_PF>(
+            lds_chain<T, QB, KS, BWD_PF<D>>(
                 sp, [&](int qb, int ks) { return load_frag<T>(src + LQ::off(qb * 32 + ln, ks * 2 * E + hl * E)); },
                 [&](int, int ks) { return kvf[ks]; });
         }
@@ -479,7 +479,7 @@ __global__ __launch_bounds__(256, sizeof(T) == 4 ? 1 : 2) void bwd_dq_kernel(Bwd
             // (chain 0: S, chain 1: dP; operands read ahead)
             f32x16 sd[2] = {zero16(), zero16()};
             __builtin_amdgcn_s_setprio(1);
-            lds_chain<T, 2, KS, BWD_PF>(
+            lds_chain<T, 2, KS, BWD_PF<D>>(
                 sd, [&](int c, int ks) { return load_frag<T>((c ? v : k) + LK::off(ln, ks * 2 * E + hl * E)); },
                 [&](int c, int ks) { return c ? of[ks] : qf[ks]; });
             __builtin_amdgcn_s_setprio(0);

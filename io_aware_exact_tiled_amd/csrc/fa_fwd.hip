@@ -236,7 +236,7 @@ __global__ __launch_bounds__(256, sizeof(T) == 4 ? 1 : 2) void fwd_kernel(FwdArg
 #pragma unroll
             for (int kb = 0; kb < KB; ++kb) s[kb] = zero16();
             __builtin_amdgcn_s_setprio(1);
-            lds_chain<T, KB, KS, FWD_PF>(
+            lds_chain<T, KB, KS, FWD_PF<D>>(
                 s, [&](int kb, int ks) { return load_frag<T>(k + LK::off(kb * 32 + ln, ks * 2 * E + hl * E)); },
                 [&](int, int ks) { return qf[ks]; });
             __builtin_amdgcn_s_setprio(0);

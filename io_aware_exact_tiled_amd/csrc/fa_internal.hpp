@@ -25,15 +25,11 @@ constexpr int BWD_KV_BR32 = 32;  // fp32 inputs (LDS budget of the double buffer
 constexpr int BWD_DQ_BR = 128;
 constexpr int BWD_DQ_BC = 32;
 // How many MFMA steps ahead the LDS operands of the S (and dP) products are
-// read: forward and backward.
-#ifndef FWD_PF_STEPS
-#define FWD_PF_STEPS 3
-#endif
-#ifndef BWD_PF_STEPS
-#define BWD_PF_STEPS 3
-#endif
-constexpr int FWD_PF = FWD_PF_STEPS;
-constexpr int BWD_PF = BWD_PF_STEPS;
+// read.  Deeper read-ahead hides more LDS latency but costs registers: at
+// d = 64 one step keeps the forward at 4 waves per SIMD and two keep the dQ
+// kernel at 4 (measured faster there than deeper read-ahead at 3 waves).
+template <int D> constexpr int FWD_PF = D == 64 ? 1 : 3;
+template <int D> constexpr int BWD_PF = D == 64 ? 2 : 3;
 template <class T> struct BwdTiles {
     static constexpr int KV_BR = sizeof(T) == 4 ? BWD_KV_BR32 : BWD_KV_BR16;
 };
