@@ -29,8 +29,14 @@ What it computes is the plain definition that tiled exact attention reaches
       D_i = sum_j P_ij dP_ij,  dS = P * (dP - D),
       dQ = scale dS K,  dK = scale dS^T Q.
 
-Arrays are numpy float64 [B, H, N, d]; the callers convert the storage-dtype
-tensors exactly.  Long inputs are processed in chunks of query rows; every
+* grouped-query attention (tutorial section 9.2-9.3, MQA and GQA): K and V
+  may have Hkv heads, Hkv dividing H; query head h uses K/V head
+  h // (H / Hkv) (contiguous groups -- the pages do not fix the grouping),
+  so dK, dV of a K/V head are the sums over its query heads.  Hkv = H is
+  plain multi-head attention, Hkv = 1 multi-query.
+
+Arrays are numpy float64 [B, H, N, d] (K, V: [B, Hkv, N, d]); the callers
+convert the storage-dtype tensors exactly.  Long inputs are processed in chunks of query rows; every
 row is always complete, so chunking changes nothing in the arithmetic.
 """
 
@@ -95,6 +101,11 @@ def _rows_scores(q, k, rows, scale):
     return scale * (q[rows] @ k.T)
 
 
+def kv_head(h: int, H: int, Hkv: int) -> int:
+    """K/V head that query head h reads (contiguous groups of H/Hkv)."""
+    return h // (H // Hkv)
+
+
 def _pairs(B, H, pairs):
     return pairs if pairs is not None else [(b, h) for b in range(B) for h in range(H)]
 
@@ -105,21 +116,23 @@ def attn_fwd(q, k, v, scale, causal=False, key_lens=None, block_mask=None,
     `pairs` restricts the work to a list of (b, h) (other heads stay 0)."""
     q, k, v = as_f64(q), as_f64(k), as_f64(v)
     B, H, N, d = q.shape
+    Hkv = k.shape[1]
     sc = scale_f32(scale)
     rows = np.arange(N) if rows is None else np.asarray(rows)
     O = np.zeros((B, H, len(rows), v.shape[-1]))
     LSE = np.zeros((B, H, len(rows)))
     for b, h in _pairs(B, H, pairs):
         kl = _key_len(key_lens, b)
+        g = kv_head(h, H, Hkv)
         for s in range(0, len(rows), chunk):
             r = rows[s:s + chunk]
-            S = _rows_scores(q[b, h], k[b, h], r, sc)
+            S = _rows_scores(q[b, h], k[b, g], r, sc)
             A = validity(r, N, causal, kl, block_mask)
             P, lse, _, _ = safe_softmax(S, A)
             if dropout_p > 0.0:
                 Z = keep_mask(seed, rng_offset, dropout_p, b, h, H, r, np.arange(N))
                 P = P * Z / (1.0 - float(np.float32(dropout_p)))
-            O[b, h, s:s + chunk] = P @ v[b, h]
+            O[b, h, s:s + chunk] = P @ v[b, g]
             LSE[b, h, s:s + chunk] = lse
     return O, LSE
 
@@ -136,11 +149,13 @@ def attn_bwd(q, k, v, do, scale, causal=False, key_lens=None, block_mask=None,
     dk = np.zeros_like(k)
     dv = np.zeros_like(v)
     Dall = np.zeros((B, H, N))
+    Hkv = k.shape[1]
     for b, h in _pairs(B, H, pairs):
         kl = _key_len(key_lens, b)
+        g = kv_head(h, H, Hkv)
         for s in range(0, N, chunk):
             r = np.arange(s, min(s + chunk, N))
-            S = _rows_scores(q[b, h], k[b, h], r, sc)
+            S = _rows_scores(q[b, h], k[b, g], r, sc)
             A = validity(r, N, causal, kl, block_mask)
             P, _, _, _ = safe_softmax(S, A)
             if dropout_p > 0.0:
@@ -148,13 +163,13 @@ def attn_bwd(q, k, v, do, scale, causal=False, key_lens=None, block_mask=None,
             else:
                 Z = np.ones_like(P, dtype=bool)
             P_hat = P * Z * keep_scale
-            dP_hat = do[b, h, r] @ v[b, h].T
-            dv[b, h] += P_hat.T @ do[b, h, r]
+            dP_hat = do[b, h, r] @ v[b, g].T
+            dv[b, g] += P_hat.T @ do[b, h, r]
             dP = dP_hat * Z * keep_scale
             D = (P * dP).sum(axis=1)
             dS = P * (dP - D[:, None])
-            dq[b, h, r] = sc * (dS @ k[b, h])
-            dk[b, h] += sc * (dS.T @ q[b, h, r])
+            dq[b, h, r] = sc * (dS @ k[b, g])
+            dk[b, g] += sc * (dS.T @ q[b, h, r])
             Dall[b, h, r] = D
     return dq, dk, dv, Dall
 
@@ -176,34 +191,36 @@ def attn_bwd_rows_cols(q, k, v, do, scale, rows, cols, lse_all, D_all,
     keep_scale = 1.0 / (1.0 - float(np.float32(dropout_p))) if dropout_p > 0 else 1.0
     rows = np.asarray(rows)
     cols = np.asarray(cols)
+    Hkv = k.shape[1]
     dq = np.zeros((B, H, len(rows), d))
-    dk = np.zeros((B, H, len(cols), d))
-    dv = np.zeros((B, H, len(cols), d))
+    dk = np.zeros((B, Hkv, len(cols), d))
+    dv = np.zeros((B, Hkv, len(cols), d))
     for b, h in _pairs(B, H, pairs):
         kl = _key_len(key_lens, b)
+        g = kv_head(h, H, Hkv)
         # dQ rows: full rows of S
-        S = _rows_scores(q[b, h], k[b, h], rows, sc)
+        S = _rows_scores(q[b, h], k[b, g], rows, sc)
         A = validity(rows, N, causal, kl, block_mask)
         P, _, _, _ = safe_softmax(S, A)
         Z = (keep_mask(seed, rng_offset, dropout_p, b, h, H, rows, np.arange(N))
              if dropout_p > 0 else np.ones_like(P, dtype=bool))
-        dP = (do[b, h, rows] @ v[b, h].T) * Z * keep_scale
+        dP = (do[b, h, rows] @ v[b, g].T) * Z * keep_scale
         D = (P * dP).sum(axis=1)
-        dq[b, h] = sc * ((P * (dP - D[:, None])) @ k[b, h])
+        dq[b, h] = sc * ((P * (dP - D[:, None])) @ k[b, g])
         # dK, dV columns: all query rows, selected keys
         for s in range(0, N, chunk):
             r = np.arange(s, min(s + chunk, N))
-            Sc = sc * (q[b, h, r] @ k[b, h, cols].T)
+            Sc = sc * (q[b, h, r] @ k[b, g, cols].T)
             Ac = validity(r, N, causal, kl, block_mask)[:, cols]
             lse = lse_all[b, h, r]
             live = np.isfinite(lse)[:, None] & Ac
             Pc = np.where(live, np.exp(np.where(live, Sc - lse[:, None], -np.inf)), 0.0)
             Zc = (keep_mask(seed, rng_offset, dropout_p, b, h, H, r, cols)
                   if dropout_p > 0 else np.ones_like(Pc, dtype=bool))
-            dv[b, h] += (Pc * Zc * keep_scale).T @ do[b, h, r]
-            dPc = (do[b, h, r] @ v[b, h, cols].T) * Zc * keep_scale
+            dv[b, g] += (Pc * Zc * keep_scale).T @ do[b, h, r]
+            dPc = (do[b, h, r] @ v[b, g, cols].T) * Zc * keep_scale
             dSc = Pc * (dPc - D_all[b, h, r][:, None])
-            dk[b, h] += sc * (dSc.T @ q[b, h, r])
+            dk[b, g] += sc * (dSc.T @ q[b, h, r])
     return dq, dk, dv
 
 
@@ -217,16 +234,18 @@ def attn_stats(q, k, v, do, scale, causal=False, key_lens=None, block_mask=None,
     keep_scale = 1.0 / (1.0 - float(np.float32(dropout_p))) if dropout_p > 0 else 1.0
     LSE = np.zeros((B, H, N))
     Dall = np.zeros((B, H, N))
+    Hkv = k.shape[1]
     for b, h in _pairs(B, H, heads):
         kl = _key_len(key_lens, b)
+        g = kv_head(h, H, Hkv)
         for s in range(0, N, chunk):
             r = np.arange(s, min(s + chunk, N))
-            S = _rows_scores(q[b, h], k[b, h], r, sc)
+            S = _rows_scores(q[b, h], k[b, g], r, sc)
             A = validity(r, N, causal, kl, block_mask)
             P, lse, _, _ = safe_softmax(S, A)
             Z = (keep_mask(seed, rng_offset, dropout_p, b, h, H, r, np.arange(N))
                  if dropout_p > 0 else np.ones_like(P, dtype=bool))
-            dP = (do[b, h, r] @ v[b, h].T) * Z * keep_scale
+            dP = (do[b, h, r] @ v[b, g].T) * Z * keep_scale
             LSE[b, h, r] = lse
             Dall[b, h, r] = (P * dP).sum(axis=1)
     return LSE, Dall

@@ -196,6 +196,7 @@ def test_fully_masked_rows():
 
 def _sdpa_ref(q, k, v, do, scale, causal, key_lens, block_mask):
     tq, tk, tv = (torch.tensor(x, dtype=torch.float64, requires_grad=True) for x in (q, k, v))
+    gqa = k.shape[1] != q.shape[1]
     B, H, N, d = q.shape
     mask = torch.ones(B, 1, N, N, dtype=torch.bool)
     if causal:
@@ -206,7 +207,7 @@ def _sdpa_ref(q, k, v, do, scale, causal, key_lens, block_mask):
         idx = torch.arange(N) // 128
         mask &= torch.tensor(block_mask).bool()[idx[:, None], idx[None, :]]
     o = torch.nn.functional.scaled_dot_product_attention(
-        tq, tk, tv, attn_mask=mask, scale=float(np.float32(scale)))
+        tq, tk, tv, attn_mask=mask, scale=float(np.float32(scale)), enable_gqa=gqa)
     o.backward(torch.tensor(do))
     return o.detach().numpy(), tq.grad.numpy(), tk.grad.numpy(), tv.grad.numpy()
 
@@ -226,6 +227,51 @@ def test_against_torch_sdpa_fp64(variant):
     assert np.allclose(O, Or, rtol=0, atol=1e-12)
     for a, b in ((dq, dqr), (dk, dkr), (dv, dvr)):
         assert np.allclose(a, b, rtol=0, atol=1e-11)
+
+
+@pytest.mark.parametrize("hkv,variant", [(2, 0), (2, 1), (1, 3), (3, 4), (1, 2)])
+def test_gqa_against_torch_sdpa_fp64(hkv, variant):
+    """Grouped-query / multi-query attention (tutorial section 9.2-9.3): the
+    oracle with Hkv < H K/V heads against torch's own GQA path
+    (enable_gqa), forward and autograd gradients, dK and dV summed over each
+    group of H / Hkv query heads."""
+    N, H = 300, 6
+    rng = np.random.default_rng(40 + hkv + variant)
+    q, do = rng.standard_normal((2, H, N, 16)), rng.standard_normal((2, H, N, 16))
+    k, v = rng.standard_normal((2, hkv, N, 16)), rng.standard_normal((2, hkv, N, 16))
+    kw = mask_variants(N, 2)[variant]
+    if variant == 3:
+        kw["key_lens"] = np.array([N - 100, N - 3])
+    O, L = oracle.attn_fwd(q, k, v, 0.3, **kw)
+    dq, dk, dv, _ = oracle.attn_bwd(q, k, v, do, 0.3, **kw)
+    assert dk.shape == k.shape and dv.shape == v.shape
+    Or, dqr, dkr, dvr = _sdpa_ref(q, k, v, do, 0.3, kw.get("causal", False), kw.get("key_lens"),
+                                  kw.get("block_mask"))
+    assert np.allclose(O, Or, rtol=0, atol=1e-12)
+    for a, b in ((dq, dqr), (dk, dkr), (dv, dvr)):
+        assert np.allclose(a, b, rtol=0, atol=1e-11)
+
+
+def test_gqa_grouping_and_sampled_variants():
+    """Query head h reads K/V head h // (H / Hkv): moving K/V head 1 changes
+    exactly the outputs of query heads 2 and 3 (H = 4, Hkv = 2); the sampled
+    row/column backward and the statistics pass agree with the full pass."""
+    N, H = 130, 4
+    rng = np.random.default_rng(7)
+    q, do = rng.standard_normal((1, H, N, 8)), rng.standard_normal((1, H, N, 8))
+    k, v = rng.standard_normal((1, 2, N, 8)), rng.standard_normal((1, 2, N, 8))
+    O, L = oracle.attn_fwd(q, k, v, 0.4, causal=True)
+    k2 = k.copy()
+    k2[0, 1] += 0.5 * rng.standard_normal((N, 8))   # (a constant shift would cancel in the softmax)
+    O2, _ = oracle.attn_fwd(q, k2, v, 0.4, causal=True)
+    changed = [not np.allclose(O[0, h], O2[0, h]) for h in range(H)]
+    assert changed == [False, False, True, True]
+    dq, dk, dv, D = oracle.attn_bwd(q, k, v, do, 0.4, causal=True)
+    L2, D2 = oracle.attn_stats(q, k, v, do, 0.4, causal=True)
+    assert np.allclose(L2, L) and np.allclose(D2, D)
+    rows, cols = np.array([0, 7, 129]), np.array([3, 64, 128])
+    sq, sk, sv = oracle.attn_bwd_rows_cols(q, k, v, do, 0.4, rows, cols, L2, D2, causal=True)
+    assert np.allclose(sq, dq[:, :, rows]) and np.allclose(sk, dk[:, :, cols]) and np.allclose(sv, dv[:, :, cols])
 
 
 # ---------------------------------------------------------------- gradients
