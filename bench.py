@@ -154,7 +154,7 @@ def time_workload(w, steps, warmup, ev):
               block_mask=None if x["block_mask"] is None else x["block_mask"].to(dev), scale=w.scale)
     o = torch.empty_like(q)
     lse = torch.empty(w.B, w.H, w.N, dtype=torch.float32, device=dev)
-    grads = tuple(torch.empty_like(q) for _ in range(3))
+    grads = (torch.empty_like(q), torch.empty_like(k), torch.empty_like(v))
     ws = torch.empty(fa.bwd_workspace_bytes(w.B, w.H, w.N, w.d), dtype=torch.uint8, device=dev)
     fws = torch.empty(max(1, fa.fwd_workspace_bytes(w.B, w.H, w.N, w.d, q.dtype)), dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream(dev).cuda_stream
@@ -284,9 +284,9 @@ def main():
         "vs_baseline": None,
         "dtype": w.dtype,
         "data": "synthetic (seeded Gaussian Q, K, V, dO)",
-        "config": {"workload": f"{w.name}: B={w.B} H={w.H} N={w.N} d={w.d} {w.dtype}"
-                               f"{' causal' if w.causal else ''}", "B": w.B, "H": w.H, "N": w.N, "d": w.d,
-                   "causal": w.causal, "valid_pairs": r["pairs"]},
+        "config": {"workload": f"{w.name}: B={w.B} H={w.H}{f' Hkv={w.Hkv}' if w.Hkv != w.H else ''} N={w.N} "
+                               f"d={w.d} {w.dtype}{' causal' if w.causal else ''}", "B": w.B, "H": w.H,
+                   "Hkv": w.Hkv, "N": w.N, "d": w.d, "causal": w.causal, "valid_pairs": r["pairs"]},
         "pct_peak": round(100 * total_tflops / peak, 2),
         "fwd_tflops": round(fwd_tf, 2), "fwd_pct_peak": round(100 * fwd_tf / peak, 2), "fwd_ms": round(fwd_ms, 4),
         "bwd_tflops": round(bwd_tf, 2), "bwd_pct_peak": round(100 * bwd_tf / peak, 2), "bwd_ms": round(bwd_ms, 4),

@@ -34,7 +34,8 @@
  *    enqueued on `stream` in order and the call returns before it completes.
  *    A workspace must not be used by two calls whose work overlaps.
  *  - Q, K, V, O, dO, dQ, dK, dV are contiguous [B][H][N][d] row-major with
- *    16-byte aligned base addresses.  LSE and D are float [B][H][N].
+ *    16-byte aligned base addresses; K, V, dK, dV have opts->kv_heads heads
+ *    instead of H when that is set (grouped-query attention).  LSE and D are float [B][H][N].
  *    Outputs must not alias inputs.
  *  - LSE_i = ln sum_j exp(S_ij) over valid j (natural log, scaled scores);
  *    a row without any valid key has O = 0, LSE = -inf and zero gradients.
@@ -61,7 +62,7 @@
 extern "C" {
 #endif
 
-#define FA_ABI_VERSION 2
+#define FA_ABI_VERSION 3
 
 typedef enum { FA_F32 = 0, FA_F16 = 1, FA_BF16 = 2 } fa_dtype;
 
@@ -112,6 +113,13 @@ typedef struct {
                                    kernels, without the D pre-pass)             */
     hipEvent_t main_mid;        /* fa_bwd profiling, optional: recorded between
                                    the dK/dV kernel and the dQ kernel            */
+    int32_t kv_heads;           /* grouped-query attention: K and V (and dK, dV)
+                                   are [B][kv_heads][N][d] and query head h uses
+                                   K/V head h / (H / kv_heads); kv_heads must
+                                   divide H (else FA_ERR_OPTS); 1 = multi-query;
+                                   0 = H.  Callers whose struct_size predates
+                                   this field get H.  dK, dV are summed over
+                                   the query heads that share a K/V head.      */
 } fa_opts;
 
 /* Bytes of device workspace fa_fwd needs.  bf16: the forward multiplies P

@@ -33,17 +33,28 @@ def _dtype_code(t: torch.Tensor) -> int:
     return _DT[t.dtype]
 
 
-def _check_qkv(*ts: torch.Tensor):
-    ref = ts[0]
-    if ref.dim() != 4:
+def _check_qkv(q, k, v, *more):
+    """q (and dO, O): [B, H, N, d]; k, v: [B, Hkv, N, d] with Hkv dividing H
+    (grouped-query attention; Hkv == H is plain multi-head).  Returns Hkv."""
+    if q.dim() != 4:
         raise ValueError("expected [B, H, N, d] tensors")
-    for t in ts:
+    for t in (q, k, v) + more:
         if not t.is_cuda:
             raise ValueError("tensors must be on a GPU device")
-        if t.shape != ref.shape or t.dtype != ref.dtype or t.device != ref.device:
-            raise ValueError("q, k, v (and dO) must share shape, dtype and device")
+        if t.dtype != q.dtype or t.device != q.device:
+            raise ValueError("q, k, v (and dO) must share dtype and device")
         if not t.is_contiguous():
             raise ValueError("tensors must be contiguous [B, H, N, d]")
+    for t in more:
+        if t.shape != q.shape:
+            raise ValueError("dO must have q's shape")
+    B, H, N, d = q.shape
+    if k.shape != v.shape or k.dim() != 4 or k.shape[0] != B or k.shape[2:] != q.shape[2:]:
+        raise ValueError("k, v must be [B, Hkv, N, d] with q's B, N, d")
+    hkv = k.shape[1]
+    if hkv < 1 or H % hkv:
+        raise ValueError("the number of K/V heads must divide the number of query heads")
+    return hkv
 
 
 def _stream(dev: torch.device) -> ctypes.c_void_p:
@@ -51,8 +62,9 @@ def _stream(dev: torch.device) -> ctypes.c_void_p:
 
 
 def _opts(B, H, N, d, pass_, key_lens, rng_offset, o_fp32, record_tiles, reverse_kv, device, dtype_code,
-          events=None):
+          events=None, kv_heads=0):
     opts = FaOpts()
+    opts.kv_heads = 0 if kv_heads == H else int(kv_heads)
     if events is not None:
         opts.main_begin, opts.main_end = events[0], events[1]
         if len(events) > 2:
@@ -103,7 +115,7 @@ def fwd(q, k, v, *, causal=False, dropout_p=0.0, seed=0, rng_offset=0, key_lens=
     recorded around the kernel (profiling).  O is fp32 when o_fp32, else q's dtype; LSE is fp32
     [B, H, N].  `workspace`: a uint8 device tensor of fwd_workspace_bytes
     (allocated here when None and needed)."""
-    _check_qkv(q, k, v)
+    hkv = _check_qkv(q, k, v)
     B, H, N, d = q.shape
     scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
     dt = _dtype_code(q)
@@ -111,7 +123,7 @@ def fwd(q, k, v, *, causal=False, dropout_p=0.0, seed=0, rng_offset=0, key_lens=
                                                 device=q.device)
     l = lse if lse is not None else torch.empty((B, H, N), dtype=torch.float32, device=q.device)
     opts, keep, tiles = _opts(B, H, N, d, 0, key_lens, rng_offset, o_fp32, record_tiles, reverse_kv,
-                              q.device, dt, events)
+                              q.device, dt, events, hkv)
     bm, bmp = _mask_ptr(block_mask, q.device, N)
     need = fwd_workspace_bytes(B, H, N, d, q.dtype)
     ws = workspace
@@ -133,10 +145,11 @@ def bwd_workspace_bytes(B, H, N, d) -> int:
 def bwd(q, k, v, o, do, lse, *, causal=False, dropout_p=0.0, seed=0, rng_offset=0, key_lens=None,
         block_mask=None, scale: Optional[float] = None, record_tiles=False, workspace=None, grads=None,
         events=None):
-    """Backward pass.  Returns (dQ, dK, dV) in q's dtype, plus, when
+    """Backward pass.  Returns (dQ, dK, dV) in q's dtype (dK, dV with k's
+    shape: summed over the query heads that share a K/V head), plus, when
     record_tiles is set, the (dK/dV kernel, dQ kernel) tile-visit maps.
     O may be fp32 (if the forward wrote it so) or q's dtype."""
-    _check_qkv(q, k, v, do)
+    hkv = _check_qkv(q, k, v, do)
     B, H, N, d = q.shape
     scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
     dt = _dtype_code(q)
@@ -146,13 +159,13 @@ def bwd(q, k, v, o, do, lse, *, causal=False, dropout_p=0.0, seed=0, rng_offset=
         raise ValueError("LSE must be contiguous fp32 [B, H, N]")
     o_fp32 = o.dtype == torch.float32 and q.dtype != torch.float32
     if grads is None:
-        dq, dk, dv = (torch.empty_like(q) for _ in range(3))
+        dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
     else:
         dq, dk, dv = grads
     need = bwd_workspace_bytes(B, H, N, d)
     ws = workspace if workspace is not None else torch.empty(need, dtype=torch.uint8, device=q.device)
     opts, keep, tiles = _opts(B, H, N, d, 1, key_lens, rng_offset, o_fp32, record_tiles, False, q.device, dt,
-                              events)
+                              events, hkv)
     bm, bmp = _mask_ptr(block_mask, q.device, N)
     code = _lib.lib().fa_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), do.data_ptr(),
                              lse.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), B, H, N, d, dt,

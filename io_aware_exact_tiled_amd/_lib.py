@@ -39,6 +39,7 @@ class FaOpts(ctypes.Structure):
         ("main_begin", ctypes.c_void_p),
         ("main_end", ctypes.c_void_p),
         ("main_mid", ctypes.c_void_p),
+        ("kv_heads", ctypes.c_int32),
     ]
 
 

@@ -4,6 +4,7 @@
 
 #include <cmath>
 #include <cstdint>
+#include <cstddef>
 #include <cstring>
 
 #include "../../include/fa.h"
@@ -40,11 +41,21 @@ fa_status check_common(int32_t B, int32_t H, int32_t N, int32_t d, fa_dtype dtyp
     if (!std::isfinite(dropout_p) || dropout_p < 0.0f || dropout_p >= 1.0f) return FA_ERR_DROPOUT;
     if (!std::isfinite(scale) || scale <= 0.0f) return FA_ERR_SCALE;
     if (opts) {
-        if (opts->struct_size != sizeof(fa_opts)) return FA_ERR_OPTS;
+        // the current layout, or the one before kv_heads was appended
+        if (opts->struct_size != sizeof(fa_opts) && opts->struct_size != offsetof(fa_opts, kv_heads))
+            return FA_ERR_OPTS;
         if (opts->flags & ~(uint32_t)(FA_FLAG_RECORD_TILES | FA_FLAG_REVERSE_KV)) return FA_ERR_OPTS;
         if ((opts->flags & FA_FLAG_RECORD_TILES) && !opts->tile_visits) return FA_ERR_NULL;
     }
     return FA_OK;
+}
+
+// K/V heads: opts->kv_heads when the caller's struct has the field and sets
+// it, else H.  Returns 0 when it does not divide H.
+int32_t kv_heads(int32_t H, const fa_opts* opts) {
+    if (!opts || opts->struct_size < offsetof(fa_opts, kv_heads) + sizeof(int32_t) || opts->kv_heads == 0) return H;
+    const int32_t k = opts->kv_heads;
+    return (k >= 1 && k <= H && H % k == 0) ? k : 0;
 }
 
 uint32_t drop_threshold(float p) {
@@ -130,9 +141,11 @@ fa_status fa_fwd(const void* Q, const void* K, const void* V, void* O, float* LS
     const size_t need = fa_fwd_workspace_bytes(B, H, N, d, dtype);
     if (need && (!workspace || workspace_bytes < need || (reinterpret_cast<uintptr_t>(workspace) & 255u)))
         return FA_ERR_WORKSPACE;
+    const int32_t hkv = kv_heads(H, opts);
+    if (!hkv) return FA_ERR_OPTS;
     fa::FwdArgs a;
     a.q = Q; a.k = K; a.v = V; a.o = O; a.lse = LSE;
-    a.B = B; a.H = H; a.N = N;
+    a.B = B; a.H = H; a.N = N; a.Hkv = hkv;
     a.scale_log2 = scale * LOG2E;
     a.o_f32 = (opts && opts->o_fp32) ? 1 : 0;
     a.mask = mask_args(N, causal, block_mask, opts);
@@ -165,11 +178,13 @@ fa_status fa_bwd(const void* Q, const void* K, const void* V, const void* O, con
     const size_t need = fa_bwd_workspace_bytes(B, H, N, d);
     if (!workspace || workspace_bytes < need || (reinterpret_cast<uintptr_t>(workspace) & 255u))
         return FA_ERR_WORKSPACE;
+    const int32_t hkv = kv_heads(H, opts);
+    if (!hkv) return FA_ERR_OPTS;
     fa::BwdArgs a;
     a.q = Q; a.k = K; a.v = V; a.o = O; a.dout = dO; a.lse = LSE;
     a.dq = dQ; a.dk = dK; a.dv = dV;
     a.delta = static_cast<float*>(workspace);
-    a.B = B; a.H = H; a.N = N;
+    a.B = B; a.H = H; a.N = N; a.Hkv = hkv;
     a.scale = scale;
     a.scale_log2 = scale * LOG2E;
     a.o_f32 = (opts && opts->o_fp32) ? 1 : 0;

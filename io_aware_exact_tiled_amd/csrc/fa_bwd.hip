@@ -165,24 +165,22 @@ __global__ __launch_bounds__(512, 1) void bwd_kv_kernel(BwdArgs a) {
     const int hl = lane >> 5, ln = lane & 31;
     const int kb = wave & 3;                      // key block of this wave
     const bool roleA = wave < 4;
-    const int N = a.N, H = a.H;
+    const int N = a.N, H = a.H, Hkv = a.Hkv, G = H / Hkv;
     const int Tr = (N + BR - 1) / BR, Tc = (N + BC - 1) / BC;
-    const int total = Tc * H * a.B;
+    const int total = Tc * Hkv * a.B;
     const int item = xcd_item((int)blockIdx.x, (total + 7) / 8);
     if (item >= total) return;
-    const int bhi = item / Tc;
+    const int bkv = item / Tc;                    // (b, K/V head)
+    const int bidx = bkv / Hkv, g = bkv % Hkv;
     const int jt = item % Tc;                     // key tile of this workgroup
     const int kbase = jt * BC, kw0 = kbase + kb * 32;
-    const size_t bh = (size_t)bhi;
-    const size_t hoff = bh * (size_t)N * D;
-    const T* __restrict__ Qg = (const T*)a.q + hoff;
-    const T* __restrict__ Kg = (const T*)a.k + hoff;
-    const T* __restrict__ Vg = (const T*)a.v + hoff;
-    const T* __restrict__ dOg = (const T*)a.dout + hoff;
-    const float* __restrict__ lseg = a.lse + bh * N;
-    const float* __restrict__ delg = a.delta + bh * N;
+    const size_t koff = (size_t)bkv * N * D;
+    const T* __restrict__ Kg = (const T*)a.k + koff;
+    const T* __restrict__ Vg = (const T*)a.v + koff;
+    // the G query heads that share this K/V head: dK_j, dV_j sum over all of them
+    auto qhead = [&](int hh) -> size_t { return (size_t)bidx * H + (size_t)g * G + hh; };
 
-    const int kend = clamp_len(a.mask.key_lens, bhi / H, N);
+    const int kend = clamp_len(a.mask.key_lens, bidx, N);
     const int causal = a.mask.causal;
     const bool live = kbase < kend;
     const int i_begin = (causal && live) ? kbase / BR : 0;
@@ -194,9 +192,10 @@ __global__ __launch_bounds__(512, 1) void bwd_kv_kernel(BwdArgs a) {
         return -1;
     };
 
-    uint8_t* vis = a.tile_visits ? a.tile_visits + bh * Tr * (size_t)Tc + jt : nullptr;
-    if (vis)
-        for (int i = tid; i < Tr; i += NW * 64) vis[(size_t)i * Tc] = 0;
+    auto vis_at = [&](int hh) { return a.tile_visits + qhead(hh) * Tr * (size_t)Tc + jt; };
+    if (a.tile_visits)
+        for (int hh = 0; hh < G; ++hh)
+            for (int i = tid; i < Tr; i += NW * 64) vis_at(hh)[(size_t)i * Tc] = 0;
 
     const int krow = kw0 + ln;           // this lane's key
     // role A holds K_j, role B holds V_j (as the MFMA B operand of S / dP)
@@ -214,13 +213,14 @@ __global__ __launch_bounds__(512, 1) void bwd_kv_kernel(BwdArgs a) {
 
     // ---- staging of one query tile: Q, dO by global->LDS DMA; LSE, D via registers
     float lreg = 0.0f;
-    auto load_tile = [&](int i, int qbuf, int obuf) {
+    auto load_tile = [&](int hh, int i, int qbuf, int obuf) {
         const int q0 = i * BR;
-        dma_rows<T, BR, D, NW>(sQ + qbuf * TQ, Qg, q0, N, wave, lane);
-        dma_rows<T, BR, D, NW>(sdO + obuf * TQ, dOg, q0, N, wave, lane);
+        const size_t qh = qhead(hh);
+        dma_rows<T, BR, D, NW>(sQ + qbuf * TQ, (const T*)a.q + qh * N * D, q0, N, wave, lane);
+        dma_rows<T, BR, D, NW>(sdO + obuf * TQ, (const T*)a.dout + qh * N * D, q0, N, wave, lane);
         if (tid < 2 * BR) {
             const int q = q0 + (tid % BR);
-            lreg = (q < N) ? (tid < BR ? lseg[q] : delg[q]) : (tid < BR ? INFINITY : 0.0f);
+            lreg = (q < N) ? (tid < BR ? a.lse[qh * N + q] : a.delta[qh * N + q]) : (tid < BR ? INFINITY : 0.0f);
         }
     };
     auto publish_stats = [&](int obuf) {
@@ -243,9 +243,18 @@ __global__ __launch_bounds__(512, 1) void bwd_kv_kernel(BwdArgs a) {
     // register-allocated on its own; both pass the same barriers.
     auto run = [&](auto role) __attribute__((always_inline)) {
     constexpr bool RA = decltype(role)::value;
-    int i = tile_at(i_begin);
+    // walk over (query head hh of the group, visited query tile i); every head
+    // visits the same tiles
+    const int i_first = tile_at(i_begin);
+    int hh = 0, i = i_first;
+    auto next_step = [&](int& h2, int& i2) {
+        const int t = tile_at(i2 + 1);
+        if (t >= 0) i2 = t;
+        else if (h2 + 1 < G) { ++h2; i2 = i_first; }
+        else i2 = -1;
+    };
     if (i >= 0) {
-        load_tile(i, 0, 0);
+        load_tile(hh, i, 0, 0);
         publish_stats(0);
     }
     __builtin_amdgcn_s_waitcnt(0);
@@ -254,13 +263,15 @@ __global__ __launch_bounds__(512, 1) void bwd_kv_kernel(BwdArgs a) {
     bool have_prev = false;              // B holds dS of the previous step in dsf
     while (i >= 0) {
         const int q0 = i * BR;
-        if (vis && tid == 0) vis[(size_t)i * Tc] = 1;
-        const int in = tile_at(i + 1);
+        const uint32_t bh = (uint32_t)qhead(hh);  // query head: the dropout stream
+        if (a.tile_visits && tid == 0) vis_at(hh)[(size_t)i * Tc] = 1;
+        int hn = hh, in = i;
+        next_step(hn, in);
         const int qnext = qbuf == 2 ? 0 : qbuf + 1;
         // lands in the other buffers during this step; the Q buffer last held
         // step n-2 (read by B before the previous step's first barrier), the
         // dO buffer step n-1 (read before the previous step's second barrier)
-        if (in >= 0) load_tile(in, qnext, obuf ^ 1);
+        if (in >= 0) load_tile(hn, in, qnext, obuf ^ 1);
 
         const T* q = sQ + qbuf * TQ;
         const T* o = sdO + obuf * TQ;
@@ -367,6 +378,7 @@ __global__ __launch_bounds__(512, 1) void bwd_kv_kernel(BwdArgs a) {
         qprev = qbuf;
         qbuf = qnext;
         obuf ^= 1;
+        hh = hn;
         i = in;
     }
     // B: the last step's dK product (its Q tile is still in place: no DMA follows)
@@ -378,7 +390,7 @@ __global__ __launch_bounds__(512, 1) void bwd_kv_kernel(BwdArgs a) {
     else run(std::false_type{});
 
     // ---- dV_j = acc (A), dK_j = scale * acc (B); lane holds column db*32+ln, rows = keys
-    T* dst = (T*)(roleA ? a.dv : a.dk) + hoff;
+    T* dst = (T*)(roleA ? a.dv : a.dk) + koff;
     const float sc = roleA ? 1.0f : a.scale;
 #pragma unroll
     for (int db = 0; db < DB; ++db)
@@ -418,9 +430,10 @@ __global__ __launch_bounds__(256, sizeof(T) == 4 ? 1 : 2) void bwd_dq_kernel(Bwd
     const int q0 = it * BR, qw0 = q0 + wave * 32;
     const size_t bh = (size_t)bhi;
     const size_t hoff = bh * (size_t)N * D;
+    const size_t koff = ((size_t)(bhi / H) * a.Hkv + (bhi % H) / (H / a.Hkv)) * (size_t)N * D;
     const T* __restrict__ Qg = (const T*)a.q + hoff;
-    const T* __restrict__ Kg = (const T*)a.k + hoff;
-    const T* __restrict__ Vg = (const T*)a.v + hoff;
+    const T* __restrict__ Kg = (const T*)a.k + koff;
+    const T* __restrict__ Vg = (const T*)a.v + koff;
     const T* __restrict__ dOg = (const T*)a.dout + hoff;
 
     const int kend = clamp_len(a.mask.key_lens, bhi / H, N);
@@ -550,7 +563,7 @@ hipError_t launch_t(const BwdArgs& a, hipStream_t s) {
     hipError_t e = hipLaunchKernel((const void*)&bwd_pre_kernel<T, D>, dim3((unsigned)((rows + RPB - 1) / RPB)),
                                    dim3(256), args, 0, s);
     if (e != hipSuccess) return e;
-    const int kv_total = ((a.N + BWD_KV_BC - 1) / BWD_KV_BC) * a.H * a.B;
+    const int kv_total = ((a.N + BWD_KV_BC - 1) / BWD_KV_BC) * a.Hkv * a.B;
     const int dq_total = ((a.N + BWD_DQ_BR - 1) / BWD_DQ_BR) * a.H * a.B;
     if (a.ev_begin && (e = hipEventRecord(a.ev_begin, s)) != hipSuccess) return e;
     e = hipLaunchKernel((const void*)&bwd_kv_kernel<T, D, DROP>, dim3((unsigned)(8 * ((kv_total + 7) / 8))),

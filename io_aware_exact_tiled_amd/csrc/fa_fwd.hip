@@ -161,9 +161,13 @@ __global__ __launch_bounds__(256, sizeof(T) == 4 ? 1 : 2) void fwd_kernel(FwdArg
     const int q0 = it * BR, qw0 = q0 + wave * 32;
     const size_t bh = (size_t)bhi;
     const size_t hoff = bh * (size_t)N * D;
+    // K/V head of this query head (grouped-query attention: H / Hkv query
+    // heads share one K/V head)
+    const size_t bkv = (size_t)(bhi / H) * a.Hkv + (bhi % H) / (H / a.Hkv);
+    const size_t koff = bkv * (size_t)N * D;
     const T* __restrict__ Qg = (const T*)a.q + hoff;
-    const T* __restrict__ Kg = (const T*)a.k + hoff;
-    const TV* __restrict__ Vg = (const TV*)a.v + hoff;   // the fp16 copy for bf16 inputs
+    const T* __restrict__ Kg = (const T*)a.k + koff;
+    const TV* __restrict__ Vg = (const TV*)a.v + koff;   // the fp16 copy for bf16 inputs
 
     int kend = N;
     if (a.mask.key_lens) {
@@ -309,7 +313,7 @@ __global__ __launch_bounds__(256, sizeof(T) == 4 ? 1 : 2) void fwd_kernel(FwdArg
     const float l_tot = pair_sum(l_run);
     float inv = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
     if constexpr (DROP) inv *= a.drop.keep_scale;
-    const int vx = a.vexp ? a.vexp[bhi] : 0;
+    const int vx = a.vexp ? a.vexp[bkv] : 0;
     if (qrow < N) {
         const size_t orow = hoff + (size_t)qrow * D;
 #pragma unroll
@@ -367,7 +371,7 @@ hipError_t launch_fwd(FwdArgs a, fa_dtype dt, int d, void* workspace, hipStream_
         p.nch = L.nch;
         p.chunk = L.chunk;
         void* args[] = {(void*)&p};
-        const dim3 grid((unsigned)((size_t)a.B * a.H * L.nch));
+        const dim3 grid((unsigned)((size_t)a.B * a.Hkv * L.nch));
         hipError_t e = hipLaunchKernel((const void*)&v16_absmax_kernel, grid, dim3(256), args, 0, s);
         if (e != hipSuccess) return e;
         e = hipLaunchKernel((const void*)&v16_convert_kernel, grid, dim3(256), args, 0, s);

@@ -55,6 +55,7 @@ struct FwdArgs {
     void* o;
     float* lse;
     int B, H, N;
+    int Hkv;              // K/V heads; query head h reads K/V head h / (H / Hkv)
     float scale_log2;     // scale * log2(e)
     int o_f32;            // O stored as fp32 instead of the input dtype
     MaskArgs mask;
@@ -114,6 +115,7 @@ struct BwdArgs {
     void* dv;
     float* delta;         // fp32 [B][H][N] workspace: D = rowsum(dO o O)
     int B, H, N;
+    int Hkv;              // K/V heads (K, V, dK, dV are [B][Hkv][N][d])
     float scale;
     float scale_log2;
     int o_f32;

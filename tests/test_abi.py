@@ -41,7 +41,7 @@ def test_library_exports_every_declared_symbol():
 
 def test_scalars():
     L = _lib()
-    assert L.fa_abi_version() == 2
+    assert L.fa_abi_version() == 3
     for code in list(lib_mod.STATUS) + [-99]:
         assert isinstance(L.fa_status_string(code), bytes)
     br, bc = ctypes.c_int32(), ctypes.c_int32()
@@ -126,6 +126,25 @@ def test_fwd_workspace_validation():
     assert fwd(L, ws=None) == -8
     assert fwd(L, ws_bytes=need - 1) == -8
     assert fwd(L, ws=P + 16) == -8                  # not 256-byte aligned
+
+
+def test_kv_heads_validation():
+    """Grouped-query attention: kv_heads must divide H; 0 means H; a struct
+    from before the field (struct_size up to kv_heads) is still accepted."""
+    L = _lib()
+    o = lib_mod.FaOpts()
+    o.struct_size = ctypes.sizeof(lib_mod.FaOpts)
+    for bad in (3, 5, 8, -1):
+        o.kv_heads = bad
+        assert fwd(L, H=4, opts=ctypes.byref(o)) == -10, bad
+        assert bwd(L, H=4, opts=ctypes.byref(o)) == -10, bad
+    o.kv_heads = 2
+    assert fwd(L, H=4, d=96, opts=ctypes.byref(o)) == -3     # past the options check
+    o.struct_size = lib_mod.FaOpts.kv_heads.offset            # the previous layout
+    o.kv_heads = 3                                            # not read
+    assert fwd(L, H=4, d=96, opts=ctypes.byref(o)) == -3
+    o.struct_size = lib_mod.FaOpts.kv_heads.offset - 8
+    assert fwd(L, H=4, opts=ctypes.byref(o)) == -10
 
 
 def test_bwd_validation():

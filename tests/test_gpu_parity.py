@@ -78,6 +78,48 @@ def test_edge_matrix(case):
     run_and_check(x, label=str(case))
 
 
+GQA_CASES = [
+    # (H, Hkv, N, d, dtype, causal, key_lens, sparse, dropout)
+    (4, 2, 300, 64, "bf16", True, None, False, 0.0),
+    (6, 1, 257, 128, "bf16", False, "mixed", False, 0.0),
+    (4, 1, 200, 64, "fp16", False, "mixed", False, 0.1),
+    (8, 2, 384, 128, "bf16", True, None, True, 0.0),
+    (4, 2, 130, 128, "fp32", True, None, False, 0.0),
+    (6, 3, 513, 64, "bf16", True, "mixed", False, 0.2),
+]
+
+
+@pytest.mark.parametrize("case", GQA_CASES, ids=lambda c: "H%d-Hkv%d-N%d-d%d-%s-c%d-kl%s-sp%d-p%g" % c)
+def test_grouped_query_matrix(case):
+    """Grouped-query and multi-query attention: K, V (and dK, dV) have Hkv
+    heads; dK, dV are the sums over each group's query heads."""
+    H, hkv, N, d, dtype, causal, kl, sparse, p = case
+    x = W.random_case(2, H, N, d, dtype=dtype, seed=N * 3 + hkv, causal=causal, dropout_p=p,
+                      dropout_seed=N + 5, rng_offset=1 if p else 0,
+                      sparse_density=0.4 if sparse else None, kv_heads=hkv)
+    assert x["k"].shape[1] == hkv
+    if kl == "mixed":
+        x["key_lens"] = torch.tensor([max(N // 3, 1), N], dtype=torch.int32)
+    run_and_check(x, label=str(case))
+
+
+def test_grouped_query_tile_visits():
+    """With grouped K/V heads the dK/dV kernel walks every query head of its
+    group: each query head's visit map is still the exact tile set."""
+    N = 700
+    x = W.random_case(1, 4, N, 64, dtype="bf16", seed=31, causal=True, sparse_density=0.3, kv_heads=1)
+    q, k, v, do = (cuda(x[n]) for n in ("q", "k", "v", "do"))
+    o, lse = fa.fwd(q, k, v, **fa_kw(x))
+    dq, dk, dv, tb = fa.bwd(q, k, v, o, do, lse, record_tiles=True, **fa_kw(x))
+    okw = oracle_kw(x)
+    for pass_, t in ((1, tb[0]), (2, tb[1])):
+        br, bc = fa.tile_shape(64, 2, pass_)
+        want = oracle.expected_tiles(N, br, bc, 1, okw["causal"], okw["key_lens"], okw["block_mask"])
+        got = t.cpu().numpy()
+        for h in range(4):
+            assert np.array_equal(got[:, h], want), f"pass {pass_} head {h}"
+
+
 def test_fully_masked_rows_and_empty_keys():
     x = W.random_case(3, 2, 200, 64, dtype="bf16", seed=5)
     x["key_lens"] = torch.tensor([0, 1, 200], dtype=torch.int32)

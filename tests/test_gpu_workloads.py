@@ -1,9 +1,10 @@
-"""GPU parity at the full sizes of the five workloads, through the C ABI and
+"""GPU parity at the full sizes of the workloads, through the C ABI and
 in the launch configuration bench.py times.  Where the fp64 oracle cannot
 cover every output in seconds (the 16K-token workloads) it checks sampled
 query rows (O, LSE, dQ: each needs only that row's full score row) and, for
-two heads, sampled key rows (dK, dV: each needs the full score column plus
-every row's LSE and D from a chunked fp64 pass)."""
+two K/V heads, sampled key rows (dK, dV: each needs the full score columns
+of every query head that reads that K/V head, plus every row's LSE and D
+from a chunked fp64 pass)."""
 
 import numpy as np
 import pytest
@@ -44,7 +45,7 @@ def test_workload_full_oracle(name):
     print(f"[ok] {name} {res}", flush=True)
 
 
-@pytest.mark.parametrize("name", ["long", "sparse"])
+@pytest.mark.parametrize("name", ["long", "sparse", "gqa"])
 def test_workload_sampled_oracle(name):
     w = W.WORKLOADS[name]
     print(f"[case] {name} sampled", flush=True)
@@ -56,8 +57,11 @@ def test_workload_sampled_oracle(name):
     O, L = oracle.attn_fwd(x["q"], x["k"], x["v"], x["scale"], rows=rows, **okw)
     res = dict(o=check_o(o32[:, :, rows], O, dtype), lse=check_lse(lse[:, :, rows], L, dtype),
                o_stored=check_o(o[:, :, rows], O, dtype, "O(stored)", stored=True))
-    # dQ on the sampled rows of every head; dK, dV on sampled keys of two heads
-    heads = [(0, 0), (0, w.H - 1)]
+    # dQ on the sampled rows of every head; dK, dV on sampled keys of two K/V
+    # heads (summed over the query heads that read them)
+    G = w.H // w.Hkv
+    kvh = [(0, 0), (w.B - 1, w.Hkv - 1)]
+    heads = [(b, g * G + hh) for b, g in kvh for hh in range(G)]
     cols = W.sample_rows(w.N, 128, w.seed + 1)
     Ls, Ds = oracle.attn_stats(x["q"], x["k"], x["v"], x["do"], x["scale"], heads=heads, **okw)
     rq, _, _ = oracle.attn_bwd_rows_cols(x["q"], x["k"], x["v"], x["do"], x["scale"], rows,
@@ -65,8 +69,8 @@ def test_workload_sampled_oracle(name):
     res["dq"] = check_grad(dq[:, :, rows], rq, dtype, "dQ(rows)")
     _, rk, rv = oracle.attn_bwd_rows_cols(x["q"], x["k"], x["v"], x["do"], x["scale"], rows[:1], cols,
                                           Ls, Ds, pairs=heads, **okw)
-    for b, h in heads:
-        res[f"dk{h}"] = check_grad(dk[b:b + 1, h:h + 1, cols], rk[b:b + 1, h:h + 1], dtype, f"dK(h{h})")
-        res[f"dv{h}"] = check_grad(dv[b:b + 1, h:h + 1, cols], rv[b:b + 1, h:h + 1], dtype, f"dV(h{h})")
+    for b, g in kvh:
+        res[f"dk{b}.{g}"] = check_grad(dk[b:b + 1, g:g + 1, cols], rk[b:b + 1, g:g + 1], dtype, f"dK(b{b} g{g})")
+        res[f"dv{b}.{g}"] = check_grad(dv[b:b + 1, g:g + 1, cols], rv[b:b + 1, g:g + 1], dtype, f"dV(b{b} g{g})")
     # the LSE and D the oracle used for the columns are its own, all rows
     print(f"[ok] {name} {res}", flush=True)

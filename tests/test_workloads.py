@@ -45,3 +45,12 @@ def test_key_lengths_and_sparse_mask_recipe():
 def test_sample_rows():
     r = W.sample_rows(16384, 256, 4)
     assert len(r) == 256 and (r[:16] == np.arange(16)).all() and (np.diff(r) > 0).all()
+
+
+def test_grouped_query_shapes():
+    w = W.WORKLOADS["gqa"].with_(B=1, N=64, d=8)
+    x = W.make_inputs(w)
+    assert x["q"].shape == x["do"].shape == (1, 32, 64, 8)
+    assert x["k"].shape == x["v"].shape == (1, 8, 64, 8)
+    # MHA workloads keep their draws: K/V heads default to H
+    assert W.WORKLOADS["tiny"].Hkv == 2

@@ -9,8 +9,9 @@ attention arithmetic.
 Recipe (one ``numpy.random.default_rng(seed)`` PCG64 stream per workload):
 
 1. Q, K, V, dO are drawn in that order as fp64 ``standard_normal`` of shape
-   [B, H, N, d], each multiplied by ``std``, then rounded to the storage dtype
-   with round-to-nearest-even (torch's CPU conversion).
+   [B, H, N, d] (K and V: [B, Hkv, N, d] for grouped-query workloads), each
+   multiplied by ``std``, then rounded to the storage dtype with
+   round-to-nearest-even (torch's CPU conversion).
 2. Then, from the same stream, the key lengths (inclusive uniform integers,
    one per sequence, shared by all heads) if the workload pads keys.
 3. Then the block mask if the workload is block-sparse: a band |i - j| <= 1 of
@@ -18,9 +19,11 @@ Recipe (one ``numpy.random.default_rng(seed)`` PCG64 stream per workload):
    round(density * T^2) tiles are set.
 
 The workload shapes follow the pages' own workloads (GPT-2 small and
-BERT-large attention shapes, a 16K-token long-context case and the
-block-sparse extension of the FlashAttention paper); the seeded Gaussian data
-stands in for the text corpora those models were trained on.
+BERT-large attention shapes, a 16K-token long-context case, the block-sparse
+extension of the FlashAttention paper, and the grouped-query shape of the
+Self-Attention tutorial's MHA / GQA / MQA comparison: 32 query heads, 8 K/V
+heads, head_dim 128, 4096 tokens); the seeded Gaussian data stands in for the
+text corpora those models were trained on.
 """
 
 from __future__ import annotations
@@ -54,6 +57,11 @@ class Workload:
     rng_offset: int = 0
     sparse_density: Optional[float] = None  # block-sparse target density or None
     sample_rows: Optional[int] = None       # rows the oracle checks at full size
+    kv_heads: Optional[int] = None          # K/V heads (grouped-query); None = H
+
+    @property
+    def Hkv(self) -> int:
+        return self.H if self.kv_heads is None else self.kv_heads
 
     @property
     def scale(self) -> float:
@@ -79,6 +87,9 @@ WORKLOADS = {
     # block-sparse, 128x128 tiles, band of 3 + random to density 0.1
     "sparse": Workload("sparse", 1, 8, 16384, 64, "bf16", seed=5,
                        sparse_density=0.1, sample_rows=256),
+    # grouped-query attention: 32 query heads share 8 K/V heads, causal
+    "gqa": Workload("gqa", 4, 32, 4096, 128, "bf16", seed=6, causal=True, kv_heads=8,
+                    sample_rows=256),
 }
 
 
@@ -115,10 +126,10 @@ def make_inputs(w: Workload, dtype: Optional[str] = None, with_do: bool = True) 
     None) and the scalar settings."""
     dtype = dtype or w.dtype
     rng = np.random.default_rng(w.seed)
-    shape = (w.B, w.H, w.N, w.d)
     out = {}
     for name in ("q", "k", "v", "do"):
-        x = rng.standard_normal(shape) * w.std
+        heads = w.Hkv if name in ("k", "v") else w.H
+        x = rng.standard_normal((w.B, heads, w.N, w.d)) * w.std
         out[name] = round_to(x, dtype)
         del x
     key_lens = None
@@ -139,12 +150,12 @@ def make_inputs(w: Workload, dtype: Optional[str] = None, with_do: bool = True) 
 
 def random_case(B, H, N, d, dtype="bf16", seed=0, std=1.0, causal=False,
                 key_len_range=None, dropout_p=0.0, dropout_seed=0, rng_offset=0,
-                sparse_density=None) -> dict:
+                sparse_density=None, kv_heads=None) -> dict:
     """Ad-hoc shape with the same recipe (used for ragged / edge-case tests)."""
     w = Workload("case", B, H, N, d, dtype, seed=seed, std=std, causal=causal,
                  key_len_range=key_len_range, dropout_p=dropout_p,
                  dropout_seed=dropout_seed, rng_offset=rng_offset,
-                 sparse_density=sparse_density)
+                 sparse_density=sparse_density, kv_heads=kv_heads)
     return make_inputs(w)
 
 
