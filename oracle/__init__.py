@@ -22,7 +22,7 @@ One part is only partly pinned and says so: the Philox4x32 multipliers M0, M1
 multipliers come from the SC'11 paper without a known-answer vector here).
 """
 
-from .attention import (attn_fwd, attn_bwd, attn_bwd_rows_cols, attn_stats, kv_head,  # noqa: F401
+from .attention import (attn_fwd, attn_bwd, attn_bwd_rows_cols, attn_stats, kv_head, decode_fwd,  # noqa: F401
                         tiled_fwd, attn_bwd_jacobian, validity, safe_softmax,
                         as_f64, scale_f32)
 from .philox import (philox4x32_10, philox4_scalar, keep_mask,  # noqa: F401

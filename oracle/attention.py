@@ -29,6 +29,11 @@ What it computes is the plain definition that tiled exact attention reaches
       D_i = sum_j P_ij dP_ij,  dS = P * (dP - D),
       dQ = scale dS K,  dK = scale dS^T Q.
 
+* decode (tutorial section 11.2: one new query -- or a few -- against the
+  whole key/value cache): Nq query rows per (b, h) against a cache of Nk
+  rows of which the first len_b are valid; query row i sits at position
+  len_b - Nq + i (the newest tokens), and with the causal mask sees keys
+  j <= that position.  Same softmax, same LSE.
 * grouped-query attention (tutorial section 9.2-9.3, MQA and GQA): K and V
   may have Hkv heads, Hkv dividing H; query head h uses K/V head
   h // (H / Hkv) (contiguous groups -- the pages do not fix the grouping),
@@ -326,3 +331,29 @@ def attn_bwd_jacobian(q, k, v, do, scale, causal=False, key_lens=None,
                 dq[b, h, i] += sc * (ds @ k[b, h])
                 dk[b, h] += sc * np.outer(ds, q[b, h, i])
     return dq, dk, dv
+
+
+def decode_fwd(q, k, v, scale, kv_lens=None, causal=False):
+    """Decode attention.  q [B,H,Nq,d], k and v [B,Hkv,Nk,d] (a cache whose
+    first kv_lens[b] rows are valid; None = Nk).  Returns O [B,H,Nq,d] and
+    LSE [B,H,Nq]; query row i of sequence b is at position kv_lens[b]-Nq+i."""
+    q, k, v = as_f64(q), as_f64(k), as_f64(v)
+    B, H, Nq, d = q.shape
+    Hkv, Nk = k.shape[1], k.shape[2]
+    sc = scale_f32(scale)
+    O = np.zeros((B, H, Nq, v.shape[-1]))
+    LSE = np.zeros((B, H, Nq))
+    j = np.arange(Nk)
+    for b in range(B):
+        L = Nk if kv_lens is None else min(max(int(np.asarray(kv_lens)[b]), 0), Nk)
+        pos = L - Nq + np.arange(Nq)
+        A = np.broadcast_to(j[None, :] < L, (Nq, Nk)).copy()
+        if causal:
+            A &= j[None, :] <= pos[:, None]
+        for h in range(H):
+            g = kv_head(h, H, Hkv)
+            S = sc * (q[b, h] @ k[b, g].T)
+            P, lse, _, _ = safe_softmax(S, A)
+            O[b, h] = P @ v[b, g]
+            LSE[b, h] = lse
+    return O, LSE

@@ -274,6 +274,50 @@ def test_gqa_grouping_and_sampled_variants():
     assert np.allclose(sq, dq[:, :, rows]) and np.allclose(sk, dk[:, :, cols]) and np.allclose(sv, dv[:, :, cols])
 
 
+@pytest.mark.parametrize("causal,hkv", [(False, 4), (True, 2), (True, 1)])
+def test_decode_against_torch_sdpa_fp64(causal, hkv):
+    """Decode: Nq newest query rows against a cache with per-sequence valid
+    lengths, the causal mask aligned to the end of each sequence; against
+    torch CPU fp64 SDPA with the same boolean mask and enable_gqa."""
+    B, H, Nq, Nk, d = 3, 4, 5, 700, 16
+    rng = np.random.default_rng(50 + hkv)
+    q = rng.standard_normal((B, H, Nq, d))
+    k, v = rng.standard_normal((B, hkv, Nk, d)), rng.standard_normal((B, hkv, Nk, d))
+    lens = np.array([700, 3, 411])       # the second sequence is shorter than Nq
+    O, L = oracle.decode_fwd(q, k, v, 0.25, kv_lens=lens, causal=causal)
+    j = torch.arange(Nk)
+    mask = torch.zeros(B, 1, Nq, Nk, dtype=torch.bool)
+    for b in range(B):
+        pos = lens[b] - Nq + torch.arange(Nq)
+        m = (j[None, :] < lens[b]).expand(Nq, Nk)
+        if causal:
+            m = m & (j[None, :] <= pos[:, None])
+        mask[b, 0] = m
+    tq, tk, tv = (torch.tensor(x) for x in (q, k, v))
+    ref = torch.nn.functional.scaled_dot_product_attention(tq, tk, tv, attn_mask=mask, scale=0.25,
+                                                           enable_gqa=hkv != H).numpy()
+    rows = mask[:, 0].any(-1).numpy()                      # SDPA NaNs rows with no valid key
+    for b in range(B):
+        for h in range(H):
+            assert np.allclose(O[b, h][rows[b]], ref[b, h][rows[b]], rtol=0, atol=1e-12)
+            assert (O[b, h][~rows[b]] == 0).all() and np.isneginf(L[b, h][~rows[b]]).all()
+    # empty rows exist only where causal and the sequence is shorter than Nq
+    assert (~rows).any() == causal
+
+
+def test_decode_reduces_to_square_attention():
+    """Nq = Nk = len: the decode rows are all rows, aligned as in square
+    causal attention; one query row with a one-key cache returns that V row."""
+    q, k, v, _ = small_case(B=2, H=2, N=40, d=8, seed=60)
+    for causal in (False, True):
+        O, L = oracle.decode_fwd(q, k, v, 0.3, causal=causal)
+        O2, L2 = oracle.attn_fwd(q, k, v, 0.3, causal=causal)
+        assert np.allclose(O, O2, rtol=0, atol=1e-13) and np.allclose(L, L2, rtol=0, atol=1e-13)
+    O, L = oracle.decode_fwd(q[:, :, :1], k, v, 0.3, kv_lens=np.array([1, 1]), causal=True)
+    assert np.allclose(O[:, :, 0], v[:, :, 0])
+    assert np.allclose(L[:, :, 0], float(np.float32(0.3)) * (q[:, :, 0] * k[:, :, 0]).sum(-1), rtol=0, atol=1e-12)
+
+
 # ---------------------------------------------------------------- gradients
 
 def _loss(q, k, v, do, scale, kw):
