@@ -165,6 +165,27 @@ fa_status fa_bwd(const void* Q, const void* K, const void* V, const void* O,
                  const uint8_t* block_mask, const fa_opts* opts,
                  void* workspace, size_t workspace_bytes, hipStream_t stream);
 
+/* Decode attention over a key/value cache (Self-Attention tutorial, section
+ * 11.2: the decode phase, one new token -- or a few -- per step against the
+ * whole cache).  Q: [B][H][Nq][d]; K, V: [B][Hkv][Nk][d], a cache of which
+ * the first kv_lens[b] rows are valid (device int32[B], clamped to [0, Nk];
+ * NULL = Nk); Hkv divides H and query head h reads K/V head h / (H / Hkv).
+ * Query row i of sequence b stands for position kv_lens[b] - Nq + i; with
+ * `causal` it sees keys j <= that position, else all valid keys.  O:
+ * [B][H][Nq][d] of `dtype`; LSE: float [B][H][Nq] (natural log, scaled
+ * scores; -inf and O = 0 for a row without valid keys).  dtype: FA_BF16 or
+ * FA_F16.  No dropout, no block mask, no backward.  Supported: d in {64, 128},
+ * (H / Hkv) * Nq <= 65535, Nk * d < 2^31.  The cache is cut into chunks read
+ * by separate workgroups whose softmax partials are merged (the two-block
+ * rule of the summary's incremental softmax); workspace: device memory of at
+ * least fa_decode_workspace_bytes(...) bytes, 256-byte aligned, holding those
+ * partials. */
+size_t fa_decode_workspace_bytes(int32_t B, int32_t H, int32_t Hkv, int32_t Nq, int32_t Nk, int32_t d);
+fa_status fa_decode(const void* Q, const void* K, const void* V, void* O, float* LSE,
+                    int32_t B, int32_t H, int32_t Hkv, int32_t Nq, int32_t Nk, int32_t d,
+                    fa_dtype dtype, float scale, int32_t causal, const int32_t* kv_lens,
+                    void* workspace, size_t workspace_bytes, hipStream_t stream);
+
 /* Dropout keep bits of every element, for tests: keep is device
  * uint8[B][H][N][N], 1 = kept.  Uses the same device generator as the
  * attention kernels.  O(N^2) memory: test sizes only. */

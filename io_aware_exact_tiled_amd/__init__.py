@@ -21,8 +21,8 @@ import torch
 from . import _lib
 from ._lib import FaOpts, check
 
-__all__ = ["fwd", "bwd", "dropout_keep_mask", "tile_shape", "fwd_workspace_bytes", "bwd_workspace_bytes",
-           "abi_version"]
+__all__ = ["fwd", "bwd", "decode", "dropout_keep_mask", "tile_shape", "fwd_workspace_bytes",
+           "bwd_workspace_bytes", "decode_workspace_bytes", "abi_version"]
 
 _DT = {torch.float32: _lib.FA_F32, torch.float16: _lib.FA_F16, torch.bfloat16: _lib.FA_BF16}
 
@@ -174,6 +174,38 @@ def bwd(q, k, v, o, do, lse, *, causal=False, dropout_p=0.0, seed=0, rng_offset=
     check(code, "fa_bwd")
     del keep, bm
     return (dq, dk, dv, tiles) if record_tiles else (dq, dk, dv)
+
+
+def decode_workspace_bytes(B, H, Hkv, Nq, Nk, d) -> int:
+    return int(_lib.lib().fa_decode_workspace_bytes(B, H, Hkv, Nq, Nk, d))
+
+
+def decode(q, k, v, *, kv_lens=None, causal=False, scale: Optional[float] = None, out=None, lse=None,
+           workspace=None):
+    """Decode attention: q [B, H, Nq, d] (the newest Nq tokens) against a
+    key/value cache k, v [B, Hkv, Nk, d] whose first kv_lens[b] rows are valid
+    (all Nk when None).  Returns (O [B, H, Nq, d], LSE [B, H, Nq])."""
+    if q.dim() != 4 or k.dim() != 4 or k.shape != v.shape:
+        raise ValueError("q [B, H, Nq, d], k and v [B, Hkv, Nk, d]")
+    for t in (q, k, v):
+        if not t.is_cuda or not t.is_contiguous() or t.dtype != q.dtype or t.device != q.device:
+            raise ValueError("q, k, v must be contiguous GPU tensors of one dtype and device")
+    B, H, Nq, d = q.shape
+    Hkv, Nk = k.shape[1], k.shape[2]
+    if k.shape[0] != B or k.shape[3] != d:
+        raise ValueError("k, v must share q's B and d")
+    scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    o = out if out is not None else torch.empty_like(q)
+    l = lse if lse is not None else torch.empty((B, H, Nq), dtype=torch.float32, device=q.device)
+    need = decode_workspace_bytes(B, H, Hkv, Nq, Nk, d)
+    ws = workspace if workspace is not None else torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    kl = None if kv_lens is None else kv_lens.to(device=q.device, dtype=torch.int32).contiguous()
+    code = _lib.lib().fa_decode(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), l.data_ptr(), B, H, Hkv,
+                                Nq, Nk, d, _dtype_code(q), scale, 1 if causal else 0,
+                                None if kl is None else kl.data_ptr(), ws.data_ptr(), ws.numel(), _stream(q.device))
+    check(code, "fa_decode")
+    del kl, ws
+    return o, l
 
 
 def dropout_keep_mask(seed, rng_offset, p, B, H, N, device="cuda"):

@@ -158,6 +158,49 @@ fa_status fa_fwd(const void* Q, const void* K, const void* V, void* O, float* LS
     return e == hipSuccess ? FA_OK : hip_fail(e);
 }
 
+namespace {
+fa_status check_decode(int32_t B, int32_t H, int32_t Hkv, int32_t Nq, int32_t Nk, int32_t d) {
+    if (d != 64 && d != 128) return FA_ERR_HEAD_DIM;
+    if (B < 1 || H < 1 || Hkv < 1 || Nq < 1 || Nk < 1 || B > 65535 || H > 65535 || H % Hkv) return FA_ERR_SHAPE;
+    if ((int64_t)Nk * d >= (int64_t(1) << 31) || (int64_t)B * H * Nq >= (int64_t(1) << 31) ||
+        (int64_t)B * Hkv * Nk >= (int64_t(1) << 31) || (int64_t)(H / Hkv) * Nq > 65535)
+        return FA_ERR_SHAPE;
+    return FA_OK;
+}
+}  // namespace
+
+size_t fa_decode_workspace_bytes(int32_t B, int32_t H, int32_t Hkv, int32_t Nq, int32_t Nk, int32_t d) {
+    if (check_decode(B, H, Hkv, Nq, Nk, d) != FA_OK) return 0;
+    return fa::decode_workspace_bytes(B, H, Hkv, Nq, Nk, d);
+}
+
+fa_status fa_decode(const void* Q, const void* K, const void* V, void* O, float* LSE, int32_t B, int32_t H,
+                    int32_t Hkv, int32_t Nq, int32_t Nk, int32_t d, fa_dtype dtype, float scale, int32_t causal,
+                    const int32_t* kv_lens, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+    if (!Q || !K || !V || !O || !LSE) return FA_ERR_NULL;
+    fa_status st = check_decode(B, H, Hkv, Nq, Nk, d);
+    if (st != FA_OK) return st;
+    if (dtype != FA_BF16 && dtype != FA_F16) return FA_ERR_DTYPE;
+    if (!std::isfinite(scale) || scale <= 0.0f) return FA_ERR_SCALE;
+    if (!aligned16(Q) || !aligned16(K) || !aligned16(V) || !aligned16(O) || !aligned16(LSE)) return FA_ERR_ALIGN;
+    const size_t need = fa::decode_workspace_bytes(B, H, Hkv, Nq, Nk, d);
+    if (!workspace || workspace_bytes < need || (reinterpret_cast<uintptr_t>(workspace) & 255u))
+        return FA_ERR_WORKSPACE;
+    const fa::DecodeSplit sp = fa::decode_split(B, H, Hkv, Nq, Nk);
+    fa::DecodeArgs a;
+    a.q = Q; a.k = K; a.v = V; a.o = O; a.lse = LSE;
+    const size_t rows = (size_t)B * H * Nq;
+    a.opart = static_cast<float*>(workspace);
+    a.lpart = reinterpret_cast<float*>(static_cast<char*>(workspace) + fa::align256(rows * sp.S * d * 4));
+    a.kv_lens = kv_lens;
+    a.B = B; a.H = H; a.Hkv = Hkv; a.Nq = Nq; a.Nk = Nk;
+    a.S = sp.S; a.C = sp.C; a.QBn = sp.QBn;
+    a.causal = causal ? 1 : 0;
+    a.scale_log2 = scale * LOG2E;
+    const hipError_t e = fa::launch_decode(a, dtype, d, stream);
+    return e == hipSuccess ? FA_OK : hip_fail(e);
+}
+
 size_t fa_bwd_workspace_bytes(int32_t B, int32_t H, int32_t N, int32_t d) {
     if (check_shape(B, H, N, d) != FA_OK) return 0;
     const size_t rows = (size_t)B * H * N;

@@ -127,6 +127,41 @@ struct BwdArgs {
     hipEvent_t ev_mid;             // optional: between the two main kernels
 };
 
+// Decode (split key/value cache): see fa_decode.hip.
+struct DecodeArgs {
+    const void* q;        // [B][H][Nq][d]
+    const void* k;        // [B][Hkv][Nk][d]
+    const void* v;
+    void* o;              // [B][H][Nq][d]
+    float* lse;           // [B][H][Nq]
+    float* opart;         // workspace [B*H*Nq][S][d]: per-split O
+    float* lpart;         // workspace [B*H*Nq][S]: per-split log2-sum-exp
+    const int32_t* kv_lens;   // device [B] valid cache rows, or null (= Nk)
+    int B, H, Hkv, Nq, Nk;
+    int S, C, QBn;        // splits, cache rows per split, 32-row query blocks per K/V head
+    int causal;
+    float scale_log2;
+};
+constexpr int DECODE_TARGET_WGS = 2048;   // workgroups the split count aims for
+struct DecodeSplit { int S, C, QBn; };
+inline DecodeSplit decode_split(int B, int H, int Hkv, int Nq, int Nk) {
+    DecodeSplit p;
+    p.QBn = ((H / Hkv) * Nq + 31) / 32;
+    const long base = (long)B * Hkv * p.QBn;
+    long want = (DECODE_TARGET_WGS + base - 1) / base;
+    const long maxs = (Nk + 127) / 128;
+    want = want < 1 ? 1 : (want > maxs ? maxs : want);
+    p.C = (int)((((long)Nk + want - 1) / want + 127) / 128 * 128);
+    p.S = (Nk + p.C - 1) / p.C;
+    return p;
+}
+inline size_t decode_workspace_bytes(int B, int H, int Hkv, int Nq, int Nk, int d) {
+    const DecodeSplit p = decode_split(B, H, Hkv, Nq, Nk);
+    const size_t rows = (size_t)B * H * Nq;
+    return align256(rows * p.S * d * 4) + align256(rows * p.S * 4);
+}
+hipError_t launch_decode(const DecodeArgs& a, fa_dtype dt, int d, hipStream_t s);
+
 hipError_t launch_fwd(FwdArgs a, fa_dtype dt, int d, void* workspace, hipStream_t s);
 hipError_t launch_bwd(const BwdArgs& a, fa_dtype dt, int d, hipStream_t s);
 hipError_t launch_keep_mask(uint32_t k0, uint32_t k1, uint32_t off, uint32_t thr,

@@ -168,3 +168,26 @@ def test_keep_mask_validation():
     assert L.fa_dropout_keep_mask(0, 0, 0.1, 1, 1, 8, None, None) == -1
     assert L.fa_dropout_keep_mask(0, 0, 1.5, 1, 1, 8, P, None) == -5
     assert L.fa_dropout_keep_mask(0, 0, 0.1, 0, 1, 8, P, None) == -2
+
+
+def test_decode_validation_and_workspace():
+    L = _lib()
+
+    def dec(B=1, H=4, Hkv=2, Nq=1, Nk=100, d=64, dt=2, scale=0.125, ws=P, ws_bytes=1 << 24, ptrs=None):
+        ptrs = ptrs or [P] * 5
+        return L.fa_decode(*ptrs, B, H, Hkv, Nq, Nk, d, dt, scale, 0, None, ws, ws_bytes, None)
+
+    assert dec(Hkv=3) == -2                  # must divide H
+    assert dec(Hkv=0) == -2 and dec(Nq=0) == -2 and dec(Nk=0) == -2
+    assert dec(d=80) == -3
+    assert dec(dt=0) == -4                   # fp32 decode is not provided
+    assert dec(scale=0.0) == -6
+    assert dec(ptrs=[P, P, None, P, P]) == -1
+    assert dec(ptrs=[P, P, P, P + 4, P]) == -7
+    need = L.fa_decode_workspace_bytes(1, 4, 2, 1, 100, 64)
+    assert need > 0 and need % 256 == 0
+    assert dec(ws=None) == -8 and dec(ws_bytes=need - 1) == -8 and dec(ws=P + 16) == -8
+    assert L.fa_decode_workspace_bytes(1, 4, 3, 1, 100, 64) == 0
+    # per-split partials: O (fp32 x d) and one log-sum-exp per query row and split
+    big = L.fa_decode_workspace_bytes(16, 32, 8, 1, 16384, 128)
+    assert big >= 16 * 32 * 1 * (128 * 4 + 4)

@@ -120,6 +120,38 @@ def test_grouped_query_tile_visits():
             assert np.array_equal(got[:, h], want), f"pass {pass_} head {h}"
 
 
+DECODE_CASES = [
+    # (B, H, Hkv, Nq, Nk, d, dtype, causal, kv_lens)
+    (2, 4, 4, 1, 1000, 128, "bf16", False, None),
+    (3, 8, 2, 1, 3000, 128, "bf16", True, (3000, 1, 777)),
+    (2, 8, 1, 4, 700, 64, "fp16", True, (700, 3)),
+    (2, 6, 3, 16, 513, 64, "bf16", True, (513, 100)),
+    (1, 16, 2, 8, 900, 128, "fp16", True, None),
+    (2, 4, 1, 2, 4097, 64, "bf16", False, (4097, 2048)),
+]
+
+
+@pytest.mark.parametrize("case", DECODE_CASES, ids=lambda c: "B%d-H%d-Hkv%d-Nq%d-Nk%d-d%d-%s-c%d-%s" % (
+    c[:8] + ("kl" if c[8] else "full",)))
+def test_decode_matrix(case):
+    """Decode over a key/value cache: split chunks merged on the device, against
+    the fp64 oracle; rows with no valid key (cache shorter than Nq under the
+    causal mask) give O = 0 and LSE = -inf."""
+    B, H, hkv, nq, nk, d, dtype, causal, lens = case
+    print(f"[case] decode {case}", flush=True)
+    rng = np.random.default_rng(nk + nq + hkv)
+    dt = DT[dtype]
+    q = torch.from_numpy(rng.standard_normal((B, H, nq, d))).to(dt)
+    k = torch.from_numpy(rng.standard_normal((B, hkv, nk, d))).to(dt)
+    v = torch.from_numpy(rng.standard_normal((B, hkv, nk, d))).to(dt)
+    kl = None if lens is None else torch.tensor(lens, dtype=torch.int32)
+    o, lse = fa.decode(cuda(q), cuda(k), cuda(v), kv_lens=cuda(kl), causal=causal)
+    torch.cuda.synchronize()
+    O, L = oracle.decode_fwd(q, k, v, 1.0 / np.sqrt(d), kv_lens=None if kl is None else kl.numpy(), causal=causal)
+    res = dict(o=check_o(o, O, dt, "O(stored)", stored=True), lse=check_lse(lse, L, dt))
+    print(f"[ok] decode {case} {res}", flush=True)
+
+
 def test_fully_masked_rows_and_empty_keys():
     x = W.random_case(3, 2, 200, 64, dtype="bf16", seed=5)
     x["key_lens"] = torch.tensor([0, 1, 200], dtype=torch.int32)
