@@ -2,6 +2,7 @@
 """Throughput of tiled exact attention (forward + backward) on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload long]
+    python bench.py --workload decode     # decode over a key/value cache, GB/s
 
 A step is one full pass of the hot path on one batch: the forward (for bf16
 the V pre-pass, then the forward kernel: O, LSE) followed by the backward
@@ -41,7 +42,8 @@ HBM_GBPS = 8000.0
 ROOT = os.path.dirname(os.path.abspath(__file__))
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.json")
 CSRC = os.path.join(ROOT, "io_aware_exact_tiled_amd", "csrc")
-KERNEL_SOURCES = {"fwd_kernel": "fa_fwd.hip", "bwd_kv_kernel": "fa_bwd.hip", "bwd_dq_kernel": "fa_bwd.hip"}
+KERNEL_SOURCES = {"fwd_kernel": "fa_fwd.hip", "bwd_kv_kernel": "fa_bwd.hip", "bwd_dq_kernel": "fa_bwd.hip",
+                  "decode_split_kernel": "fa_decode.hip"}
 
 
 def kernel_sources_sha256(kernel: str) -> str:
@@ -201,6 +203,111 @@ def time_workload(w, steps, warmup, ev):
                 step_ms=step_ms, fwd_pass_ms=fwd_pass_ms, bwd_pass_ms=bwd_pass_ms)
 
 
+def decode_bytes(x, w):
+    """Algorithmic HBM bytes of one decode call, split by kernel: the chunk
+    kernel must read Q and the valid cache rows of K and V (sum over b of
+    kv_lens[b] rows per K/V head); the merge kernel must write O and LSE.  The
+    chunk partials it also writes and the merge reads back are not counted."""
+    el = 2
+    L = np.full(w.B, w.N) if x["key_lens"] is None else np.clip(x["key_lens"].numpy().astype(np.int64), 0, w.N)
+    kv = int(L.sum()) * w.Hkv * w.d * el * 2
+    q = w.B * w.H * w.decode_q * w.d * el
+    o = q + w.B * w.H * w.decode_q * 4
+    return kv + q, o
+
+
+def time_decode(w, steps, warmup, ev):
+    import torch
+    import io_aware_exact_tiled_amd as fa
+    import workloads as W
+
+    x = W.make_inputs(w, with_do=False)
+    dev = torch.device("cuda:0")
+    q, k, v = (x[n].to(dev) for n in ("q", "k", "v"))
+    kl = None if x["key_lens"] is None else x["key_lens"].to(dev)
+    o = torch.empty_like(q)
+    lse = torch.empty(w.B, w.H, w.decode_q, dtype=torch.float32, device=dev)
+    ws = torch.empty(fa.decode_workspace_bytes(w.B, w.H, w.Hkv, w.decode_q, w.N, w.d), dtype=torch.uint8,
+                     device=dev)
+    evs = [[ev.create() for _ in range(3)] for _ in range(steps)]
+
+    def step(i=None):
+        fa.decode(q, k, v, kv_lens=kl, causal=w.causal, scale=w.scale, out=o, lse=lse, workspace=ws,
+                  events=None if i is None else evs[i])
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        step(i)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    split_ms = [ev.ms(e[0], e[1]) for e in evs]
+    merge_ms = [ev.ms(e[1], e[2]) for e in evs]
+    call_ms = [ev.ms(e[0], e[2]) for e in evs]
+    for e in evs:
+        for h in e:
+            ev.destroy(h)
+    return dict(x=x, wall_s=wall, split_ms=split_ms, merge_ms=merge_ms, call_ms=call_ms)
+
+
+def decode_report(w, args, ev):
+    """One JSON line for a decode workload: memory-bound, so HBM GB/s of
+    algorithmic bytes against the 8 TB/s peak."""
+    r = time_decode(w, args.steps, args.warmup, ev)
+    rd, wr = decode_bytes(r["x"], w)
+    med = lambda a: float(np.median(a))
+    call_ms = med(r["call_ms"])
+    split_avg = float(np.mean(r["split_ms"]))
+    gbps = (rd + wr) / (call_ms * 1e-3) / 1e9
+    achieved = rd / (split_avg * 1e-3) / 1e9
+    out = {
+        "metric": "decode attention HBM GB/s (algorithmic bytes: valid K/V cache rows, Q, O, LSE)",
+        "value": round(gbps, 1),
+        "unit": "GB/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(call_ms, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic (seeded Gaussian Q and K/V cache, uniform valid lengths)",
+        "config": {"workload": f"{w.name}: B={w.B} H={w.H} Hkv={w.Hkv} Nq={w.decode_q} Nk={w.N} d={w.d} "
+                               f"{w.dtype}{' causal' if w.causal else ''} kv_lens U{list(w.key_len_range)}",
+                   "B": w.B, "H": w.H, "Hkv": w.Hkv, "Nq": w.decode_q, "Nk": w.N, "d": w.d,
+                   "bytes_per_call": rd + wr},
+        "split_ms": round(med(r["split_ms"]), 5), "merge_ms": round(med(r["merge_ms"]), 5),
+        "roofline": {"bound": "hbm", "kernel": "decode_split_kernel", "achieved": round(achieved, 1),
+                     "peak": HBM_GBPS, "unit": "GB/s", "frac": round(achieved / HBM_GBPS, 4),
+                     "traffic": measured_traffic("decode_split_kernel", w.name),
+                     "avg_launch_ms": round(split_avg, 5), "bytes_per_launch": rd},
+        "wall_s": round(r["wall_s"], 3),
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline_decode(w, rd + wr)
+    print(json.dumps(out), flush=True)
+
+
+def cpu_baseline_decode(w, bytes_per_call):
+    """The fp64 oracle (untuned) on the whole decode workload, scaled to the
+    same algorithmic bytes as the GPU figure."""
+    import oracle
+    import workloads as W
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        threads = os.cpu_count()
+    x = W.make_inputs(w, with_do=False)
+    kl = None if x["key_lens"] is None else x["key_lens"].numpy()
+    t0 = time.perf_counter()
+    oracle.decode_fwd(x["q"], x["k"], x["v"], w.scale, kv_lens=kl, causal=w.causal)
+    dt = time.perf_counter() - t0
+    return {"value": round(bytes_per_call / dt / 1e9, 3), "unit": "GB/s", "cores": int(threads), "kind": "oracle",
+            "seconds": round(dt, 2),
+            "sample": f"fp64 numpy oracle decode over the whole workload ({w.B} sequences x {w.H} heads), "
+                      f"rated by the same bf16 algorithmic bytes"}
+
+
 def cpu_baseline(w, rows):
     """The fp64 oracle (untuned) on a bounded sample of the same workload: the
     leading `rows` query rows of every head.  For causal attention those rows
@@ -252,6 +359,9 @@ def main():
         torch.cuda.synchronize()
         del src, dst
     w = W.WORKLOADS[args.workload]
+    if w.decode_q is not None:
+        decode_report(w, args, ev)
+        return
     r = time_workload(w, args.steps, args.warmup, ev)
     fwd_flop = 4.0 * w.d * r["pairs"]
     bwd_flop = 10.0 * w.d * r["pairs"]

@@ -62,7 +62,7 @@
 extern "C" {
 #endif
 
-#define FA_ABI_VERSION 3
+#define FA_ABI_VERSION 4
 
 typedef enum { FA_F32 = 0, FA_F16 = 1, FA_BF16 = 2 } fa_dtype;
 
@@ -179,12 +179,15 @@ fa_status fa_bwd(const void* Q, const void* K, const void* V, const void* O,
  * by separate workgroups whose softmax partials are merged (the two-block
  * rule of the summary's incremental softmax); workspace: device memory of at
  * least fa_decode_workspace_bytes(...) bytes, 256-byte aligned, holding those
- * partials. */
+ * partials.  events: NULL, or three events recorded on `stream` before the
+ * chunk kernel, between it and the merge kernel, and after the merge (for
+ * timing; the caller creates and owns them). */
 size_t fa_decode_workspace_bytes(int32_t B, int32_t H, int32_t Hkv, int32_t Nq, int32_t Nk, int32_t d);
 fa_status fa_decode(const void* Q, const void* K, const void* V, void* O, float* LSE,
                     int32_t B, int32_t H, int32_t Hkv, int32_t Nq, int32_t Nk, int32_t d,
                     fa_dtype dtype, float scale, int32_t causal, const int32_t* kv_lens,
-                    void* workspace, size_t workspace_bytes, hipStream_t stream);
+                    const hipEvent_t* events, void* workspace, size_t workspace_bytes,
+                    hipStream_t stream);
 
 /* Dropout keep bits of every element, for tests: keep is device
  * uint8[B][H][N][N], 1 = kept.  Uses the same device generator as the

@@ -181,10 +181,12 @@ def decode_workspace_bytes(B, H, Hkv, Nq, Nk, d) -> int:
 
 
 def decode(q, k, v, *, kv_lens=None, causal=False, scale: Optional[float] = None, out=None, lse=None,
-           workspace=None):
+           workspace=None, events=None):
     """Decode attention: q [B, H, Nq, d] (the newest Nq tokens) against a
     key/value cache k, v [B, Hkv, Nk, d] whose first kv_lens[b] rows are valid
-    (all Nk when None).  Returns (O [B, H, Nq, d], LSE [B, H, Nq])."""
+    (all Nk when None).  Returns (O [B, H, Nq, d], LSE [B, H, Nq]).  events:
+    None or three hipEvent_t handles recorded around the chunk and merge
+    kernels."""
     if q.dim() != 4 or k.dim() != 4 or k.shape != v.shape:
         raise ValueError("q [B, H, Nq, d], k and v [B, Hkv, Nk, d]")
     for t in (q, k, v):
@@ -200,9 +202,15 @@ def decode(q, k, v, *, kv_lens=None, causal=False, scale: Optional[float] = None
     need = decode_workspace_bytes(B, H, Hkv, Nq, Nk, d)
     ws = workspace if workspace is not None else torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
     kl = None if kv_lens is None else kv_lens.to(device=q.device, dtype=torch.int32).contiguous()
+    ev = None
+    if events is not None:
+        if len(events) != 3:
+            raise ValueError("events: three hipEvent_t handles")
+        ev = (ctypes.c_void_p * 3)(*events)
     code = _lib.lib().fa_decode(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), l.data_ptr(), B, H, Hkv,
                                 Nq, Nk, d, _dtype_code(q), scale, 1 if causal else 0,
-                                None if kl is None else kl.data_ptr(), ws.data_ptr(), ws.numel(), _stream(q.device))
+                                None if kl is None else kl.data_ptr(), ev, ws.data_ptr(), ws.numel(),
+                                _stream(q.device))
     check(code, "fa_decode")
     del kl, ws
     return o, l

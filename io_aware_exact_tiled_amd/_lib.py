@@ -72,7 +72,7 @@ def lib():
         L.fa_bwd.restype = i32
         L.fa_bwd_workspace_bytes.argtypes = [i32, i32, i32, i32]
         L.fa_bwd_workspace_bytes.restype = sz
-        L.fa_decode.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32, f32, i32, vp, vp, sz, vp]
+        L.fa_decode.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32, f32, i32, vp, vp, vp, sz, vp]
         L.fa_decode.restype = i32
         L.fa_decode_workspace_bytes.argtypes = [i32, i32, i32, i32, i32, i32]
         L.fa_decode_workspace_bytes.restype = sz

@@ -176,7 +176,8 @@ size_t fa_decode_workspace_bytes(int32_t B, int32_t H, int32_t Hkv, int32_t Nq, 
 
 fa_status fa_decode(const void* Q, const void* K, const void* V, void* O, float* LSE, int32_t B, int32_t H,
                     int32_t Hkv, int32_t Nq, int32_t Nk, int32_t d, fa_dtype dtype, float scale, int32_t causal,
-                    const int32_t* kv_lens, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+                    const int32_t* kv_lens, const hipEvent_t* events, void* workspace, size_t workspace_bytes,
+                    hipStream_t stream) {
     if (!Q || !K || !V || !O || !LSE) return FA_ERR_NULL;
     fa_status st = check_decode(B, H, Hkv, Nq, Nk, d);
     if (st != FA_OK) return st;
@@ -197,7 +198,7 @@ fa_status fa_decode(const void* Q, const void* K, const void* V, void* O, float*
     a.S = sp.S; a.C = sp.C; a.QBn = sp.QBn;
     a.causal = causal ? 1 : 0;
     a.scale_log2 = scale * LOG2E;
-    const hipError_t e = fa::launch_decode(a, dtype, d, stream);
+    const hipError_t e = fa::launch_decode(a, dtype, d, events, stream);
     return e == hipSuccess ? FA_OK : hip_fail(e);
 }
 

@@ -9,7 +9,10 @@
 // incremental softmax: m = max(m1, m2), l = e^{m1-m} l1 + e^{m2-m} l2).
 //
 // decode_split_kernel: one workgroup per (sequence b, K/V head g, block of 32
-//   query rows, chunk of C cache rows).  The 32 rows are those of the G = H/Hkv
+//   query rows, chunk s of the sequence's valid rows).  The S chunks split the
+//   len_b valid rows evenly (32-row multiples), so the workgroups of a
+//   sequence read equal amounts; rows at or past len_b are never read, so the
+//   cache past them may hold anything.  The 32 rows are those of the G = H/Hkv
 //   query heads that read head g, times the Nq decode rows (row r = hh*Nq + i,
 //   query head g*G + hh, decode row i; rows past G*Nq are padding), so every
 //   byte of K and V is read once for the whole group.  Four waves take the
@@ -68,8 +71,9 @@ __global__ __launch_bounds__(256, 2) void decode_split_kernel(DecodeArgs a) {
         const int x = a.kv_lens[b];
         L = x < 0 ? 0 : (x > Nk ? Nk : x);
     }
-    const int c0 = s * a.C;
-    const int c1 = min(c0 + a.C, L);
+    const int Cb = ((L + a.S - 1) / a.S + 31) & ~31;  // rows per chunk of this sequence
+    const int c0 = min(s * Cb, L);
+    const int c1 = min(c0 + Cb, L);
     const size_t koff = ((size_t)b * a.Hkv + g) * (size_t)Nk * D;
     const T* __restrict__ Kg = (const T*)a.k + koff;
     const T* __restrict__ Vg = (const T*)a.v + koff;
@@ -101,11 +105,12 @@ __global__ __launch_bounds__(256, 2) void decode_split_kernel(DecodeArgs a) {
     typename MM::frag kf[2][KS];
     auto load_k = [&](int n, int slot) {
         int row = kt_of(n) + ln;
-        row = row < Nk ? row : Nk - 1;                 // masked below as a key >= L
+        row = row < c1 ? row : c1 - 1;                 // masked below as a key >= c1
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) kf[slot][ks] = load_frag<T>(Kg + (size_t)row * D + ks * 2 * E + hl * E);
     };
-    auto load_v = [&](int n, int slot) { dma_rows<T, 32, D, 1>(vbuf + slot * TT, Vg, kt_of(n), Nk, 0, lane); };
+    // rows at or past c1 arrive as zeros (the descriptor ends there)
+    auto load_v = [&](int n, int slot) { dma_rows<T, 32, D, 1>(vbuf + slot * TT, Vg, kt_of(n), c1, 0, lane); };
 
     if (nmine > 0) {
         load_k(0, 0);
@@ -236,28 +241,52 @@ __global__ __launch_bounds__(256, 2) void decode_split_kernel(DecodeArgs a) {
 
 template <class T, int D>
 __global__ __launch_bounds__(256) void decode_merge_kernel(DecodeArgs a) {
-    // one wave per query row; each lane owns D/64 columns
+    // one wave per query row; each lane owns D/64 columns.  The splits' lse2
+    // values are read 64 at a time (one per lane) and their weights handed to
+    // every lane with readlane, so that the partial-O loads of a batch of
+    // splits are independent and in flight together.
     constexpr int CPL = D / 64;
+    constexpr int U = 8;                               // partial rows per batch
     const int lane = threadIdx.x & 63;
     const size_t row = (size_t)blockIdx.x * 4 + (threadIdx.x >> 6);
     const size_t rows = (size_t)a.B * a.H * a.Nq;
     if (row >= rows) return;
-    const float* lp = a.lpart + row * a.S;
+    const int S = a.S;
+    const float* lp = a.lpart + row * S;
+    const float* op = a.opart + row * S * D + lane * CPL;
     float M = -INFINITY;
-    for (int s = 0; s < a.S; ++s) M = fmaxf(M, lp[s]);
+    for (int s0 = 0; s0 < S; s0 += 64)
+        if (s0 + lane < S) M = fmaxf(M, lp[s0 + lane]);
+#pragma unroll
+    for (int x = 32; x >= 1; x >>= 1) M = fmaxf(M, __shfl_xor(M, x));
     float acc[CPL], wsum = 0.0f;
 #pragma unroll
-    for (int j = 0; j < CPL; ++j) acc[j] = 0.0f;
+    for (int c = 0; c < CPL; ++c) acc[c] = 0.0f;
     if (M != -INFINITY) {
-        for (int s = 0; s < a.S; ++s) {
-            const float ls = lp[s];
-            if (ls == -INFINITY) continue;             // no valid key in this split
-            const float w = fast_exp2(ls - M);
-            wsum += w;
-            const float* op = a.opart + (row * a.S + s) * D + lane * CPL;
+        for (int s0 = 0; s0 < S; s0 += 64) {
+            const float ls = s0 + lane < S ? lp[s0 + lane] : -INFINITY;
+            const float wl = fast_exp2(ls - M);        // 0 for a split without valid keys
+            wsum += wl;
+            const int n = min(64, S - s0);
+            for (int j = 0; j < n; j += U) {
+                float w[U], v[U][CPL];
 #pragma unroll
-            for (int j = 0; j < CPL; ++j) acc[j] += w * op[j];
+                for (int u = 0; u < U; ++u) {
+                    const int k = j + u < n ? j + u : n - 1;
+                    const float wk = __builtin_bit_cast(
+                        float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, wl), k));
+                    w[u] = j + u < n ? wk : 0.0f;
+#pragma unroll
+                    for (int c = 0; c < CPL; ++c) v[u][c] = op[(size_t)(s0 + k) * D + c];
+                }
+#pragma unroll
+                for (int u = 0; u < U; ++u)
+#pragma unroll
+                    for (int c = 0; c < CPL; ++c) acc[c] = fmaf(w[u], v[u][c], acc[c]);
+            }
         }
+#pragma unroll
+        for (int x = 32; x >= 1; x >>= 1) wsum += __shfl_xor(wsum, x);
     }
     const float inv = wsum > 0.0f ? 1.0f / wsum : 0.0f;
     T* o = (T*)a.o + row * D + lane * CPL;
@@ -273,22 +302,26 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(DecodeArgs a) {
 
 namespace {
 template <class T, int D>
-hipError_t launch_t(const DecodeArgs& a, hipStream_t st) {
+hipError_t launch_t(const DecodeArgs& a, const hipEvent_t* ev, hipStream_t st) {
     DecodeArgs copy = a;
     void* args[] = {(void*)&copy};
     const size_t nsplit = (size_t)a.B * a.Hkv * a.QBn * a.S;
-    hipError_t e = hipLaunchKernel((const void*)&decode_split_kernel<T, D>, dim3((unsigned)nsplit), dim3(256),
-                                   args, 0, st);
+    hipError_t e = ev ? hipEventRecord(ev[0], st) : hipSuccess;
     if (e != hipSuccess) return e;
+    e = hipLaunchKernel((const void*)&decode_split_kernel<T, D>, dim3((unsigned)nsplit), dim3(256), args, 0, st);
+    if (e != hipSuccess) return e;
+    if (ev && (e = hipEventRecord(ev[1], st)) != hipSuccess) return e;
     const size_t rows = (size_t)a.B * a.H * a.Nq;
-    return hipLaunchKernel((const void*)&decode_merge_kernel<T, D>, dim3((unsigned)((rows + 3) / 4)), dim3(256),
-                           args, 0, st);
+    e = hipLaunchKernel((const void*)&decode_merge_kernel<T, D>, dim3((unsigned)((rows + 3) / 4)), dim3(256),
+                        args, 0, st);
+    if (e != hipSuccess) return e;
+    return ev ? hipEventRecord(ev[2], st) : hipSuccess;
 }
 }  // namespace
 
-hipError_t launch_decode(const DecodeArgs& a, fa_dtype dt, int d, hipStream_t s) {
-    if (dt == FA_BF16) return d == 64 ? launch_t<bf16, 64>(a, s) : launch_t<bf16, 128>(a, s);
-    return d == 64 ? launch_t<f16, 64>(a, s) : launch_t<f16, 128>(a, s);
+hipError_t launch_decode(const DecodeArgs& a, fa_dtype dt, int d, const hipEvent_t* ev, hipStream_t s) {
+    if (dt == FA_BF16) return d == 64 ? launch_t<bf16, 64>(a, ev, s) : launch_t<bf16, 128>(a, ev, s);
+    return d == 64 ? launch_t<f16, 64>(a, ev, s) : launch_t<f16, 128>(a, ev, s);
 }
 
 }  // namespace fa

@@ -160,7 +160,8 @@ inline size_t decode_workspace_bytes(int B, int H, int Hkv, int Nq, int Nk, int 
     const size_t rows = (size_t)B * H * Nq;
     return align256(rows * p.S * d * 4) + align256(rows * p.S * 4);
 }
-hipError_t launch_decode(const DecodeArgs& a, fa_dtype dt, int d, hipStream_t s);
+// events: null or three events (before the chunk kernel, between, after the merge)
+hipError_t launch_decode(const DecodeArgs& a, fa_dtype dt, int d, const hipEvent_t* ev, hipStream_t s);
 
 hipError_t launch_fwd(FwdArgs a, fa_dtype dt, int d, void* workspace, hipStream_t s);
 hipError_t launch_bwd(const BwdArgs& a, fa_dtype dt, int d, hipStream_t s);

@@ -41,7 +41,7 @@ def test_library_exports_every_declared_symbol():
 
 def test_scalars():
     L = _lib()
-    assert L.fa_abi_version() == 3
+    assert L.fa_abi_version() == 4
     for code in list(lib_mod.STATUS) + [-99]:
         assert isinstance(L.fa_status_string(code), bytes)
     br, bc = ctypes.c_int32(), ctypes.c_int32()
@@ -175,7 +175,7 @@ def test_decode_validation_and_workspace():
 
     def dec(B=1, H=4, Hkv=2, Nq=1, Nk=100, d=64, dt=2, scale=0.125, ws=P, ws_bytes=1 << 24, ptrs=None):
         ptrs = ptrs or [P] * 5
-        return L.fa_decode(*ptrs, B, H, Hkv, Nq, Nk, d, dt, scale, 0, None, ws, ws_bytes, None)
+        return L.fa_decode(*ptrs, B, H, Hkv, Nq, Nk, d, dt, scale, 0, None, None, ws, ws_bytes, None)
 
     assert dec(Hkv=3) == -2                  # must divide H
     assert dec(Hkv=0) == -2 and dec(Nq=0) == -2 and dec(Nk=0) == -2

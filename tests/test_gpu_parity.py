@@ -128,6 +128,8 @@ DECODE_CASES = [
     (2, 6, 3, 16, 513, 64, "bf16", True, (513, 100)),
     (1, 16, 2, 8, 900, 128, "fp16", True, None),
     (2, 4, 1, 2, 4097, 64, "bf16", False, (4097, 2048)),
+    (1, 2, 1, 1, 16384, 64, "bf16", True, (16000,)),      # 128 chunks: two batches in the merge
+    (1, 4, 1, 3, 2600, 128, "fp16", True, (2599,)),       # 21 chunks
 ]
 
 
@@ -150,6 +152,34 @@ def test_decode_matrix(case):
     O, L = oracle.decode_fwd(q, k, v, 1.0 / np.sqrt(d), kv_lens=None if kl is None else kl.numpy(), causal=causal)
     res = dict(o=check_o(o, O, dt, "O(stored)", stored=True), lse=check_lse(lse, L, dt))
     print(f"[ok] decode {case} {res}", flush=True)
+
+
+@pytest.mark.parametrize("dtype,d", [("bf16", 128), ("fp16", 64)])
+def test_decode_ignores_cache_past_valid_length(dtype, d):
+    """Cache rows at or past kv_lens[b] are never read: filled with NaN they
+    change nothing.  The expected values come from the oracle on the same cache
+    with those rows zeroed (keys past the valid length take no part)."""
+    B, H, hkv, nq, nk = 3, 8, 2, 2, 2048
+    lens = (1500, 37, 2048)
+    print(f"[case] decode NaN past length {dtype} d={d}", flush=True)
+    rng = np.random.default_rng(91)
+    dt = DT[dtype]
+    q = torch.from_numpy(rng.standard_normal((B, H, nq, d))).to(dt)
+    k = torch.from_numpy(rng.standard_normal((B, hkv, nk, d))).to(dt)
+    v = torch.from_numpy(rng.standard_normal((B, hkv, nk, d))).to(dt)
+    kn, vn = k.clone(), v.clone()
+    for b, L in enumerate(lens):
+        k[b, :, L:] = 0
+        v[b, :, L:] = 0
+        kn[b, :, L:] = float("nan")
+        vn[b, :, L:] = float("nan")
+    kl = torch.tensor(lens, dtype=torch.int32)
+    o, lse = fa.decode(cuda(q), cuda(kn), cuda(vn), kv_lens=cuda(kl), causal=True)
+    torch.cuda.synchronize()
+    assert torch.isfinite(o).all() and torch.isfinite(lse).all()
+    O, L = oracle.decode_fwd(q, k, v, 1.0 / np.sqrt(d), kv_lens=kl.numpy(), causal=True)
+    res = dict(o=check_o(o, O, dt, "O(stored)", stored=True), lse=check_lse(lse, L, dt))
+    print(f"[ok] decode NaN past length {res}", flush=True)
 
 
 def test_fully_masked_rows_and_empty_keys():

@@ -74,3 +74,17 @@ def test_workload_sampled_oracle(name):
         res[f"dv{b}.{g}"] = check_grad(dv[b:b + 1, g:g + 1, cols], rv[b:b + 1, g:g + 1], dtype, f"dV(b{b} g{g})")
     # the LSE and D the oracle used for the columns are its own, all rows
     print(f"[ok] {name} {res}", flush=True)
+
+
+def test_decode_workload_full_oracle():
+    """The decode workload at full size: one new token per sequence against a
+    16K-row cache with per-sequence valid lengths, grouped K/V heads."""
+    w = W.WORKLOADS["decode"]
+    print("[case] decode full", flush=True)
+    x = W.make_inputs(w)
+    dtype = W.torch_dtype(w.dtype)
+    o, lse = fa.decode(cuda(x["q"]), cuda(x["k"]), cuda(x["v"]), kv_lens=cuda(x["key_lens"]), causal=w.causal)
+    torch.cuda.synchronize()
+    O, L = oracle.decode_fwd(x["q"], x["k"], x["v"], x["scale"], kv_lens=x["key_lens"].numpy(), causal=w.causal)
+    res = dict(o=check_o(o, O, dtype, "O(stored)", stored=True), lse=check_lse(lse, L, dtype))
+    print(f"[ok] decode {res}", flush=True)

@@ -54,3 +54,12 @@ def test_grouped_query_shapes():
     assert x["k"].shape == x["v"].shape == (1, 8, 64, 8)
     # MHA workloads keep their draws: K/V heads default to H
     assert W.WORKLOADS["tiny"].Hkv == 2
+
+
+def test_decode_workload_shapes():
+    w = W.WORKLOADS["decode"].with_(B=3, N=300, d=8, key_len_range=(100, 300))
+    x = W.make_inputs(w)
+    assert x["q"].shape == (3, 32, 1, 8) and x["k"].shape == x["v"].shape == (3, 8, 300, 8)
+    assert "do" not in x
+    kl = x["key_lens"].numpy()
+    assert kl.min() >= 100 and kl.max() <= 300

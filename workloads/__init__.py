@@ -58,6 +58,7 @@ class Workload:
     sparse_density: Optional[float] = None  # block-sparse target density or None
     sample_rows: Optional[int] = None       # rows the oracle checks at full size
     kv_heads: Optional[int] = None          # K/V heads (grouped-query); None = H
+    decode_q: Optional[int] = None          # decode: Nq new query rows against an N-row cache
 
     @property
     def Hkv(self) -> int:
@@ -90,6 +91,10 @@ WORKLOADS = {
     # grouped-query attention: 32 query heads share 8 K/V heads, causal
     "gqa": Workload("gqa", 4, 32, 4096, 128, "bf16", seed=6, causal=True, kv_heads=8,
                     sample_rows=256),
+    # decode: one new token per sequence against a 16K-row cache (valid
+    # lengths 8K..16K), the same head shape
+    "decode": Workload("decode", 16, 32, 16384, 128, "bf16", seed=7, causal=True, kv_heads=8,
+                       key_len_range=(8192, 16384), decode_q=1),
 }
 
 
@@ -128,8 +133,11 @@ def make_inputs(w: Workload, dtype: Optional[str] = None, with_do: bool = True) 
     rng = np.random.default_rng(w.seed)
     out = {}
     for name in ("q", "k", "v", "do"):
+        if name == "do" and w.decode_q is not None:
+            continue                      # decode has no backward
         heads = w.Hkv if name in ("k", "v") else w.H
-        x = rng.standard_normal((w.B, heads, w.N, w.d)) * w.std
+        rows = w.decode_q if (name == "q" and w.decode_q is not None) else w.N
+        x = rng.standard_normal((w.B, heads, rows, w.d)) * w.std
         out[name] = round_to(x, dtype)
         del x
     key_lens = None
@@ -144,7 +152,7 @@ def make_inputs(w: Workload, dtype: Optional[str] = None, with_do: bool = True) 
                causal=w.causal, dropout_p=w.dropout_p, seed=w.dropout_seed,
                rng_offset=w.rng_offset, dtype=dtype)
     if not with_do:
-        out.pop("do")
+        out.pop("do", None)
     return out
 
 
