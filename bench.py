@@ -81,6 +81,9 @@ def parse():
     ap.add_argument("--cpu-rows", type=int, default=6144,
                     help="leading causal rows per head the oracle baseline computes")
     ap.add_argument("--sweep", action="store_true", help="also time the N sweep (extra JSON lines)")
+    ap.add_argument("--compare-standard", action="store_true",
+                    help="also time standard attention (five separate ops on vendor GEMMs) against this "
+                         "library at N = 1K, 2K, 4K (extra JSON lines)")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="first run one plain device-to-device copy of MIB MiB (a known-size kernel "
                          "that hardware byte counters can be scaled by)")
@@ -201,6 +204,114 @@ def time_workload(w, steps, warmup, ev):
     pairs = valid_pairs(x, w)
     return dict(x=x, pairs=pairs, wall_s=wall, fwd_ms=fwd_ms, bwd_main_ms=bwd_ms, kv_ms=kv_ms, dq_ms=dq_ms,
                 step_ms=step_ms, fwd_pass_ms=fwd_pass_ms, bwd_pass_ms=bwd_pass_ms)
+
+
+def standard_attention(q, k, v, do, scale, causal, p, events=None):
+    """Standard attention as the pages describe it, for comparison: five
+    separate operations per forward, each reading and writing a full N x N
+    matrix in HBM (FlashAttention explainer, "kernel fusion"; Self-Attention
+    tutorial, section 4):
+        S = scale * Q K^T  (vendor GEMM)   ->  masked_fill(-inf) (causal)
+        P = softmax(S)     ->  dropout(P)  ->  O = P V  (vendor GEMM)
+    and the matching backward (dV = P_d^T dO, dP_d = dO V^T, dropout
+    backward, softmax backward dS = P o (dP - rowsum(dP o P)), dQ = dS K,
+    dK = dS^T Q, scale folded).  The N x N matrices enter every GEMM in their
+    natural layout (dV and dK are computed transposed, as dO^T P_d and Q^T dS,
+    with the small left operands made contiguous), so no N x N transpose is
+    materialised and no GEMM operand is a transposed view.  Returns (O, dQ, dK, dV, dropout keep mask or None).
+    events: (e0, e1, e2) hipEvent_t handles recorded before the forward,
+    between the passes and after the backward on the current stream."""
+    import torch
+    hip = HipEvents() if events is not None else None
+    stream = torch.cuda.current_stream(q.device).cuda_stream if hip else None
+    N = q.shape[2]
+    if hip:
+        hip.record(events[0], stream)
+    s = torch.matmul(q * scale, k.transpose(-1, -2).contiguous())
+    if causal:
+        s.masked_fill_(torch.ones(N, N, dtype=torch.bool, device=q.device).triu_(1), float("-inf"))
+    pm = torch.softmax(s, dim=-1)
+    del s
+    keep = None
+    if p > 0:
+        pd, keep = torch.ops.aten.native_dropout(pm, p, True)
+    else:
+        pd = pm
+    o = torch.matmul(pd, v)
+    if hip:
+        hip.record(events[1], stream)
+    dv = torch.matmul(do.transpose(-1, -2).contiguous(), pd).transpose(-1, -2)
+    del pd
+    dp = torch.matmul(do, v.transpose(-1, -2).contiguous())
+    if keep is not None:
+        dp = torch.ops.aten.native_dropout_backward(dp, keep, 1.0 / (1.0 - p))
+    ds = torch.ops.aten._softmax_backward_data(dp, pm, -1, pm.dtype)
+    del dp, pm
+    dq = torch.matmul(ds, k) * scale
+    dk = torch.matmul(q.transpose(-1, -2).contiguous(), ds).transpose(-1, -2) * scale
+    if hip:
+        hip.record(events[2], stream)
+    return o, dq, dk, dv, keep
+
+
+def compare_standard(ev, steps, warmup, d=64, heads=16, tokens=16384, p=0.1):
+    """This library against standard attention on the same inputs: causal,
+    dropout p, bf16, H heads, B*N = tokens, N = 1K, 2K, 4K.  Times fwd and
+    bwd by HIP events (medians), and the peak device memory each step adds on
+    top of the resident Q, K, V, dO (torch's allocator statistics)."""
+    import torch
+    import io_aware_exact_tiled_amd as fa
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.current_stream(dev).cuda_stream
+    for N in (1024, 2048, 4096):
+        B = tokens // N
+        g = torch.Generator(device="cpu").manual_seed(N)
+        q, k, v, do = (torch.randn(B, heads, N, d, generator=g).to(torch.bfloat16).to(dev) for _ in range(4))
+        scale = 1.0 / np.sqrt(d)
+        res = {}
+        for name in ("ours", "standard"):
+            e = [[ev.create() for _ in range(3)] for _ in range(steps)]
+
+            def step(i=None):
+                if name == "ours":
+                    if i is not None:
+                        ev.record(e[i][0], stream)
+                    o, lse = fa.fwd(q, k, v, causal=True, dropout_p=p, seed=1, scale=scale)
+                    if i is not None:
+                        ev.record(e[i][1], stream)
+                    out = fa.bwd(q, k, v, o, do, lse, causal=True, dropout_p=p, seed=1, scale=scale)
+                    if i is not None:
+                        ev.record(e[i][2], stream)
+                    return out
+                return standard_attention(q, k, v, do, scale, True, p, None if i is None else e[i])
+
+            for _ in range(warmup):
+                step()
+            torch.cuda.synchronize()
+            base = torch.cuda.memory_allocated(dev)
+            torch.cuda.reset_peak_memory_stats(dev)
+            for i in range(steps):
+                out = step(i)
+                del out
+            torch.cuda.synchronize()
+            peak = torch.cuda.max_memory_allocated(dev) - base
+            fm = float(np.median([ev.ms(x[0], x[1]) for x in e]))
+            bm = float(np.median([ev.ms(x[1], x[2]) for x in e]))
+            for x in e:
+                for h in x:
+                    ev.destroy(h)
+            res[name] = (fm, bm, peak)
+        (of, ob, om), (sf, sb, sm) = res["ours"], res["standard"]
+        print(json.dumps({"compare": "standard attention (5 separate ops, vendor GEMMs)", "B": B, "H": heads, "N": N,
+                          "d": d, "causal": True, "dropout_p": p, "dtype": "bf16",
+                          "ours_fwd_ms": round(of, 4), "ours_bwd_ms": round(ob, 4),
+                          "std_fwd_ms": round(sf, 4), "std_bwd_ms": round(sb, 4),
+                          "speedup_fwd": round(sf / of, 2), "speedup_bwd": round(sb / ob, 2),
+                          "speedup_step": round((sf + sb) / (of + ob), 2),
+                          "ours_peak_extra_MiB": round(om / 2**20, 1), "std_peak_extra_MiB": round(sm / 2**20, 1),
+                          "memory_ratio": round(sm / om, 1)}), flush=True)
+        del q, k, v, do
+        torch.cuda.empty_cache()
 
 
 def decode_bytes(x, w):
@@ -413,6 +524,8 @@ def main():
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(w, args.cpu_rows)
     print(json.dumps(out), flush=True)
+    if args.compare_standard:
+        compare_standard(ev, max(5, args.steps // 2), 2)
     if args.sweep:
         for d in (64, 128):
             for causal in (False, True):

@@ -427,3 +427,29 @@ def test_dropout_is_unbiased_and_lse_undropped():
     outs = np.stack(outs)
     mean, se = outs.mean(0), outs.std(0) / np.sqrt(len(outs))
     assert (np.abs(mean - O0) <= 5 * se + 1e-12).all()
+
+
+def test_standard_attention_baseline_matches_oracle():
+    """The standard-attention comparison baseline (five separate ops and their
+    backward, bench.py) computes the same function as the oracle: fp64 on the
+    CPU, causal and not, without dropout; with dropout its keep mask applied
+    to the oracle's P reproduces its O."""
+    import bench
+    rng = np.random.default_rng(12)
+    B, H, N, d = 2, 3, 70, 16
+    q, k, v, do = (torch.from_numpy(rng.standard_normal((B, H, N, d))) for _ in range(4))
+    scale = float(np.float32(1 / np.sqrt(d)))         # the oracle takes the scale as float32
+    for causal in (False, True):
+        o, dq, dk, dv, _ = bench.standard_attention(q, k, v, do, scale, causal, 0.0)
+        O, _ = oracle.attn_fwd(q, k, v, scale, causal=causal)
+        dQ, dK, dV, _ = oracle.attn_bwd(q, k, v, do, scale, causal=causal)
+        for got, want in ((o, O), (dq, dQ), (dk, dK), (dv, dV)):
+            np.testing.assert_allclose(got.numpy(), want, atol=1e-12, rtol=1e-10)
+    torch.manual_seed(0)
+    o, *_, keep = bench.standard_attention(q, k, v, do, scale, True, 0.25)
+    S = scale * np.einsum("bhid,bhjd->bhij", q.numpy(), k.numpy())
+    S = np.where(np.tril(np.ones((N, N), dtype=bool)), S, -np.inf)
+    P = np.exp(S - S.max(-1, keepdims=True))
+    P /= P.sum(-1, keepdims=True)
+    want = np.einsum("bhij,bhjd->bhid", P * keep.numpy() / 0.75, v.numpy())
+    np.testing.assert_allclose(o.numpy(), want, atol=1e-12)
