@@ -8,7 +8,8 @@ attention arithmetic).
 
 Contents
   attention.py  plain materialising fwd/bwd, sampled-row variants, the pages'
-                tiled forward as a model for the merge checks, and an explicit
+                tiled forward as a model for the merge checks, the key/value-
+                outer forward with its HBM access counts, and an explicit
                 softmax-Jacobian backward for tiny inputs
   philox.py     Philox4x32-10 and the dropout keep rule
   tiles.py      expected tile-visit sets and valid-pair counts
@@ -23,7 +24,7 @@ multipliers come from the SC'11 paper without a known-answer vector here).
 """
 
 from .attention import (attn_fwd, attn_bwd, attn_bwd_rows_cols, attn_stats, kv_head, decode_fwd,  # noqa: F401
-                        tiled_fwd, attn_bwd_jacobian, validity, safe_softmax,
+                        tiled_fwd, kv_outer_fwd, attn_bwd_jacobian, validity, safe_softmax,
                         as_f64, scale_f32)
 from .philox import (philox4x32_10, philox4_scalar, keep_mask,  # noqa: F401
                      dropout_threshold)

@@ -34,6 +34,10 @@ What it computes is the plain definition that tiled exact attention reaches
   rows of which the first len_b are valid; query row i sits at position
   len_b - Nq + i (the newest tokens), and with the causal mask sees keys
   j <= that position.  Same softmax, same LSE.
+* the key/value-outer loop order of the original algorithm (explainer,
+  step-by-step algorithm): the same O and LSE, reached block by block with
+  the running statistics stored between steps; it also counts the HBM
+  element traffic of that order for the IO model (`kv_outer_fwd`).
 * grouped-query attention (tutorial section 9.2-9.3, MQA and GQA): K and V
   may have Hkv heads, Hkv dividing H; query head h uses K/V head
   h // (H / Hkv) (contiguous groups -- the pages do not fix the grouping),
@@ -282,25 +286,86 @@ def tiled_fwd(q, k, v, scale, Br, Bc, causal=False, key_lens=None, block_mask=No
                     Sij = sc * (q[b, h, r] @ k[b, h, c].T)
                     Aij = validity(r, N, causal, kl, block_mask)[:, c]
                     Sij = np.where(Aij, Sij, -np.inf)
-                    m_t = Sij.max(axis=1)                       # block row max
-                    mt_ref = np.where(np.isfinite(m_t), m_t, 0.0)
-                    P_t = np.exp(Sij - mt_ref[:, None])         # block probabilities
-                    l_t = P_t.sum(axis=1)                       # block row sum
-                    m_new = np.maximum(m, m_t)
-                    mn_ref = np.where(np.isfinite(m_new), m_new, 0.0)
-                    a_old = np.exp(m - mn_ref)                  # e^{m - m_new}
-                    a_blk = np.exp(m_t - mn_ref)                # e^{m~ - m_new}
-                    l_new = a_old * l + a_blk * l_t
-                    with np.errstate(invalid="ignore", divide="ignore"):
-                        Oi = np.where(l_new[:, None] > 0,
-                                      (l[:, None] * a_old[:, None] * Oi
-                                       + a_blk[:, None] * (P_t @ v[b, h, c])) / l_new[:, None],
-                                      0.0)
-                    m, l = m_new, l_new
+                    m, l, Oi = _merge_block(m, l, Oi, Sij, v[b, h, c])
                 O[b, h, r] = Oi
                 with np.errstate(divide="ignore"):
                     LSE[b, h, r] = np.where(l > 0, m + np.log(np.where(l > 0, l, 1.0)), -np.inf)
     return O, LSE
+
+
+def kv_outer_fwd(q, k, v, scale, Br, Bc, causal=False):
+    """The pages' forward in its original loop order, key/value blocks outer
+    and query blocks inner (FlashAttention explainer, azimuth.plus,
+    step-by-step algorithm; FlashAttention summary, xyznot.com, "Method"),
+    with the running O, l, m kept in "HBM" arrays that every inner step
+    loads, updates and stores back.  Blocks holding no valid pair (causal:
+    above the diagonal) are skipped, as the block-sparse section of both
+    pages skips zero blocks.  Returns (O, LSE, io), io = {"read": {...},
+    "write": {...}} counting the elements each HBM array sees under the
+    algorithm's loads and stores (summed over heads), for the IO model
+    Theta(N^2 d^2 / M) of the summary's "complexity" section.  No dropout."""
+    q, k, v = as_f64(q), as_f64(k), as_f64(v)
+    B, H, N, d = q.shape
+    sc = scale_f32(scale)
+    rd = dict(Q=0, K=0, V=0, O=0, l=0, m=0)
+    wr = dict(O=0, l=0, m=0)
+    O = np.zeros_like(q)
+    LSE = np.zeros((B, H, N))
+    for b in range(B):
+        for h in range(H):
+            # initialise O = 0, l = 0, m = -inf in HBM
+            Oh = np.zeros((N, d))
+            lh = np.zeros(N)
+            mh = np.full(N, -np.inf)
+            wr["O"] += N * d
+            wr["l"] += N
+            wr["m"] += N
+            for j0 in range(0, N, Bc):
+                c = np.arange(j0, min(j0 + Bc, N))
+                rows = [np.arange(i0, min(i0 + Br, N)) for i0 in range(0, N, Br)]
+                rows = [r for r in rows if validity(r, N, causal)[:, c].any()]
+                if not rows:
+                    continue
+                Kj, Vj = k[b, h, c], v[b, h, c]                  # load K_j, V_j
+                rd["K"] += Kj.size
+                rd["V"] += Vj.size
+                for r in rows:
+                    Qi, Oi, li, mi = q[b, h, r], Oh[r], lh[r], mh[r]    # load Q_i, O_i, l_i, m_i
+                    rd["Q"] += Qi.size
+                    rd["O"] += Oi.size
+                    rd["l"] += li.size
+                    rd["m"] += mi.size
+                    Sij = np.where(validity(r, N, causal)[:, c], sc * (Qi @ Kj.T), -np.inf)
+                    mi_new, li_new, Oi_new = _merge_block(mi, li, Oi, Sij, Vj)
+                    Oh[r], lh[r], mh[r] = Oi_new, li_new, mi_new     # write O_i, l_i, m_i
+                    wr["O"] += Oi_new.size
+                    wr["l"] += li_new.size
+                    wr["m"] += mi_new.size
+            O[b, h] = Oh
+            with np.errstate(divide="ignore"):
+                LSE[b, h] = np.where(lh > 0, mh + np.log(np.where(lh > 0, lh, 1.0)), -np.inf)
+    return O, LSE, {"read": rd, "write": wr}
+
+
+def _merge_block(m, l, Oi, Sij, Vj):
+    """One block step of the summary's "Method" (block row max m~, block
+    probabilities P~ = exp(S - m~), block row sum l~; m_new = max(m, m~),
+    l_new = e^{m - m_new} l + e^{m~ - m_new} l~, O_new = diag(l_new)^-1
+    (diag(l) e^{m - m_new} O + e^{m~ - m_new} P~ V)).  Rows with no valid key
+    so far keep m = -inf, l = 0, O = 0."""
+    m_t = Sij.max(axis=1)
+    mt_ref = np.where(np.isfinite(m_t), m_t, 0.0)
+    P_t = np.exp(Sij - mt_ref[:, None])
+    l_t = P_t.sum(axis=1)
+    m_new = np.maximum(m, m_t)
+    mn_ref = np.where(np.isfinite(m_new), m_new, 0.0)
+    a_old = np.exp(m - mn_ref)
+    a_blk = np.exp(m_t - mn_ref)
+    l_new = a_old * l + a_blk * l_t
+    with np.errstate(invalid="ignore", divide="ignore"):
+        O_new = np.where(l_new[:, None] > 0,
+                         (l[:, None] * a_old[:, None] * Oi + a_blk[:, None] * (P_t @ Vj)) / l_new[:, None], 0.0)
+    return m_new, l_new, O_new
 
 
 def attn_bwd_jacobian(q, k, v, do, scale, causal=False, key_lens=None,

@@ -453,3 +453,42 @@ def test_standard_attention_baseline_matches_oracle():
     P /= P.sum(-1, keepdims=True)
     want = np.einsum("bhij,bhjd->bhid", P * keep.numpy() / 0.75, v.numpy())
     np.testing.assert_allclose(o.numpy(), want, atol=1e-12)
+
+
+@pytest.mark.parametrize("N,Br,Bc,causal", [(70, 16, 8, False), (70, 8, 16, True), (64, 16, 16, True),
+                                             (33, 32, 8, True), (5, 4, 4, False)])
+def test_kv_outer_fwd_matches_definition(N, Br, Bc, causal):
+    """The key/value-outer block order (running O, l, m stored between
+    steps) reaches the plain definition's O and LSE."""
+    rng = np.random.default_rng(N + Br + Bc)
+    B, H, d = 2, 2, 8
+    q, k, v = (rng.standard_normal((B, H, N, d)) * 1.5 for _ in range(3))
+    O, L, _ = oracle.kv_outer_fwd(q, k, v, 0.4, Br, Bc, causal=causal)
+    O2, L2 = oracle.attn_fwd(q, k, v, 0.4, causal=causal)
+    np.testing.assert_allclose(O, O2, atol=1e-12, rtol=1e-10)
+    np.testing.assert_allclose(L, L2, atol=1e-12, rtol=1e-12)
+
+
+def test_kv_outer_io_counts_closed_form():
+    """HBM element counts of the key/value-outer order (explainer,
+    step-by-step algorithm): K and V once; every (query block, key block)
+    step loads Q_i, O_i, l_i, m_i and stores O_i, l_i, m_i; plus the initial
+    stores of O, l, m.  Non-causal: T_c steps per row, so Q and O traffic is
+    T_c N d -- Theta(N^2 d / B_c), the summary's Theta(N^2 d^2 / M) with
+    B_c ~ M / 4d.  Causal with B_r = B_c = b and N = T b: T (T + 1) / 2 steps."""
+    B, H, d = 1, 3, 4
+    for N, Br, Bc in ((48, 8, 16), (50, 16, 8), (7, 3, 2)):
+        x = np.zeros((B, H, N, d))
+        _, _, io = oracle.kv_outer_fwd(x, x, x, 1.0, Br, Bc, causal=False)
+        Tc = -(-N // Bc)
+        BH = B * H
+        assert io["read"] == dict(Q=Tc * N * d * BH, K=N * d * BH, V=N * d * BH, O=Tc * N * d * BH,
+                                  l=Tc * N * BH, m=Tc * N * BH)
+        assert io["write"] == dict(O=(1 + Tc) * N * d * BH, l=(1 + Tc) * N * BH, m=(1 + Tc) * N * BH)
+    T, b = 6, 8
+    N = T * b
+    x = np.zeros((B, H, N, d))
+    _, _, io = oracle.kv_outer_fwd(x, x, x, 1.0, b, b, causal=True)
+    steps = T * (T + 1) // 2
+    assert io["read"]["Q"] == steps * b * d * H and io["read"]["O"] == steps * b * d * H
+    assert io["read"]["K"] == N * d * H and io["write"]["l"] == (N + steps * b) * H
