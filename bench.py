@@ -81,6 +81,9 @@ def parse():
     ap.add_argument("--cpu-rows", type=int, default=6144,
                     help="leading causal rows per head the oracle baseline computes")
     ap.add_argument("--sweep", action="store_true", help="also time the N sweep (extra JSON lines)")
+    ap.add_argument("--io-ablation", action="store_true",
+                    help="also run the key/value-outer forward beside the query-outer one at N = 2K, 4K, 8K "
+                         "(extra JSON lines with the HBM bytes each order implies)")
     ap.add_argument("--compare-standard", action="store_true",
                     help="also time standard attention (five separate ops on vendor GEMMs) against this "
                          "library at N = 1K, 2K, 4K (extra JSON lines)")
@@ -314,6 +317,89 @@ def compare_standard(ev, steps, warmup, d=64, heads=16, tokens=16384, p=0.1):
         torch.cuda.empty_cache()
 
 
+def kv_outer_bytes(B, H, N, d, e, causal, bc, G):
+    """Bytes the key/value-outer kernel moves by its own loop (fwd_kvo_kernel):
+    each of the G workgroups of a head loads every key tile its query blocks
+    need (K and V, e bytes per element); for each key tile, each 32-row wave
+    whose rows see it loads its Q rows (e), and -- after the first tile --
+    its running O (fp32) and (m, l); it stores them back (fp32), or, on its
+    last tile, O (e) and LSE.  Also the pages' model of the same order
+    (FlashAttention explainer, step-by-step algorithm): K, V once; Q, O, l, m
+    loaded and O, l, m stored at every (query block, key block) step,
+    elements in the same sizes."""
+    Tr, Tc = -(-N // 128), -(-N // bc)
+    rd = wr = 0
+    for g in range(min(G, Tr)):
+        its = list(range(g, Tr, G))
+        j_end = min(Tc, (min(its[-1] * 128 + 128, N) - 1) // bc + 1) if causal else Tc
+        for j in range(j_end):
+            rows = min(bc, N - j * bc)
+            rd += 2 * rows * d * e
+            for it in its:
+                for w in range(4):
+                    q0 = it * 128 + w * 32
+                    if q0 >= N or (causal and j * bc > q0 + 31):
+                        continue
+                    r = min(32, N - q0)
+                    rd += r * d * e + (r * (d * 4 + 8) if j > 0 else 0)
+                    last = (q0 // bc) if causal else Tc - 1
+                    wr += r * d * e + r * 4 if j == last else r * (d * 4 + 8)
+    # the pages' order with blocks of 128 query rows and bc keys, skipping
+    # blocks above the diagonal: K, V once, then per step Q, O (e), l, m
+    steps = 0
+    for j in range(Tc):
+        for i in range(Tr):
+            if not causal or j * bc <= min(i * 128 + 127, N - 1):
+                steps += min(128, N - i * 128)
+    model_rd = 2 * N * d * e + steps * (2 * d * e + 8)
+    model_wr = N * (d * e + 8) + steps * (d * e + 8)
+    BH = B * H
+    return rd * BH, wr * BH, model_rd * BH, model_wr * BH
+
+
+def io_ablation(ev, steps, warmup):
+    """Key/value-outer forward against the query-outer one: causal bf16,
+    B=1, H=16, d=128, N = 2K/4K/8K, key tiles of 64 and 128, 1 and 4
+    workgroups per head.  Times both by HIP events and prints the bytes each
+    order implies; the HBM bytes measured for them are in profiles/."""
+    import torch
+    import io_aware_exact_tiled_amd as fa
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.current_stream(dev).cuda_stream
+    B, H, d = 1, 16, 128
+    for N in (2048, 4096, 8192):
+        g = torch.Generator(device="cpu").manual_seed(N)
+        q, k, v = (torch.randn(B, H, N, d, generator=g).to(torch.bfloat16).to(dev) for _ in range(3))
+        e = [ev.create(), ev.create()]
+        ws = torch.empty(fa.fwd_workspace_bytes(B, H, N, d, q.dtype), dtype=torch.uint8, device=dev)
+        ts = []
+        for i in range(warmup + steps):
+            fa.fwd(q, k, v, causal=True, workspace=ws, events=e if i >= warmup else None)
+            if i >= warmup:
+                ts.append(ev.ms(e[0], e[1]))
+        qo_ms = float(np.median(ts))
+        qo_bytes = B * H * (4 * N * d * 2 + 4 * N)
+        for bc in (64, 128):
+            for G in (1, 4):
+                ts = []
+                for i in range(warmup + steps):
+                    fa.fwd_kv_outer(q, k, v, causal=True, block_cols=bc, groups_per_head=G,
+                                    events=e if i >= warmup else None)
+                    if i >= warmup:
+                        ts.append(ev.ms(e[0], e[1]))
+                rd, wr, mrd, mwr = kv_outer_bytes(B, H, N, d, 2, True, bc, G)
+                print(json.dumps({"io_ablation": "key/value-outer forward", "B": B, "H": H, "N": N, "d": d,
+                                  "causal": True, "block_cols": bc, "groups_per_head": G,
+                                  "kv_outer_ms": round(float(np.median(ts)), 4), "q_outer_ms": round(qo_ms, 4),
+                                  "kv_outer_read_MiB": round(rd / 2**20, 1), "kv_outer_write_MiB": round(wr / 2**20, 1),
+                                  "model_read_MiB": round(mrd / 2**20, 1), "model_write_MiB": round(mwr / 2**20, 1),
+                                  "q_outer_min_MiB": round(qo_bytes / 2**20, 1)}), flush=True)
+        for h in e:
+            ev.destroy(h)
+        del q, k, v, ws
+        torch.cuda.empty_cache()
+
+
 def decode_bytes(x, w):
     """Algorithmic HBM bytes of one decode call, split by kernel: the chunk
     kernel must read Q and the valid cache rows of K and V (sum over b of
@@ -526,6 +612,8 @@ def main():
     print(json.dumps(out), flush=True)
     if args.compare_standard:
         compare_standard(ev, max(5, args.steps // 2), 2)
+    if args.io_ablation:
+        io_ablation(ev, max(2, args.steps // 4), 1)
     if args.sweep:
         for d in (64, 128):
             for causal in (False, True):

@@ -62,7 +62,7 @@
 extern "C" {
 #endif
 
-#define FA_ABI_VERSION 4
+#define FA_ABI_VERSION 5
 
 typedef enum { FA_F32 = 0, FA_F16 = 1, FA_BF16 = 2 } fa_dtype;
 
@@ -188,6 +188,30 @@ fa_status fa_decode(const void* Q, const void* K, const void* V, void* O, float*
                     fa_dtype dtype, float scale, int32_t causal, const int32_t* kv_lens,
                     const hipEvent_t* events, void* workspace, size_t workspace_bytes,
                     hipStream_t stream);
+
+/* Forward pass in the key/value-outer loop order of the original algorithm
+ * (FlashAttention explainer, step-by-step algorithm; summary, "Method"):
+ * for each key/value tile of block_cols keys, every query block that sees it
+ * loads its running O, m, l from the workspace, updates them and stores them
+ * back; the last tile a row sees writes O and LSE.  Same O and LSE as fa_fwd
+ * (to rounding); kept as an IO ablation: its HBM traffic grows as
+ * T_c * N * d per head (summary, "complexity": Theta(N^2 d^2 / M)), where
+ * fa_fwd moves about N * d.  Q, K, V, O: [B][H][N][d] of `dtype` (FA_BF16 or
+ * FA_F16); LSE float [B][H][N]; causal or not; no dropout, key padding,
+ * block mask or grouped heads.  block_cols: 64 or 128 (else FA_ERR_OPTS).
+ * groups_per_head: workgroups per head, each taking every G-th 128-row
+ * query block (K and V are read G times per head); 0 picks
+ * min(ceil(N / 128), ceil(1024 / (B*H))); more than ceil(N / 128) is
+ * FA_ERR_SHAPE.  workspace: at least fa_fwd_kv_outer_workspace_bytes(...)
+ * bytes, 256-byte aligned (running O fp32 [B][H][N][d], then (m, l) float
+ * [B][H][N][2]).  events: NULL or two events recorded on `stream` before and
+ * after the kernel. */
+size_t fa_fwd_kv_outer_workspace_bytes(int32_t B, int32_t H, int32_t N, int32_t d);
+fa_status fa_fwd_kv_outer(const void* Q, const void* K, const void* V, void* O, float* LSE,
+                          int32_t B, int32_t H, int32_t N, int32_t d, fa_dtype dtype,
+                          float scale, int32_t causal, int32_t block_cols,
+                          int32_t groups_per_head, const hipEvent_t* events,
+                          void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /* Dropout keep bits of every element, for tests: keep is device
  * uint8[B][H][N][N], 1 = kept.  Uses the same device generator as the

@@ -216,6 +216,40 @@ def decode(q, k, v, *, kv_lens=None, causal=False, scale: Optional[float] = None
     return o, l
 
 
+def fwd_kv_outer_workspace_bytes(B, H, N, d) -> int:
+    return int(_lib.lib().fa_fwd_kv_outer_workspace_bytes(B, H, N, d))
+
+
+def fwd_kv_outer(q, k, v, *, causal=False, scale: Optional[float] = None, block_cols=128, groups_per_head=0,
+                 out=None, lse=None, workspace=None, events=None):
+    """Forward in the key/value-outer loop order (an IO ablation: the running
+    O, m, l go through device memory after every key tile).  q, k, v: [B, H,
+    N, d] bf16 or fp16.  Returns (O, LSE).  events: None or two hipEvent_t
+    handles recorded around the kernel."""
+    if q.dim() != 4 or k.shape != q.shape or v.shape != q.shape:
+        raise ValueError("q, k, v must all be [B, H, N, d]")
+    for t in (q, k, v):
+        if not t.is_cuda or not t.is_contiguous() or t.dtype != q.dtype or t.device != q.device:
+            raise ValueError("q, k, v must be contiguous GPU tensors of one dtype and device")
+    B, H, N, d = q.shape
+    scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    o = out if out is not None else torch.empty_like(q)
+    l = lse if lse is not None else torch.empty((B, H, N), dtype=torch.float32, device=q.device)
+    need = fwd_kv_outer_workspace_bytes(B, H, N, d)
+    ws = workspace if workspace is not None else torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    ev = None
+    if events is not None:
+        if len(events) != 2:
+            raise ValueError("events: two hipEvent_t handles")
+        ev = (ctypes.c_void_p * 2)(*events)
+    code = _lib.lib().fa_fwd_kv_outer(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), l.data_ptr(),
+                                      B, H, N, d, _dtype_code(q), scale, 1 if causal else 0, int(block_cols),
+                                      int(groups_per_head), ev, ws.data_ptr(), ws.numel(), _stream(q.device))
+    check(code, "fa_fwd_kv_outer")
+    del ws
+    return o, l
+
+
 def dropout_keep_mask(seed, rng_offset, p, B, H, N, device="cuda"):
     """uint8 [B, H, N, N] keep bits from the device generator (tests only)."""
     keep = torch.empty((B, H, N, N), dtype=torch.uint8, device=device)

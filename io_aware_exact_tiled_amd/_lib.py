@@ -24,7 +24,8 @@ STATUS = {
 
 # every symbol include/fa.h declares
 EXPORTS = ("fa_fwd", "fa_fwd_workspace_bytes", "fa_bwd", "fa_bwd_workspace_bytes", "fa_decode",
-           "fa_decode_workspace_bytes", "fa_dropout_keep_mask", "fa_tile_shape",
+           "fa_decode_workspace_bytes", "fa_fwd_kv_outer", "fa_fwd_kv_outer_workspace_bytes",
+           "fa_dropout_keep_mask", "fa_tile_shape",
            "fa_status_string", "fa_last_hip_error", "fa_abi_version")
 
 
@@ -76,6 +77,11 @@ def lib():
         L.fa_decode.restype = i32
         L.fa_decode_workspace_bytes.argtypes = [i32, i32, i32, i32, i32, i32]
         L.fa_decode_workspace_bytes.restype = sz
+        L.fa_fwd_kv_outer.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, f32, i32, i32, i32, vp, vp, sz,
+                                      vp]
+        L.fa_fwd_kv_outer.restype = i32
+        L.fa_fwd_kv_outer_workspace_bytes.argtypes = [i32, i32, i32, i32]
+        L.fa_fwd_kv_outer_workspace_bytes.restype = sz
         L.fa_dropout_keep_mask.argtypes = [u64, u64, f32, i32, i32, i32, vp, vp]
         L.fa_dropout_keep_mask.restype = i32
         L.fa_tile_shape.argtypes = [i32, i32, i32, ctypes.POINTER(i32), ctypes.POINTER(i32)]

@@ -202,6 +202,42 @@ fa_status fa_decode(const void* Q, const void* K, const void* V, void* O, float*
     return e == hipSuccess ? FA_OK : hip_fail(e);
 }
 
+size_t fa_fwd_kv_outer_workspace_bytes(int32_t B, int32_t H, int32_t N, int32_t d) {
+    if (check_shape(B, H, N, d) != FA_OK) return 0;
+    const size_t rows = (size_t)B * H * N;
+    return fa::align256(rows * d * sizeof(float)) + fa::align256(rows * 2 * sizeof(float));
+}
+
+fa_status fa_fwd_kv_outer(const void* Q, const void* K, const void* V, void* O, float* LSE, int32_t B, int32_t H,
+                          int32_t N, int32_t d, fa_dtype dtype, float scale, int32_t causal, int32_t block_cols,
+                          int32_t groups_per_head, const hipEvent_t* events, void* workspace,
+                          size_t workspace_bytes, hipStream_t stream) {
+    if (!Q || !K || !V || !O || !LSE) return FA_ERR_NULL;
+    fa_status st = check_shape(B, H, N, d);
+    if (st != FA_OK) return st;
+    if (dtype != FA_BF16 && dtype != FA_F16) return FA_ERR_DTYPE;
+    if (!std::isfinite(scale) || scale <= 0.0f) return FA_ERR_SCALE;
+    if (!aligned16(Q) || !aligned16(K) || !aligned16(V) || !aligned16(O) || !aligned16(LSE)) return FA_ERR_ALIGN;
+    if (block_cols != 64 && block_cols != 128) return FA_ERR_OPTS;
+    const int Tr = (N + 127) / 128;
+    int G = groups_per_head;
+    if (G == 0) G = std::max(1, std::min(Tr, (1024 + B * H - 1) / (B * H)));
+    if (G < 1 || G > Tr || (int64_t)B * H * G >= (int64_t(1) << 31)) return FA_ERR_SHAPE;
+    const size_t rows = (size_t)B * H * N;
+    const size_t need = fa::align256(rows * d * sizeof(float)) + fa::align256(rows * 2 * sizeof(float));
+    if (!workspace || workspace_bytes < need || (reinterpret_cast<uintptr_t>(workspace) & 255u))
+        return FA_ERR_WORKSPACE;
+    fa::KvoArgs a;
+    a.q = Q; a.k = K; a.v = V; a.o = O; a.lse = LSE;
+    a.ow = static_cast<float*>(workspace);
+    a.ml = reinterpret_cast<float*>(static_cast<char*>(workspace) + fa::align256(rows * d * sizeof(float)));
+    a.B = B; a.H = H; a.N = N; a.G = G;
+    a.causal = causal ? 1 : 0;
+    a.scale_log2 = scale * LOG2E;
+    const hipError_t e = fa::launch_kv_outer(a, dtype, d, block_cols, events, stream);
+    return e == hipSuccess ? FA_OK : hip_fail(e);
+}
+
 size_t fa_bwd_workspace_bytes(int32_t B, int32_t H, int32_t N, int32_t d) {
     if (check_shape(B, H, N, d) != FA_OK) return 0;
     const size_t rows = (size_t)B * H * N;

@@ -45,31 +45,6 @@ namespace fa {
 
 namespace {
 
-template <class T> __device__ inline void store4g(T* p, float a, float b, float c, float d);
-template <> __device__ inline void store4g<f16>(f16* p, float a, float b, float c, float d) {
-    f16x4 w = {(f16)a, (f16)b, (f16)c, (f16)d};
-    *reinterpret_cast<f16x4*>(p) = w;
-}
-template <> __device__ inline void store4g<bf16>(bf16* p, float a, float b, float c, float d) {
-    bf16x4 w = {(bf16)a, (bf16)b, (bf16)c, (bf16)d};
-    *reinterpret_cast<bf16x4*>(p) = w;
-}
-template <> __device__ inline void store4g<float>(float* p, float a, float b, float c, float d) {
-    f32x4 w = {a, b, c, d};
-    *reinterpret_cast<f32x4*>(p) = w;
-}
-
-template <class T> __device__ inline typename Mma<T>::frag pack_f(const float* p) {
-    if constexpr (Mma<T>::E == 8) {
-        typename Mma<T>::frag f;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) f[e] = (T)p[e];
-        return f;
-    } else {
-        return p[0];
-    }
-}
-
 __device__ inline int clamp_len(const int32_t* key_lens, int b, int N) {
     if (!key_lens) return N;
     const int L = key_lens[b];
@@ -344,7 +319,7 @@ __global__ __launch_bounds__(512, 1) void bwd_kv_kernel(BwdArgs a) {
                 float pr[E];
 #pragma unroll
                 for (int e = 0; e < E; ++e) pr[e] = sp[qb][u * E + e];
-                return pack_f<T>(pr);
+                return pack_p<T>(pr);
             }, lane);
             __builtin_amdgcn_s_setprio(0);
         } else {
@@ -368,7 +343,7 @@ __global__ __launch_bounds__(512, 1) void bwd_kv_kernel(BwdArgs a) {
                     }
                 }
 #pragma unroll
-                for (int u = 0; u < QU; ++u) dsf[qb][u] = pack_f<T>(&ds[u * E]);
+                for (int u = 0; u < QU; ++u) dsf[qb][u] = pack_p<T>(&ds[u * E]);
             }
             have_prev = true;
         }
@@ -529,7 +504,7 @@ __global__ __launch_bounds__(256, sizeof(T) == 4 ? 1 : 2) void bwd_dq_kernel(Bwd
             {
                 typename MM::frag bs[PU];
 #pragma unroll
-                for (int u = 0; u < PU; ++u) bs[u] = pack_f<T>(&ds[u * E]);
+                for (int u = 0; u < PU; ++u) bs[u] = pack_p<T>(&ds[u * E]);
                 __builtin_amdgcn_s_setprio(1);
                 tr_chain<T, D, 1, true, 2>(dq, k, tro, [&](int, int u) { return bs[u]; }, lane);
                 __builtin_amdgcn_s_setprio(0);
@@ -548,7 +523,7 @@ __global__ __launch_bounds__(256, sizeof(T) == 4 ? 1 : 2) void bwd_dq_kernel(Bwd
         for (int db = 0; db < DB; ++db)
 #pragma unroll
             for (int g = 0; g < 4; ++g)
-                store4g<T>(dQg + db * 32 + 8 * g + 4 * hl, dq[db][4 * g] * a.scale, dq[db][4 * g + 1] * a.scale,
+                store4<T>(dQg + db * 32 + 8 * g + 4 * hl, dq[db][4 * g] * a.scale, dq[db][4 * g + 1] * a.scale,
                            dq[db][4 * g + 2] * a.scale, dq[db][4 * g + 3] * a.scale);
     }
 }

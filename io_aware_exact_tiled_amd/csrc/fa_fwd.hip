@@ -42,31 +42,6 @@ namespace fa {
 
 namespace {
 
-template <class T> __device__ inline void store4(T* p, float a, float b, float c, float d);
-template <> __device__ inline void store4<f16>(f16* p, float a, float b, float c, float d) {
-    f16x4 w = {(f16)a, (f16)b, (f16)c, (f16)d};
-    *reinterpret_cast<f16x4*>(p) = w;
-}
-template <> __device__ inline void store4<bf16>(bf16* p, float a, float b, float c, float d) {
-    bf16x4 w = {(bf16)a, (bf16)b, (bf16)c, (bf16)d};
-    *reinterpret_cast<bf16x4*>(p) = w;
-}
-template <> __device__ inline void store4<float>(float* p, float a, float b, float c, float d) {
-    f32x4 w = {a, b, c, d};
-    *reinterpret_cast<f32x4*>(p) = w;
-}
-
-template <class TV> __device__ inline typename Mma<TV>::frag pack_p(const float* p) {
-    if constexpr (Mma<TV>::E == 8) {
-        typename Mma<TV>::frag f;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) f[e] = (TV)p[e];
-        return f;
-    } else {
-        return p[0];
-    }
-}
-
 // maximum over a 256-thread workgroup (every thread gets it)
 __device__ inline uint32_t block_max256(uint32_t m) {
     __shared__ uint32_t red[4];

@@ -127,6 +127,22 @@ struct BwdArgs {
     hipEvent_t ev_mid;             // optional: between the two main kernels
 };
 
+// Forward in the key/value-outer order (IO ablation): see fa_kvouter.hip.
+struct KvoArgs {
+    const void* q;        // [B][H][N][d]
+    const void* k;
+    const void* v;
+    void* o;              // [B][H][N][d], input dtype
+    float* lse;           // [B][H][N]
+    float* ow;            // workspace [B][H][N][d]: running O between key tiles
+    float* ml;            // workspace [B][H][N][2]: running (m, l)
+    int B, H, N, G;       // G workgroups per head, each taking every G-th query block
+    int causal;
+    float scale_log2;
+};
+// events: null or two events (before and after the kernel)
+hipError_t launch_kv_outer(const KvoArgs& a, fa_dtype dt, int d, int bc, const hipEvent_t* ev, hipStream_t s);
+
 // Decode (split key/value cache): see fa_decode.hip.
 struct DecodeArgs {
     const void* q;        // [B][H][Nq][d]

@@ -41,7 +41,7 @@ def test_library_exports_every_declared_symbol():
 
 def test_scalars():
     L = _lib()
-    assert L.fa_abi_version() == 4
+    assert L.fa_abi_version() == 5
     for code in list(lib_mod.STATUS) + [-99]:
         assert isinstance(L.fa_status_string(code), bytes)
     br, bc = ctypes.c_int32(), ctypes.c_int32()
@@ -191,3 +191,26 @@ def test_decode_validation_and_workspace():
     # per-split partials: O (fp32 x d) and one log-sum-exp per query row and split
     big = L.fa_decode_workspace_bytes(16, 32, 8, 1, 16384, 128)
     assert big >= 16 * 32 * 1 * (128 * 4 + 4)
+
+
+def test_kv_outer_validation_and_workspace():
+    L = _lib()
+
+    def kvo(B=1, H=2, N=300, d=64, dt=2, scale=0.125, causal=0, bc=128, G=0, ws=P, ws_bytes=1 << 24,
+            ptrs=None):
+        ptrs = ptrs or [P] * 5
+        return L.fa_fwd_kv_outer(*ptrs, B, H, N, d, dt, scale, causal, bc, G, None, ws, ws_bytes, None)
+
+    assert kvo(N=0) == -2 and kvo(B=0) == -2
+    assert kvo(d=96) == -3
+    assert kvo(dt=0) == -4                   # fp32 is not provided in this order
+    assert kvo(scale=float("nan")) == -6
+    assert kvo(ptrs=[P, None, P, P, P]) == -1
+    assert kvo(ptrs=[P, P, P, P, P + 8]) == -7
+    assert kvo(bc=32) == -10 and kvo(bc=256) == -10
+    assert kvo(G=4) == -2 and kvo(G=-1) == -2  # 300 rows: 3 query blocks
+    need = L.fa_fwd_kv_outer_workspace_bytes(1, 2, 300, 64)
+    # running O fp32 [B][H][N][d] then (m, l) per row, each part 256-byte aligned
+    assert need == (1 * 2 * 300 * 64 * 4 + 255) // 256 * 256 + (1 * 2 * 300 * 8 + 255) // 256 * 256
+    assert kvo(ws=None) == -8 and kvo(ws_bytes=need - 1) == -8 and kvo(ws=P + 64) == -8
+    assert L.fa_fwd_kv_outer_workspace_bytes(1, 2, 300, 80) == 0

@@ -321,3 +321,30 @@ def test_extra_memory_is_linear_in_n():
     # all O(N d); a single N x N bf16 matrix would be 512 MiB
     linear = 4 * N * d * 2 + N * 4 + N * d * 4 + N * 4 + (1 << 20)
     assert peak <= linear, (peak, linear)
+
+
+KVO_CASES = [
+    # (B, H, N, d, dtype, causal, block_cols, groups_per_head)
+    (1, 2, 1000, 64, "bf16", True, 64, 1),
+    (2, 2, 777, 128, "bf16", False, 128, 0),
+    (1, 3, 513, 128, "fp16", True, 128, 2),
+    (2, 1, 300, 64, "fp16", False, 64, 3),
+    (1, 2, 4096, 128, "bf16", True, 128, 4),
+    (1, 1, 40, 64, "bf16", True, 128, 1),
+]
+
+
+@pytest.mark.parametrize("case", KVO_CASES, ids=lambda c: "B%d-H%d-N%d-d%d-%s-c%d-bc%d-G%d" % c)
+def test_kv_outer_forward_matrix(case):
+    """The key/value-outer forward (running O, m, l through device memory
+    after every key tile) against the fp64 oracle."""
+    B, H, N, d, dtype, causal, bc, G = case
+    print(f"[case] kv-outer fwd {case}", flush=True)
+    rng = np.random.default_rng(N + d + bc)
+    dt = DT[dtype]
+    q, k, v = (torch.from_numpy(rng.standard_normal((B, H, N, d))).to(dt) for _ in range(3))
+    o, lse = fa.fwd_kv_outer(cuda(q), cuda(k), cuda(v), causal=causal, block_cols=bc, groups_per_head=G)
+    torch.cuda.synchronize()
+    O, L = oracle.attn_fwd(q, k, v, 1.0 / np.sqrt(d), causal=causal)
+    res = dict(o=check_o(o, O, dt, "O(stored)", stored=True), lse=check_lse(lse, L, dt))
+    print(f"[ok] kv-outer {case} {res}", flush=True)

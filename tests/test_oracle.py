@@ -492,3 +492,18 @@ def test_kv_outer_io_counts_closed_form():
     steps = T * (T + 1) // 2
     assert io["read"]["Q"] == steps * b * d * H and io["read"]["O"] == steps * b * d * H
     assert io["read"]["K"] == N * d * H and io["write"]["l"] == (N + steps * b) * H
+
+
+def test_kv_outer_byte_model_matches_oracle_counts():
+    """bench.py's byte model of the key/value-outer order equals the oracle's
+    element counts of that order (same blocks: 128 query rows by bc keys),
+    weighted by the element sizes: e bytes for Q, K, V, O; 4 for l and m."""
+    import bench
+    d, e = 4, 2
+    for N, bc, causal in ((300, 64, True), (300, 128, False), (129, 64, True)):
+        x = np.zeros((1, 1, N, d))
+        _, _, io = oracle.kv_outer_fwd(x, x, x, 1.0, 128, bc, causal=causal)
+        _, _, mrd, mwr = bench.kv_outer_bytes(1, 1, N, d, e, causal, bc, 1)
+        r, w = io["read"], io["write"]
+        assert mrd == (r["Q"] + r["K"] + r["V"] + r["O"]) * e + (r["l"] + r["m"]) * 4
+        assert mwr == w["O"] * e + (w["l"] + w["m"]) * 4
