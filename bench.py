@@ -484,16 +484,38 @@ def decode_report(w, args, ev):
     print(json.dumps(out), flush=True)
 
 
+def host_info():
+    """Threads the oracle's BLAS uses, the CPU model and the BLAS library."""
+    import numpy
+    threads = None
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [0]) or None
+    except Exception:  # pragma: no cover
+        pass
+    if threads is None:
+        threads = len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else os.cpu_count()
+    cpu = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            cpu = next((l.split(":", 1)[1].strip() for l in f if l.startswith("model name")), cpu)
+    except OSError:  # pragma: no cover
+        pass
+    blas = "unknown"
+    try:
+        cfg = numpy.show_config(mode="dicts")["Build Dependencies"]["blas"]
+        blas = f"{cfg.get('name')} {cfg.get('version', '')}".strip()
+    except Exception:  # pragma: no cover
+        pass
+    return int(threads), cpu, blas
+
+
 def cpu_baseline_decode(w, bytes_per_call):
     """The fp64 oracle (untuned) on the whole decode workload, scaled to the
     same algorithmic bytes as the GPU figure."""
     import oracle
     import workloads as W
-    try:
-        from threadpoolctl import threadpool_info
-        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
-    except Exception:  # pragma: no cover
-        threads = os.cpu_count()
+    threads, cpu, blas = host_info()
     x = W.make_inputs(w, with_do=False)
     kl = None if x["key_lens"] is None else x["key_lens"].numpy()
     runs, t0 = 0, time.perf_counter()
@@ -501,8 +523,8 @@ def cpu_baseline_decode(w, bytes_per_call):
         oracle.decode_fwd(x["q"], x["k"], x["v"], w.scale, kv_lens=kl, causal=w.causal)
         runs += 1
     dt = (time.perf_counter() - t0) / runs
-    return {"value": round(bytes_per_call / dt / 1e9, 3), "unit": "GB/s", "cores": int(threads), "kind": "oracle",
-            "seconds": round(dt * runs, 2),
+    return {"value": round(bytes_per_call / dt / 1e9, 3), "unit": "GB/s", "cores": threads, "kind": "oracle",
+            "cpu": cpu, "blas": blas, "seconds": round(dt * runs, 2),
             "sample": f"fp64 numpy oracle decode over the whole workload ({w.B} sequences x {w.H} heads), "
                       f"{runs} calls, rated by the same bf16 algorithmic bytes"}
 
@@ -514,26 +536,33 @@ def cpu_baseline(w, rows):
     (O, LSE) and backward (dQ, dK, dV restricted to those rows' pairs)."""
     import oracle
     import workloads as W
-    try:
-        from threadpoolctl import threadpool_info
-        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
-    except Exception:  # pragma: no cover
-        threads = os.cpu_count()
+    threads, cpu, blas = host_info()
     x = W.make_inputs(w)
     R = min(rows, w.N)
     sub = {n: x[n][:, :, :R] for n in ("q", "k", "v", "do")}
     kl = None if x["key_lens"] is None else x["key_lens"].numpy()
     t0 = time.perf_counter()
     oracle.attn_fwd(sub["q"], sub["k"], sub["v"], w.scale, causal=w.causal, key_lens=kl)
+    t1 = time.perf_counter()
     oracle.attn_bwd(sub["q"], sub["k"], sub["v"], sub["do"], w.scale, causal=w.causal, key_lens=kl)
-    dt = time.perf_counter() - t0
+    t2 = time.perf_counter()
+    dt = t2 - t0
     pairs = oracle.valid_pair_count(R, w.B, w.H, w.causal, kl, None)
     flops = 14.0 * w.d * pairs
-    return {"value": round(flops / dt / 1e12, 6), "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
-            "seconds": round(dt, 2),
-            "sample": f"fp64 numpy oracle fwd+bwd over the leading {R} causal query rows of all "
-                      f"{w.B * w.H} heads (an exact sub-problem: causal rows < {R} see only keys < {R}); "
-                      f"{pairs} valid pairs, 14*d FLOP each"}
+    # the oracle is dense per row chunk (S over all keys, then masked), so its
+    # cost grows as rows x keys: the full problem is (N / R)^2 times the sample
+    full = dt * (w.N / R) ** 2
+    return {"value": round(flops / dt / 1e12, 6), "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+            "cpu": cpu, "blas": blas, "seconds": round(dt, 2),
+            "fwd_s": round(t1 - t0, 2), "bwd_s": round(t2 - t1, 2),
+            "fwd_gflops": round(4.0 * w.d * pairs / (t1 - t0) / 1e9, 2),
+            "bwd_gflops": round(10.0 * w.d * pairs / (t2 - t1) / 1e9, 2),
+            "extrapolated_full_s": round(full, 1),
+            "sample": f"fp64 numpy oracle fwd+bwd on the leading {R} rows and keys of all {w.B * w.H} heads"
+                      + (f" (an exact sub-problem: causal rows < {R} see only keys < {R})" if w.causal else
+                         " (the same attention at N = R)")
+                      + f"; {pairs} valid pairs, 14*d FLOP each; extrapolated_full_s scales the measured "
+                        f"time by (N/R)^2 (not measured)"}
 
 
 def main():
