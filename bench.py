@@ -568,8 +568,8 @@ def cpu_baseline(w, rows):
 def main():
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
-        print("bench.py measures one GPU: this build has no multi-GPU path (each (b, h) head is "
-              "independent; sharding over heads is described in DESIGN.md). Run with --gpus 1.",
+        print("bench.py measures one GPU: the library has no multi-GPU path (each (b, h) head is "
+              "independent, so a multi-GPU run would shard the heads with no communication). Run with --gpus 1.",
               file=sys.stderr)
         sys.exit(2)
     import torch
