@@ -21,7 +21,8 @@ The Weyl constants are the golden ratio and sqrt(3) - 1 as W-bit fractions
 multipliers for each word width.
 
 Counter layout and keep rule for attention element (b, h, i, j) -- a choice
-this build makes, since the pages are silent:
+of this library, which the FlashAttention explainer (kernel fusion, dropout)
+leaves open:
   counter = (j >> 2, i, b*H + h, lo32(rng_offset)), key = (lo32(seed), hi32(seed))
   r = output word (j & 3)
   keep iff r >= thr,  thr = min(floor(float32(p) * 2^32), 2^32 - 1)
