@@ -214,3 +214,27 @@ def test_kv_outer_validation_and_workspace():
     assert need == (1 * 2 * 300 * 64 * 4 + 255) // 256 * 256 + (1 * 2 * 300 * 8 + 255) // 256 * 256
     assert kvo(ws=None) == -8 and kvo(ws_bytes=need - 1) == -8 and kvo(ws=P + 64) == -8
     assert L.fa_fwd_kv_outer_workspace_bytes(1, 2, 300, 80) == 0
+
+
+def test_header_compiles_as_c_and_links(tmp_path):
+    """include/fa.h is a plain C99 header: a C program (tests/c_abi_check.c)
+    compiles against it with gcc, links libfa.so and sees every entry point
+    reject bad arguments on the host."""
+    _lib()
+    import shutil
+    gcc = shutil.which("gcc")
+    if gcc is None:
+        pytest.skip("gcc not available")
+    here = os.path.dirname(os.path.abspath(__file__))
+    root = os.path.dirname(here)
+    libdir = os.path.dirname(lib_mod.LIB_PATH)
+    exe = str(tmp_path / "c_abi_check")
+    cmd = [gcc, "-std=c99", "-Wall", "-Wextra", "-Werror", "-D__HIP_PLATFORM_AMD__",
+           "-I", os.path.join(root, "include"), "-I", "/opt/rocm/include",
+           "-o", exe, os.path.join(here, "c_abi_check.c"), "-L", libdir, "-l:libfa.so",
+           f"-Wl,-rpath,{libdir}"]
+    build = subprocess.run(cmd, capture_output=True, text=True)
+    assert build.returncode == 0, build.stderr
+    run = subprocess.run([exe], capture_output=True, text=True, timeout=60)
+    assert run.returncode == 0, run.stdout + run.stderr
+    assert "c abi ok" in run.stdout
