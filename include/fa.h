@@ -49,7 +49,9 @@
  *    1 <= B, H <= 65535 with N*d < 2^31 and B*H*N < 2^31; 0 <= p < 1;
  *    scale finite and > 0.
  *  - Entry points are thread-safe and keep no state between calls apart from
- *    a thread-local error string.
+ *    a thread-local error string.  They only launch kernels (and record the
+ *    optional timing events) on `stream`, so a call may be captured in a HIP
+ *    graph and replayed; the replays read the buffers' current contents.
  */
 #ifndef FA_H_
 #define FA_H_
