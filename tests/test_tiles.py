@@ -60,3 +60,28 @@ def test_valid_pair_count_brute_force(N):
 def test_valid_pairs_closed_forms():
     assert oracle.valid_pair_count(1024, 8, 12, causal=True) == 8 * 12 * 1024 * 1025 // 2
     assert oracle.valid_pair_count(16384, 1, 16, causal=True) == 2147614720
+
+
+def test_bench_work_counts_match_oracle():
+    """bench.py counts algorithmic work itself (its timed path does not
+    import the oracle): its valid-pair count equals the oracle's on every
+    workload's recipe at reduced size, and its decode byte count is the
+    closed form (valid cache rows of K and V, Q, O, LSE)."""
+    import bench
+    import workloads as W
+    for name in ("tiny", "gpt2", "bert", "long", "sparse", "gqa"):
+        w = W.WORKLOADS[name]
+        small = w.with_(B=min(w.B, 2), H=2, N=min(w.N, 640), d=8)
+        if small.key_len_range is not None:
+            small = small.with_(key_len_range=(100, 640))
+        x = W.make_inputs(small, with_do=False)
+        kl = None if x["key_lens"] is None else x["key_lens"].numpy()
+        bm = None if x["block_mask"] is None else x["block_mask"].numpy()
+        assert bench.valid_pairs(x, small) == oracle.valid_pair_count(small.N, small.B, small.H, small.causal,
+                                                                      kl, bm), name
+    w = W.WORKLOADS["decode"].with_(B=3, N=500, d=16, key_len_range=(10, 500))
+    x = W.make_inputs(w, with_do=False)
+    rd, wr = bench.decode_bytes(x, w)
+    L = x["key_lens"].numpy().astype(np.int64)
+    assert rd == int(L.sum()) * w.Hkv * w.d * 2 * 2 + w.B * w.H * 1 * w.d * 2
+    assert wr == w.B * w.H * 1 * (w.d * 2 + 4)
