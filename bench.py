@@ -149,6 +149,40 @@ def valid_pairs(x, w):
     return total * w.H
 
 
+def dominant_roofline(w, pairs, kernel_ms):
+    """The roofline object for the kernel with the largest average launch
+    time.  Algorithmic FLOPs per launch: fwd_kernel 4d per valid pair (S,
+    PV); bwd_kv_kernel 8d (S, dP, dV, dK); bwd_dq_kernel 2d (dQ; its
+    recomputed S and dP are extra work).  Minimum HBM bytes per launch (e =
+    element bytes; K, V, dK, dV have Hkv heads): fwd_kernel reads Q, K, V and
+    writes O, LSE; bwd_kv_kernel reads Q, K, V, dO, LSE, D and writes dK, dV;
+    bwd_dq_kernel reads the same and writes dQ.  A kernel whose FLOP per
+    minimum byte is below the ridge (peak FLOP/s / 8 TB/s) is rated against
+    HBM bandwidth, otherwise against the MFMA peak.  Returns (roofline,
+    {kernel: (ms, flop, bytes)})."""
+    peak = PEAK_TFLOPS[w.dtype]
+    e = {"bf16": 2, "fp16": 2, "fp32": 4}[w.dtype]
+    q_b = w.B * w.H * w.N * w.d * e
+    kv_b = w.B * w.Hkv * w.N * w.d * e
+    row_b = w.B * w.H * w.N * 4
+    kern = {"fwd_kernel": (kernel_ms["fwd_kernel"], 4.0 * w.d * pairs, 2 * q_b + 2 * kv_b + row_b),
+            "bwd_kv_kernel": (kernel_ms["bwd_kv_kernel"], 8.0 * w.d * pairs, 2 * q_b + 4 * kv_b + 2 * row_b),
+            "bwd_dq_kernel": (kernel_ms["bwd_dq_kernel"], 2.0 * w.d * pairs, 3 * q_b + 2 * kv_b + 2 * row_b)}
+    dom = max(kern, key=lambda k: kern[k][0])
+    dom_ms, dom_flop, dom_bytes = kern[dom]
+    ridge = peak * 1e12 / (HBM_GBPS * 1e9)
+    if dom_flop / dom_bytes >= ridge:
+        roofline = {"bound": "mfma", "kernel": dom, "achieved": round(dom_flop / (dom_ms * 1e-3) / 1e12, 2),
+                    "peak": peak, "unit": "TFLOP/s"}
+    else:
+        roofline = {"bound": "hbm", "kernel": dom, "achieved": round(dom_bytes / (dom_ms * 1e-3) / 1e9, 1),
+                    "peak": HBM_GBPS, "unit": "GB/s"}
+    roofline.update(frac=round(roofline["achieved"] / roofline["peak"], 4), traffic=measured_traffic(dom, w.name),
+                    avg_launch_ms=round(dom_ms, 4), flop_per_launch=dom_flop, min_bytes_per_launch=dom_bytes,
+                    flop_per_byte=round(dom_flop / dom_bytes, 1))
+    return roofline, kern
+
+
 def time_workload(w, steps, warmup, ev):
     import torch
     import io_aware_exact_tiled_amd as fa
@@ -600,15 +634,9 @@ def main():
     total_tflops = (fwd_flop + bwd_flop) / (step_ms * 1e-3) / 1e12
     fwd_tf = fwd_flop / (fwd_ms * 1e-3) / 1e12
     bwd_tf = bwd_flop / (bwd_ms * 1e-3) / 1e12
-    # dominant kernel: the one with the largest average launch time.  Algorithmic
-    # FLOPs per launch: fwd_kernel 4d per valid pair (S, PV); bwd_kv_kernel 8d
-    # (S, dP, dV, dK); bwd_dq_kernel 2d (dQ; its recomputed S and dP are extra work)
-    kern = {"fwd_kernel": (float(np.mean(r["fwd_ms"])), fwd_flop),
-            "bwd_kv_kernel": (float(np.mean(r["kv_ms"])), 8.0 * w.d * r["pairs"]),
-            "bwd_dq_kernel": (float(np.mean(r["dq_ms"])), 2.0 * w.d * r["pairs"])}
-    dom = max(kern, key=lambda k: kern[k][0])
-    dom_ms, dom_flop = kern[dom]
-    achieved = dom_flop / (dom_ms * 1e-3) / 1e12
+    roofline, kern = dominant_roofline(w, r["pairs"], {"fwd_kernel": float(np.mean(r["fwd_ms"])),
+                                                       "bwd_kv_kernel": float(np.mean(r["kv_ms"])),
+                                                       "bwd_dq_kernel": float(np.mean(r["dq_ms"]))})
     out = {
         "metric": "attention fwd/bwd TFLOP/s (bf16, d=64/128, N 1K-16K), % of MFMA peak",
         "value": round(total_tflops, 2),
@@ -630,10 +658,8 @@ def main():
         "bwd_tflops": round(bwd_tf, 2), "bwd_pct_peak": round(100 * bwd_tf / peak, 2), "bwd_ms": round(bwd_ms, 4),
         "fwd_kernel_ms": round(med(r["fwd_ms"]), 4), "bwd_main_ms": round(med(r["bwd_main_ms"]), 4),
         "bwd_kv_ms": round(med(r["kv_ms"]), 4), "bwd_dq_ms": round(med(r["dq_ms"]), 4),
-        "roofline": {"bound": "mfma", "kernel": dom, "achieved": round(achieved, 2), "peak": peak,
-                     "unit": "TFLOP/s", "frac": round(achieved / peak, 4),
-                     "traffic": measured_traffic(dom, w.name),
-                     "avg_launch_ms": round(dom_ms, 4), "flop_per_launch": dom_flop},
+        "fwd_hbm_gbps": round(kern["fwd_kernel"][2] / (fwd_ms * 1e-3) / 1e9, 1),
+        "roofline": roofline,
         "wall_s": round(r["wall_s"], 3),
     }
     if not args.no_cpu_baseline:

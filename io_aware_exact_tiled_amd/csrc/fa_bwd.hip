@@ -98,12 +98,16 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(BwdArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// dK, dV: key-stationary, with specialised waves.  Eight waves per workgroup,
-// two per block of 32 keys (waves w and w+4 share a SIMD):
-//   A (w < 4):  holds K_j; S = Q K^T, P = exp(S - LSE) with the masks, hands P
-//               to its partner through LDS, dV_j += (P o Z/(1-p))^T dO.
-//   B (w >= 4): holds V_j; dP = dO V^T, then with P from its partner
-//               dS = P o (dP o Z/(1-p) - D), dK_j += dS^T Q.
+// dK, dV: key-stationary, with specialised waves.  NW waves per workgroup,
+// two per block of 32 keys (waves w and w + NW/2 share a SIMD):
+//   A (w < NW/2):  holds K_j; S = Q K^T, P = exp(S - LSE) with the masks,
+//                  hands P to its partner through LDS, dV_j += (P o Z/(1-p))^T dO.
+//   B (w >= NW/2): holds V_j; dP = dO V^T, then with P from its partner
+//                  dS = P o (dP o Z/(1-p) - D), dK_j += dS^T Q.
+// NW = 8 (128 keys per workgroup, one workgroup per CU) for long sequences;
+// NW = 4 with 32-row query steps (64 keys, 48 KB of LDS: two workgroups per
+// CU) for short ones, where a lone workgroup per CU leaves its prologue and
+// epilogue latency exposed.
 // Each wave keeps one operand block and one accumulator block, so two waves
 // fit on a SIMD.  A and B hold the same (key, query) elements in the same
 // lane and register, so the hand-off is a plain per-lane copy.
@@ -114,13 +118,12 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(BwdArgs a) {
 //   B:  dP(n) MFMA    dK += dS(n-1)^T Q(n-1)  |  dS(n) from P(n), in regs    |
 // so B's dK product overlaps A's exponentials and A's dV product overlaps
 // B's dS arithmetic.  Q tiles stay in LDS one step longer (three buffers).
-template <class T, int D, bool DROP>
-__global__ __launch_bounds__(512, 1) void bwd_kv_kernel(BwdArgs a) {
+template <class T, int D, bool DROP, int NW, int BR>
+__global__ __launch_bounds__(NW * 64, NW == 8 ? 1 : 2) void bwd_kv_kernel(BwdArgs a) {
     typedef Mma<T> MM;
-    constexpr int NW = 8;
     constexpr int E = MM::E;
-    constexpr int BR = BwdTiles<T>::KV_BR;        // query rows per step
-    constexpr int BC = BWD_KV_BC;                 // keys per workgroup
+    constexpr int NKB = NW / 2;                   // 32-key blocks per workgroup
+    constexpr int BC = 32 * NKB;                  // keys per workgroup
     constexpr int QB = BR / 32;                   // 32-row query blocks per step
     constexpr int KS = D / (2 * E);               // MFMA steps over d
     constexpr int DB = D / 32;
@@ -134,12 +137,12 @@ __global__ __launch_bounds__(512, 1) void bwd_kv_kernel(BwdArgs a) {
     __shared__ __attribute__((aligned(16))) float sLse[2 * BR];
     __shared__ __attribute__((aligned(16))) float sDel[2 * BR];
     // hand-off [key block][plane][query block][4 chunks][64 lanes] x f32x4
-    __shared__ __attribute__((aligned(16))) f32x4 sX[4 * NX * QB * 4 * 64];
+    __shared__ __attribute__((aligned(16))) f32x4 sX[NKB * NX * QB * 4 * 64];
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int hl = lane >> 5, ln = lane & 31;
-    const int kb = wave & 3;                      // key block of this wave
-    const bool roleA = wave < 4;
+    const int kb = wave % NKB;                    // key block of this wave
+    const bool roleA = wave < NKB;
     const int N = a.N, H = a.H, Hkv = a.Hkv, G = H / Hkv;
     const int Tr = (N + BR - 1) / BR, Tc = (N + BC - 1) / BC;
     const int total = Tc * Hkv * a.B;
@@ -538,11 +541,20 @@ hipError_t launch_t(const BwdArgs& a, hipStream_t s) {
     hipError_t e = hipLaunchKernel((const void*)&bwd_pre_kernel<T, D>, dim3((unsigned)((rows + RPB - 1) / RPB)),
                                    dim3(256), args, 0, s);
     if (e != hipSuccess) return e;
-    const int kv_total = ((a.N + BWD_KV_BC - 1) / BWD_KV_BC) * a.Hkv * a.B;
+    // the dK/dV configuration (16-bit inputs): 64-key workgroups at d = 64
+    // and for causal sequences up to BWD_KV_SMALL_N, where they were measured
+    // faster (never while tile visits are recorded: that map has 128-key tiles)
+    const bool small = sizeof(T) == 2 && !a.tile_visits && (D == 64 || (a.mask.causal && a.N <= BWD_KV_SMALL_N));
+    const int kbc = small ? BWD_KV_BC / 2 : BWD_KV_BC;
+    const int kv_total = ((a.N + kbc - 1) / kbc) * a.Hkv * a.B;
     const int dq_total = ((a.N + BWD_DQ_BR - 1) / BWD_DQ_BR) * a.H * a.B;
     if (a.ev_begin && (e = hipEventRecord(a.ev_begin, s)) != hipSuccess) return e;
-    e = hipLaunchKernel((const void*)&bwd_kv_kernel<T, D, DROP>, dim3((unsigned)(8 * ((kv_total + 7) / 8))),
-                        dim3(512), args, 0, s);
+    const dim3 kv_grid((unsigned)(8 * ((kv_total + 7) / 8)));
+    if (small)
+        e = hipLaunchKernel((const void*)&bwd_kv_kernel<T, D, DROP, 4, 32>, kv_grid, dim3(256), args, 0, s);
+    else
+        e = hipLaunchKernel((const void*)&bwd_kv_kernel<T, D, DROP, 8, BwdTiles<T>::KV_BR>, kv_grid, dim3(512),
+                            args, 0, s);
     if (e != hipSuccess) return e;
     if (a.ev_mid && (e = hipEventRecord(a.ev_mid, s)) != hipSuccess) return e;
     e = hipLaunchKernel((const void*)&bwd_dq_kernel<T, D, DROP>, dim3((unsigned)(8 * ((dq_total + 7) / 8))),

@@ -12,14 +12,18 @@ namespace fa {
 
 // Tile shapes (query rows x keys).  Forward: a workgroup owns FWD_BR query
 // rows (4 waves x 32) and walks key tiles of FWD_BC.  Backward dK/dV kernel: a
-// workgroup owns BWD_KV_BC keys (4 waves x 32) and walks query tiles of
-// BwdTiles<T>::KV_BR rows.  Backward dQ kernel: a workgroup owns BWD_DQ_BR
+// workgroup owns BWD_KV_BC keys (8 waves: 4 key blocks of 32 x 2 roles) and
+// walks query tiles of BwdTiles<T>::KV_BR rows -- or, for 16-bit inputs at
+// d = 64 and for short causal sequences, half that (4 waves, 64 keys,
+// 32-row query tiles; not while tile visits are recorded).  Backward dQ
+// kernel: a workgroup owns BWD_DQ_BR
 // query rows and walks key tiles of BWD_DQ_BC.  All divide the 128-token
 // block-mask tile.
 constexpr int MASK_TILE = 128;   // block-mask granularity (tokens)
 constexpr int FWD_BR = 128;
 constexpr int FWD_BC = 64;
 constexpr int BWD_KV_BC = 128;
+constexpr int BWD_KV_SMALL_N = 2048;      // d = 128 causal N at or below this: 64-key dK/dV workgroups
 constexpr int BWD_KV_BR16 = 64;  // 16-bit inputs
 constexpr int BWD_KV_BR32 = 32;  // fp32 inputs (LDS budget of the double buffer)
 constexpr int BWD_DQ_BR = 128;

@@ -85,3 +85,21 @@ def test_bench_work_counts_match_oracle():
     L = x["key_lens"].numpy().astype(np.int64)
     assert rd == int(L.sum()) * w.Hkv * w.d * 2 * 2 + w.B * w.H * 1 * w.d * 2
     assert wr == w.B * w.H * 1 * (w.d * 2 + 4)
+
+
+def test_bench_roofline_bound_follows_intensity():
+    """The dominant kernel is rated against HBM when its FLOP per minimum byte
+    is below the ridge (2.5 PFLOP/s / 8 TB/s = 312.5), else against MFMA: the
+    BERT-shaped workload (d = 64, N = 512, padded keys) is HBM-bound, the long
+    causal one MFMA-bound (the pages' own classification of the configs)."""
+    import bench
+    import workloads as W
+    ms = {"fwd_kernel": 1.0, "bwd_kv_kernel": 2.0, "bwd_dq_kernel": 1.5}
+    long = W.WORKLOADS["long"]
+    r, k = bench.dominant_roofline(long, oracle.valid_pair_count(long.N, long.B, long.H, True), ms)
+    assert r["bound"] == "mfma" and r["kernel"] == "bwd_kv_kernel" and r["unit"] == "TFLOP/s"
+    assert k["fwd_kernel"][2] == 4 * 16 * 16384 * 128 * 2 + 16 * 16384 * 4     # 4 BHNd e + 4 BHN
+    bert = W.WORKLOADS["bert"]
+    pairs = bert.H * 320 * bert.B * bert.N                                      # E[len] = 320
+    r, _ = bench.dominant_roofline(bert, pairs, ms)
+    assert r["bound"] == "hbm" and r["unit"] == "GB/s" and r["flop_per_byte"] < 312.5
