@@ -145,9 +145,9 @@ __global__ __launch_bounds__(NW * 64, NW == 8 ? 1 : 2) void bwd_kv_kernel(BwdArg
     const bool roleA = wave < NKB;
     const int N = a.N, H = a.H, Hkv = a.Hkv, G = H / Hkv;
     const int Tr = (N + BR - 1) / BR, Tc = (N + BC - 1) / BC;
-    const int total = Tc * Hkv * a.B;
-    const int item = xcd_item((int)blockIdx.x, (total + 7) / 8);
-    if (item >= total) return;
+    // key tile jt = 0 visits the most query tiles under the causal mask
+    const int item = xcd_item((int)blockIdx.x, Hkv * a.B, Tc, a.mask.causal);
+    if (item < 0) return;
     const int bkv = item / Tc;                    // (b, K/V head)
     const int bidx = bkv / Hkv, g = bkv % Hkv;
     const int jt = item % Tc;                     // key tile of this workgroup
@@ -400,9 +400,8 @@ __global__ __launch_bounds__(256, sizeof(T) == 4 ? 1 : 2) void bwd_dq_kernel(Bwd
     const int hl = lane >> 5, ln = lane & 31;
     const int N = a.N, H = a.H;
     const int Tr = (N + BR - 1) / BR, Tc = (N + BC - 1) / BC;
-    const int total = Tr * H * a.B;
-    const int item = xcd_item((int)blockIdx.x, (total + 7) / 8);
-    if (item >= total) return;
+    const int item = xcd_item((int)blockIdx.x, H * a.B, Tr, a.mask.causal);
+    if (item < 0) return;
     const int bhi = item / Tr, r_ = item % Tr;
     const int it = a.mask.causal ? (Tr - 1 - r_) : r_;
     const int q0 = it * BR, qw0 = q0 + wave * 32;

@@ -381,11 +381,24 @@ __device__ inline void tr_chain(f32x16 (&acc)[D / 32], const T* tile, const TrOf
     }
 }
 
-// Map a linear workgroup id to a work item so that each of the 8 XCDs (which
-// receive workgroups round-robin and have their own L2) works on a contiguous
-// range of items.  `per` = ceil(total / 8); the grid has 8 * per workgroups
-// and ids whose item is >= total do nothing.
-__device__ inline int xcd_item(int wg, int per) { return (wg & 7) * per + (wg >> 3); }
+// Map a linear workgroup id to a work item (head * per_head + rank, rank 0 the
+// heaviest item of its head) so that each of the 8 XCDs -- which receive
+// workgroups round-robin and have their own L2 -- works on one contiguous range
+// of heads.  The grid has 8 * ceil(heads * per_head / 8) workgroups; ids with
+// no item get -1.  Inside an XCD's range the items are dispatched head by head,
+// or, with `by_rank` and a head count that splits evenly over the XCDs, rank by
+// rank (the heaviest item of every head in the range first), so that when the
+// range holds many short heads no heavy item is left to start last.
+__device__ inline int xcd_item(int wg, int heads, int per_head, bool by_rank) {
+    const int x = wg & 7, k = wg >> 3;
+    if (by_rank && heads % 8 == 0) {
+        const int nh = heads / 8;                      // heads per XCD; k < nh * per_head
+        return (x * nh + k % nh) * per_head + k / nh;
+    }
+    const int total = heads * per_head;
+    const int item = x * ((total + 7) / 8) + k;
+    return item < total ? item : -1;
+}
 
 // Four floats stored as one 8- or 16-byte vector of T.
 template <class T> __device__ inline void store4(T* p, float a, float b, float c, float d);

@@ -127,10 +127,9 @@ __global__ __launch_bounds__(256, sizeof(T) == 4 ? 1 : 2) void fwd_kernel(FwdArg
     const int hl = lane >> 5, ln = lane & 31;
     const int N = a.N, H = a.H;
     const int Tr = (N + BR - 1) / BR, Tc = (N + BC - 1) / BC;
-    // work item: contiguous ranges per XCD; inside a head, heaviest tiles first
-    const int total = Tr * H * a.B;
-    const int item = xcd_item((int)blockIdx.x, (total + 7) / 8);
-    if (item >= total) return;
+    // work item: contiguous head ranges per XCD; inside a head, heaviest tiles first
+    const int item = xcd_item((int)blockIdx.x, H * a.B, Tr, a.mask.causal);
+    if (item < 0) return;
     const int bhi = item / Tr, r_ = item % Tr;
     const int it = a.mask.causal ? (Tr - 1 - r_) : r_;
     const int q0 = it * BR, qw0 = q0 + wave * 32;
