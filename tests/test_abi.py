@@ -238,3 +238,22 @@ def test_header_compiles_as_c_and_links(tmp_path):
     run = subprocess.run([exe], capture_output=True, text=True, timeout=60)
     assert run.returncode == 0, run.stdout + run.stderr
     assert "c abi ok" in run.stdout
+
+
+def test_ceiling_probe_builds_for_gfx950(tmp_path):
+    """bench_ceiling.hip (the MFMA ceiling probe quoted beside the roofline)
+    still compiles for gfx950 with the library's flags; its device code
+    issues the 32x32x16 MFMAs and 16-byte LDS reads it is meant to time."""
+    import shutil
+    hipcc = shutil.which("hipcc") or "/opt/rocm/bin/hipcc"
+    if not os.path.exists(hipcc):
+        pytest.skip("hipcc not available")
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    asm = str(tmp_path / "ceiling.s")
+    cmd = [hipcc, "-O3", "--offload-arch=gfx950", "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+           "--cuda-device-only", "-S", os.path.join(root, "bench_ceiling.hip"), "-o", asm]
+    build = subprocess.run(cmd, capture_output=True, text=True)
+    assert build.returncode == 0, build.stderr
+    text = open(asm).read()
+    assert "v_mfma_f32_32x32x16_bf16" in text and "v_mfma_f32_32x32x16_f16" in text
+    assert "ds_read_b128" in text and "v_exp_f32" in text
