@@ -130,14 +130,21 @@ __global__ __launch_bounds__(NW * 64, NW == 8 ? 1 : 2) void bwd_kv_kernel(BwdArg
     constexpr int QU = 16 / E;                    // MFMA steps over 16 queries of a lane half
     constexpr int TQ = BR * D;                    // elements per staged tensor
     constexpr int NX = DROP ? 2 : 1;              // hand-off planes: P (and P o Z / (1-p))
+    // The eight-wave configuration with 16-bit inputs hands P over already
+    // packed as the dV operand (QU 16-byte fragments per 32-row block): half
+    // the hand-off bytes in the LDS-bound long-sequence case.  The four-wave
+    // one (and fp32) hands over four f32x4 chunks: there the packed form's
+    // extra registers cost a wave per SIMD.
+    constexpr bool PACKED = sizeof(T) == 2 && NW == 8;
+    constexpr int XCH = PACKED ? QU : 4;          // 16-byte hand-off slots per lane per query block
     typedef SwzTr<T, D> LQ;    // Q, dO: BR rows (MFMA row order) x D
 
     __shared__ __attribute__((aligned(16))) T sQ[3 * TQ];
     __shared__ __attribute__((aligned(16))) T sdO[2 * TQ];
     __shared__ __attribute__((aligned(16))) float sLse[2 * BR];
     __shared__ __attribute__((aligned(16))) float sDel[2 * BR];
-    // hand-off [key block][plane][query block][4 chunks][64 lanes] x f32x4
-    __shared__ __attribute__((aligned(16))) f32x4 sX[NKB * NX * QB * 4 * 64];
+    // hand-off [key block][plane][query block][XCH slots][64 lanes] x 16 bytes
+    __shared__ __attribute__((aligned(16))) f32x4 sX[NKB * NX * QB * XCH * 64];
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int hl = lane >> 5, ln = lane & 31;
@@ -206,12 +213,16 @@ __global__ __launch_bounds__(NW * 64, NW == 8 ? 1 : 2) void bwd_kv_kernel(BwdArg
         else if (tid < 2 * BR) sDel[obuf * BR + tid - BR] = lreg;
     };
     auto xslot = [&](int plane, int qb, int chunk) -> f32x4* {
-        return &sX[(((kb * NX + plane) * QB + qb) * 4 + chunk) * 64 + lane];
+        return &sX[(((kb * NX + plane) * QB + qb) * XCH + chunk) * 64 + lane];
+    };
+    auto xfrag = [&](int plane, int qb, int u) -> typename MM::frag* {
+        return reinterpret_cast<typename MM::frag*>(xslot(plane, qb, u));
     };
     // B: dK_j += dS^T Q over one query tile; dS as packed A operands (query
     // block qb, 16-query step u), Q read transposed from its LDS buffer
     const TrOffsets<T, D> tro(lane);
     typename MM::frag dsf[QB][QU];
+    typename MM::frag pf[QB][QU];        // A (16-bit inputs): P packed, the dV operand
     auto dk_product = [&](const T* q) __attribute__((always_inline)) {
         tr_chain<T, D, QB, false, 2>(acc, q, tro, [&](int qb, int u) { return dsf[qb][u]; }, lane);
     };
@@ -289,24 +300,43 @@ __global__ __launch_bounds__(NW * 64, NW == 8 ? 1 : 2) void bwd_kv_kernel(BwdArg
                         if (qq >= N || krow >= kend || (causal && krow > qq)) p[r] = 0.0f;
                     }
                 }
+                if constexpr (PACKED) {
+                    // one packing serves both the hand-off and this wave's dV operand
 #pragma unroll
-                for (int g = 0; g < 4; ++g) {
-                    const f32x4 v4 = {p[4 * g], p[4 * g + 1], p[4 * g + 2], p[4 * g + 3]};
-                    *xslot(0, qb, g) = v4;
+                    for (int u = 0; u < QU; ++u) {
+                        pf[qb][u] = pack_p<T>(&p[u * E]);
+                        *xfrag(0, qb, u) = pf[qb][u];
+                    }
+                } else {
+#pragma unroll
+                    for (int g = 0; g < 4; ++g) {
+                        const f32x4 v4 = {p[4 * g], p[4 * g + 1], p[4 * g + 2], p[4 * g + 3]};
+                        *xslot(0, qb, g) = v4;
+                    }
                 }
                 if constexpr (DROP) {
                     const uint32_t keep = keep16_quad((uint32_t)krow, (uint32_t)(q0 + qr0), (uint32_t)bh, a.drop.off,
                                                       a.drop.k0, a.drop.k1, a.drop.thr, lane);
 #pragma unroll
                     for (int r = 0; r < 16; ++r) p[r] *= ((keep >> r) & 1u) ? a.drop.keep_scale : 0.0f;
+                    if constexpr (PACKED) {
 #pragma unroll
-                    for (int g = 0; g < 4; ++g) {
-                        const f32x4 v4 = {p[4 * g], p[4 * g + 1], p[4 * g + 2], p[4 * g + 3]};
-                        *xslot(1, qb, g) = v4;
+                        for (int u = 0; u < QU; ++u) {
+                            pf[qb][u] = pack_p<T>(&p[u * E]);
+                            *xfrag(1, qb, u) = pf[qb][u];
+                        }
+                    } else {
+#pragma unroll
+                        for (int g = 0; g < 4; ++g) {
+                            const f32x4 v4 = {p[4 * g], p[4 * g + 1], p[4 * g + 2], p[4 * g + 3]};
+                            *xslot(1, qb, g) = v4;
+                        }
                     }
                 }
+                if constexpr (!PACKED) {
 #pragma unroll
-                for (int r = 0; r < 16; ++r) sp[qb][r] = p[r];
+                    for (int r = 0; r < 16; ++r) sp[qb][r] = p[r];
+                }
             }
         } else if (have_prev) {
             // the previous step's dK product, while A computes P
@@ -319,10 +349,14 @@ __global__ __launch_bounds__(NW * 64, NW == 8 ? 1 : 2) void bwd_kv_kernel(BwdArg
             // dV_j += Pd^T dO
             __builtin_amdgcn_s_setprio(1);
             tr_chain<T, D, QB, false, 2>(acc, o, tro, [&](int qb, int u) {
-                float pr[E];
+                if constexpr (PACKED) {
+                    return pf[qb][u];
+                } else {
+                    float pr[E];
 #pragma unroll
-                for (int e = 0; e < E; ++e) pr[e] = sp[qb][u * E + e];
-                return pack_p<T>(pr);
+                    for (int e = 0; e < E; ++e) pr[e] = sp[qb][u * E + e];
+                    return pack_p<T>(pr);
+                }
             }, lane);
             __builtin_amdgcn_s_setprio(0);
         } else {
@@ -331,18 +365,44 @@ __global__ __launch_bounds__(NW * 64, NW == 8 ? 1 : 2) void bwd_kv_kernel(BwdArg
             for (int qb = 0; qb < QB; ++qb) {
                 const int qr0 = qb * 32 + hl * 16;
                 float ds[16];
+                if constexpr (PACKED) {
+                    // P (and Pd = P o Z/(1-p)) of the 16 queries from the packed fragments
+                    float pv[16], pdv[16];
 #pragma unroll
-                for (int g = 0; g < 4; ++g) {
-                    const f32x4 p4 = *xslot(0, qb, g);
-                    const f32x4 d4 = *reinterpret_cast<const f32x4*>(dl + qr0 + 4 * g);
-                    if constexpr (DROP) {
-                        // dS = P dP_hat Z/(1-p) - P D = Pd dP_hat - P D
-                        const f32x4 pd4 = *xslot(1, qb, g);
+                    for (int u = 0; u < QU; ++u) {
+                        const typename MM::frag f = *xfrag(0, qb, u);
 #pragma unroll
-                        for (int e = 0; e < 4; ++e) ds[4 * g + e] = pd4[e] * sp[qb][4 * g + e] - p4[e] * d4[e];
-                    } else {
+                        for (int e = 0; e < E; ++e) pv[u * E + e] = (float)f[e];
+                        if constexpr (DROP) {
+                            const typename MM::frag fd = *xfrag(1, qb, u);
 #pragma unroll
-                        for (int e = 0; e < 4; ++e) ds[4 * g + e] = p4[e] * (sp[qb][4 * g + e] - d4[e]);
+                            for (int e = 0; e < E; ++e) pdv[u * E + e] = (float)fd[e];
+                        }
+                    }
+#pragma unroll
+                    for (int g = 0; g < 4; ++g) {
+                        const f32x4 d4 = *reinterpret_cast<const f32x4*>(dl + qr0 + 4 * g);
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) {
+                            const int r = 4 * g + e;
+                            if constexpr (DROP) ds[r] = pdv[r] * sp[qb][r] - pv[r] * d4[e];   // Pd dP_hat - P D
+                            else ds[r] = pv[r] * (sp[qb][r] - d4[e]);
+                        }
+                    }
+                } else {
+#pragma unroll
+                    for (int g = 0; g < 4; ++g) {
+                        const f32x4 p4 = *xslot(0, qb, g);
+                        const f32x4 d4 = *reinterpret_cast<const f32x4*>(dl + qr0 + 4 * g);
+                        if constexpr (DROP) {
+                            // dS = P dP_hat Z/(1-p) - P D = Pd dP_hat - P D
+                            const f32x4 pd4 = *xslot(1, qb, g);
+#pragma unroll
+                            for (int e = 0; e < 4; ++e) ds[4 * g + e] = pd4[e] * sp[qb][4 * g + e] - p4[e] * d4[e];
+                        } else {
+#pragma unroll
+                            for (int e = 0; e < 4; ++e) ds[4 * g + e] = p4[e] * (sp[qb][4 * g + e] - d4[e]);
+                        }
                     }
                 }
 #pragma unroll
@@ -549,11 +609,11 @@ hipError_t launch_t(const BwdArgs& a, hipStream_t s) {
     const int dq_total = ((a.N + BWD_DQ_BR - 1) / BWD_DQ_BR) * a.H * a.B;
     if (a.ev_begin && (e = hipEventRecord(a.ev_begin, s)) != hipSuccess) return e;
     const dim3 kv_grid((unsigned)(8 * ((kv_total + 7) / 8)));
-    if (small)
-        e = hipLaunchKernel((const void*)&bwd_kv_kernel<T, D, DROP, 4, 32>, kv_grid, dim3(256), args, 0, s);
-    else
-        e = hipLaunchKernel((const void*)&bwd_kv_kernel<T, D, DROP, 8, BwdTiles<T>::KV_BR>, kv_grid, dim3(512),
-                            args, 0, s);
+    const void* kv_fn = (const void*)&bwd_kv_kernel<T, D, DROP, 8, BwdTiles<T>::KV_BR>;
+    if constexpr (sizeof(T) == 2) {
+        if (small) kv_fn = (const void*)&bwd_kv_kernel<T, D, DROP, 4, 32>;
+    }
+    e = hipLaunchKernel(kv_fn, kv_grid, dim3(small ? 256 : 512), args, 0, s);
     if (e != hipSuccess) return e;
     if (a.ev_mid && (e = hipEventRecord(a.ev_mid, s)) != hipSuccess) return e;
     e = hipLaunchKernel((const void*)&bwd_dq_kernel<T, D, DROP>, dim3((unsigned)(8 * ((dq_total + 7) / 8))),

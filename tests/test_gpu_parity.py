@@ -64,6 +64,11 @@ CASES = [
     (130, 128, "fp32", False, None, False, 0.25),
     (513, 64, "bf16", True, None, False, 0.0),
     (640, 128, "fp16", False, None, False, 0.0),
+    # d = 128 beyond the short-causal range: the eight-wave dK/dV kernel, whose
+    # 16-bit hand-off of P (and of P o Z/(1-p)) is packed
+    (200, 128, "bf16", False, "mixed", False, 0.15),
+    (96, 128, "fp16", False, None, True, 0.3),
+    (2100, 128, "bf16", True, None, False, 0.1),
 ]
 
 
