@@ -22,10 +22,14 @@ multipliers for each word width.
 
 Counter layout and keep rule for attention element (b, h, i, j) -- a choice
 of this library, which the FlashAttention explainer (kernel fusion, dropout)
-leaves open:
-  counter = (j >> 2, i, b*H + h, lo32(rng_offset)), key = (lo32(seed), hi32(seed))
-  r = output word (j & 3)
-  keep iff r >= thr,  thr = min(floor(float32(p) * 2^32), 2^32 - 1)
+leaves open.  One generator call decides a block of 4 keys x 2 query rows:
+each of its four 32-bit output words holds two 16-bit uniforms, the low half
+for the even row of the pair and the high half for the odd one:
+  counter = (j >> 2, i >> 1, b*H + h, lo32(rng_offset)), key = (lo32(seed), hi32(seed))
+  w = output word (j & 3),  u = (w >> 16) if i is odd else (w & 0xFFFF)
+  keep iff u >= thr,  thr = min(floor(float32(p) * 2^16), 2^16 - 1)
+so the drop probability is thr / 2^16, within 2^-16 of p.  Kept entries are
+scaled by 1 / (1 - p) whenever p > 0.
 """
 
 from __future__ import annotations
@@ -81,10 +85,10 @@ def philox4x32_10(c0, c1, c2, c3, k0, k1):
 
 
 def dropout_threshold(p: float) -> int:
-    """Integer threshold on a uniform 32-bit word: drop iff r < thr.
+    """Integer threshold on a uniform 16-bit value: drop iff u < thr.
     Computed from the float32 value of p, as the kernels receive it."""
     p32 = float(np.float32(p))
-    return min(int(np.floor(p32 * 2.0 ** 32)), 2 ** 32 - 1)
+    return min(int(np.floor(p32 * 2.0 ** 16)), 2 ** 16 - 1)
 
 
 def keep_mask(seed: int, rng_offset: int, p: float, b: int, h: int, H: int,
@@ -99,10 +103,12 @@ def keep_mask(seed: int, rng_offset: int, p: float, b: int, h: int, H: int,
     seed = int(seed) & 0xFFFFFFFFFFFFFFFF
     k0, k1 = seed & 0xFFFFFFFF, seed >> 32
     c0 = (cols >> np.uint64(2))[None, :]
-    c1 = rows[:, None]
+    c1 = (rows >> np.uint64(1))[:, None]
     c2 = np.uint64(b * H + h)
     c3 = np.uint64(int(rng_offset) & 0xFFFFFFFF)
     words = philox4x32_10(c0, c1, c2, c3, k0, k1)
     sel = (cols & np.uint64(3)).astype(np.int64)[None, :]
-    r = np.choose(np.broadcast_to(sel, words[0].shape), words)
-    return r.astype(np.uint64) >= np.uint64(thr)
+    w = np.choose(np.broadcast_to(sel, words[0].shape), words).astype(np.uint64)
+    shift = ((rows & np.uint64(1)) * np.uint64(16))[:, None]
+    u = (w >> shift) & np.uint64(0xFFFF)
+    return u >= np.uint64(thr)

@@ -61,24 +61,27 @@ def test_numpy_matches_independent_c_implementation():
 
 
 def test_threshold_from_float32_p():
-    assert philox.dropout_threshold(0.1) == 429496736      # float32(0.1) * 2^32, floored
+    assert philox.dropout_threshold(0.1) == 6553           # float32(0.1) * 2^16 = 6553.6..., floored
     assert philox.dropout_threshold(0.0) == 0
-    assert philox.dropout_threshold(0.5) == 2 ** 31
-    assert philox.dropout_threshold(np.nextafter(np.float32(1), np.float32(0))) == 2 ** 32 - 256
+    assert philox.dropout_threshold(0.5) == 2 ** 15
+    assert philox.dropout_threshold(0.25) == 2 ** 14
+    assert philox.dropout_threshold(2.0 ** -17) == 0       # below one step of 2^-16
+    assert philox.dropout_threshold(np.nextafter(np.float32(1), np.float32(0))) == 2 ** 16 - 1
 
 
 def test_keep_mask_counter_layout_elementwise():
     """keep_mask equals the documented counter layout evaluated one element at a time."""
     seed, off, p, H = 0x1234_5678_9ABC_DEF0, 0x1_0000_0007, 0.3, 3
-    rows, cols = np.array([0, 1, 77, 511]), np.arange(0, 23)
+    rows, cols = np.array([0, 1, 2, 77, 510, 511]), np.arange(0, 23)
     thr = philox.dropout_threshold(p)
     for b, h in ((0, 0), (2, 1)):
         km = philox.keep_mask(seed, off, p, b, h, H, rows, cols)
         for a, i in enumerate(rows):
             for c, j in enumerate(cols):
-                w = philox.philox4_scalar((j >> 2, i, b * H + h, off & 0xFFFFFFFF),
+                w = philox.philox4_scalar((j >> 2, i >> 1, b * H + h, off & 0xFFFFFFFF),
                                           (seed & 0xFFFFFFFF, seed >> 32), 32)
-                assert km[a, c] == (w[j & 3] >= thr)
+                u = (w[j & 3] >> 16) if i & 1 else (w[j & 3] & 0xFFFF)
+                assert km[a, c] == (u >= thr)
 
 
 def test_keep_rate_is_binomial():
@@ -101,3 +104,19 @@ def test_streams_differ_across_heads_and_offsets():
         assert (a != x).mean() > 0.4
     # no two rows of one stream repeat
     assert len({r.tobytes() for r in a}) == len(a)
+
+
+def test_row_pairs_use_independent_halves():
+    """Rows 2m and 2m+1 share generator calls but read different 16-bit halves:
+    at p = 1/2 their keep bits agree about half the time, as for independent
+    rows, and neither row repeats its pair partner."""
+    rows, cols = np.arange(256), np.arange(512)
+    km = philox.keep_mask(11, 5, 0.5, 1, 2, 4, rows, cols)
+    agree = (km[0::2] == km[1::2])
+    n = agree.size
+    assert abs(agree.sum() - n / 2) < 6 * np.sqrt(n / 4)
+    assert not any(np.array_equal(km[2 * m], km[2 * m + 1]) for m in range(128))
+    # and the halves are the only difference: the pair's counter is shared
+    w = philox.philox4_scalar((3, 7, 1 * 4 + 2, 5), (11, 0), 32)
+    assert [bool((x & 0xFFFF) >= 2 ** 15) for x in w] == list(km[14, 12:16])
+    assert [bool((x >> 16) >= 2 ** 15) for x in w] == list(km[15, 12:16])
