@@ -20,12 +20,14 @@
  * are skipped entirely: not loaded, not computed.
  *
  * Dropout (kernel-fused, after softmax and before the product with V;
- * explainer, kernel fusion) uses Philox4x32-10 (Salmon et al., SC'11) with
- *     counter = (j >> 2, i, b*H + h, (uint32) rng_offset),
+ * explainer, kernel fusion) uses Philox4x32-10 (Salmon et al., SC'11), one
+ * call per block of 4 keys x 2 query rows:
+ *     counter = (j >> 2, i >> 1, b*H + h, (uint32) rng_offset),
  *     key     = ((uint32) seed, (uint32)(seed >> 32)),
- * 32-bit word (j & 3) = r, kept iff r >= min(floor(p * 2^32), 2^32 - 1) with p
- * taken as float.  Kept entries are scaled by 1 / (1 - p).  The softmax
- * statistics (and LSE) use the undropped P.
+ * element (i, j) reads 32-bit word (j & 3), its low 16 bits u for even i and
+ * its high 16 bits for odd i, and is kept iff u >= min(floor(p * 2^16),
+ * 2^16 - 1) with p taken as float.  For p > 0 kept entries are scaled by
+ * 1 / (1 - p).  The softmax statistics (and LSE) use the undropped P.
  *
  * Conventions for every entry point:
  *  - Pointers are device memory owned by the caller (allocated by whatever
@@ -64,7 +66,7 @@
 extern "C" {
 #endif
 
-#define FA_ABI_VERSION 5
+#define FA_ABI_VERSION 6
 
 typedef enum { FA_F32 = 0, FA_F16 = 1, FA_BF16 = 2 } fa_dtype;
 

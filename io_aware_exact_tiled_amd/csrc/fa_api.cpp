@@ -58,9 +58,10 @@ int32_t kv_heads(int32_t H, const fa_opts* opts) {
     return (k >= 1 && k <= H && H % k == 0) ? k : 0;
 }
 
+// threshold on an element's 16-bit uniform: drop iff u < thr
 uint32_t drop_threshold(float p) {
-    const double t = std::floor((double)p * 4294967296.0);
-    return t >= 4294967295.0 ? 0xFFFFFFFFu : (uint32_t)t;
+    const double t = std::floor((double)p * 65536.0);
+    return t >= 65535.0 ? 0xFFFFu : (uint32_t)t;
 }
 
 fa::MaskArgs mask_args(int32_t N, int32_t causal, const uint8_t* block_mask, const fa_opts* opts) {
@@ -74,8 +75,9 @@ fa::MaskArgs mask_args(int32_t N, int32_t causal, const uint8_t* block_mask, con
 
 fa::DropArgs drop_args(float p, uint64_t seed, const fa_opts* opts) {
     fa::DropArgs d;
+    d.on = p > 0.0f ? 1u : 0u;
     d.thr = drop_threshold(p);
-    d.keep_scale = (float)(1.0 / (1.0 - (double)p));
+    d.keep_scale = d.on ? (float)(1.0 / (1.0 - (double)p)) : 1.0f;
     d.k0 = (uint32_t)(seed & 0xFFFFFFFFu);
     d.k1 = (uint32_t)(seed >> 32);
     d.off = opts ? (uint32_t)(opts->rng_offset & 0xFFFFFFFFu) : 0u;

@@ -538,12 +538,9 @@ __global__ __launch_bounds__(256, sizeof(T) == 4 ? 1 : 2) void bwd_dq_kernel(Bwd
             float ds[16];
             uint32_t keep = 0xFFFFu;
             if constexpr (DROP) {
+                // keys kv0 + 16hl + r; lanes l and l ^ 1 hold rows qrow, qrow ^ 1 and share calls
                 const uint32_t g0 = (uint32_t)(kv0 + hl * 16) >> 2;
-                keep = 0;
-#pragma unroll
-                for (int g = 0; g < 4; ++g)
-                    keep |= keep4(g0 + g, (uint32_t)qrow, (uint32_t)bh, a.drop.off, a.drop.k0, a.drop.k1,
-                                  a.drop.thr) << (4 * g);
+                keep = keep16_row(g0, (uint32_t)qrow, (uint32_t)bh, a.drop.off, a.drop.k0, a.drop.k1, a.drop.thr);
             }
             float p[16];
 #pragma unroll
@@ -625,7 +622,7 @@ hipError_t launch_t(const BwdArgs& a, hipStream_t s) {
 
 template <class T>
 hipError_t launch_d(const BwdArgs& a, int d, hipStream_t s) {
-    const bool drop = a.drop.thr != 0;
+    const bool drop = a.drop.on != 0;
     if (d == 64) return drop ? launch_t<T, 64, true>(a, s) : launch_t<T, 64, false>(a, s);
     return drop ? launch_t<T, 128, true>(a, s) : launch_t<T, 128, false>(a, s);
 }

@@ -163,37 +163,73 @@ __device__ inline u32q philox4x32_10(uint32_t c0, uint32_t c1, uint32_t c2, uint
     return {c0, c1, c2, c3};
 }
 
-// Keep bits of the four consecutive keys 4*g .. 4*g+3 of query row i, as a
-// 4-bit mask (bit e = key 4*g + e).
-__device__ inline uint32_t keep4(uint32_t g, uint32_t i, uint32_t bh, uint32_t off,
-                                 uint32_t k0, uint32_t k1, uint32_t thr) {
-    const u32q r = philox4x32_10(g, i, bh, off, k0, k1);
-    return (uint32_t)(r.x >= thr) | ((uint32_t)(r.y >= thr) << 1) |
-           ((uint32_t)(r.z >= thr) << 2) | ((uint32_t)(r.w >= thr) << 3);
+// One generator call decides the block of keys 4g .. 4g+3 x query rows 2m,
+// 2m+1: counter (g, m, bh, off); output word e belongs to key 4g+e, its low
+// 16 bits to row 2m and its high 16 bits to row 2m+1; an element is kept iff
+// its 16-bit value is >= thr.  Eight keep bits, in one of two orders:
+//   ROWS:  bit 4s + e = (key 4g+e, row 2m+s)   (a row's 4 keys contiguous)
+//   PAIRS: bit 2e + s = (key 4g+e, row 2m+s)   (a key's 2 rows contiguous)
+template <bool ROWS>
+__device__ inline uint32_t keep8(uint32_t g, uint32_t m, uint32_t bh, uint32_t off, uint32_t k0, uint32_t k1,
+                                 uint32_t thr) {
+    const u32q r = philox4x32_10(g, m, bh, off, k0, k1);
+    const uint32_t w[4] = {r.x, r.y, r.z, r.w};
+    uint32_t out = 0;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        const uint32_t lo = (uint32_t)((w[e] & 0xFFFFu) >= thr), hi = (uint32_t)((w[e] >> 16) >= thr);
+        out |= ROWS ? ((lo << e) | (hi << (4 + e))) : ((lo | (hi << 1)) << (2 * e));
+    }
+    return out;
 }
 
-// Keep bits of this lane's key for 16 consecutive queries i0 .. i0+15 (bit r
-// = query i0 + r), where the 4 lanes of each quad hold the 4 keys of one
-// Philox group (lane % 4 == key % 4).  One generator call covers 4 keys, so
-// lane t of the quad runs the calls of queries i0 + t + 4m (m = 0..3) and the
-// quad shares those 16-bit results with DPP quad broadcasts: 4 calls per
-// lane instead of 16.  All 4 lanes of every quad must be active.
+// DPP moves within a quad of lanes: every lane reads lane TP of its quad, or
+// the lanes of each pair swap (quad_perm [1, 0, 3, 2]).
 template <int TP> __device__ inline uint32_t quad_bcast(uint32_t w) {
     return (uint32_t)__builtin_amdgcn_mov_dpp((int)w, TP * 0x55, 0xF, 0xF, false);   // quad_perm [TP,TP,TP,TP]
 }
+__device__ inline uint32_t pair_swap(uint32_t w) {
+    return (uint32_t)__builtin_amdgcn_mov_dpp((int)w, 0xB1, 0xF, 0xF, false);
+}
+
+// Keep bits of this lane's query row i for the 16 keys 4*g0 .. 4*g0+15 (bit r
+// = key 4*g0 + r), where lanes l and l ^ 1 hold rows i and i ^ 1 of one pair
+// with the same keys.  The pair needs four calls (one per key group); the lane
+// with row parity s runs those of groups g0 + 2s and g0 + 2s + 1, and the two
+// lanes swap results with one DPP move.  Both lanes of every pair must be
+// active.
+__device__ inline uint32_t keep16_row(uint32_t g0, uint32_t i, uint32_t bh, uint32_t off, uint32_t k0,
+                                      uint32_t k1, uint32_t thr) {
+    const uint32_t s = i & 1u;
+    const uint32_t w = keep8<true>(g0 + 2 * s, i >> 1, bh, off, k0, k1, thr) |
+                       (keep8<true>(g0 + 2 * s + 1, i >> 1, bh, off, k0, k1, thr) << 8);
+    const uint32_t o = pair_swap(w);
+    const uint32_t a = s ? o : w;        // groups g0, g0 + 1 (bytes 0, 1)
+    const uint32_t b = s ? w : o;        // groups g0 + 2, g0 + 3
+    const uint32_t sh = 4 * s;           // this row's nibble of each byte
+    return ((a >> sh) & 0xFu) | (((a >> (8 + sh)) & 0xFu) << 4) | (((b >> sh) & 0xFu) << 8) |
+           (((b >> (8 + sh)) & 0xFu) << 12);
+}
+
+// Keep bits of this lane's key for 16 consecutive queries i0 .. i0+15 (i0
+// even; bit r = query i0 + r), where the 4 lanes of each quad hold the 4 keys
+// of one group (lane % 4 == key % 4).  The 8 row pairs take 8 calls: lane t of
+// the quad runs pairs t and t + 4, and the quad shares the results with DPP
+// quad broadcasts.  All 4 lanes of every quad must be active.
 __device__ inline uint32_t keep16_quad(uint32_t key, uint32_t i0, uint32_t bh, uint32_t off, uint32_t k0,
                                        uint32_t k1, uint32_t thr, int lane) {
     const uint32_t t = (uint32_t)lane & 3u;
-    uint32_t w = 0;
-#pragma unroll
-    for (int m = 0; m < 4; ++m) w |= keep4(key >> 2, i0 + t + 4 * m, bh, off, k0, k1, thr) << (4 * m);
+    const uint32_t m0 = (i0 >> 1) + t;
+    const uint32_t w = keep8<false>(key >> 2, m0, bh, off, k0, k1, thr) |
+                       (keep8<false>(key >> 2, m0 + 4, bh, off, k0, k1, thr) << 8);
     const uint32_t W[4] = {quad_bcast<0>(w), quad_bcast<1>(w), quad_bcast<2>(w), quad_bcast<3>(w)};
     const uint32_t ks = key & 3u;
     uint32_t out = 0;
+    // byte c of W[tp] is pair tp + 4c: its bits 2ks, 2ks + 1 are queries i0 + 2(tp + 4c) + {0, 1}
 #pragma unroll
     for (int tp = 0; tp < 4; ++tp)
 #pragma unroll
-        for (int m = 0; m < 4; ++m) out |= ((W[tp] >> (4 * m + ks)) & 1u) << (4 * m + tp);
+        for (int c = 0; c < 2; ++c) out |= ((W[tp] >> (8 * c + 2 * ks)) & 3u) << (2 * tp + 8 * c);
     return out;
 }
 

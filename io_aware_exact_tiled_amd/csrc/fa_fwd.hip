@@ -9,7 +9,7 @@
 //   masks on edge tiles      causal j > i, key padding j >= len_b, N tail
 //   m_new = max(m, rowmax)   lane-local max over 16 keys + one cross-half swap
 //   P = exp2(S*scale*log2e - m_new),  l = e^{m - m_new} l + rowsum(P)
-//   dropout keep bits        Philox4x32-10, one call per 4 keys
+//   dropout keep bits        Philox4x32-10, one call per 4 keys x 2 rows
 //   O^T = e^{m - m_new} O^T + V_j^T P^T     MFMA
 // and finally writes O = O^T / l and LSE = m + ln l (incremental softmax of
 // the summary's "Method" steps 2-4 with the normalisation deferred to the end,
@@ -256,17 +256,17 @@ __global__ __launch_bounds__(256, sizeof(T) == 4 ? 1 : 2) void fwd_kernel(FwdArg
                     l_run += p[kb][r];
                 }
             if constexpr (DROP) {
+                // keys kv0 + 32kb + 16hl + r of this lane's row; rows qrow and qrow ^ 1 sit in
+                // lanes l and l ^ 1 and share their generator calls
                 const uint32_t g0 = (uint32_t)(kv0 + hl * 16) >> 2;
 #pragma unroll
-                for (int kb = 0; kb < KB; ++kb)
+                for (int kb = 0; kb < KB; ++kb) {
+                    const uint32_t bits = keep16_row(g0 + kb * 8, (uint32_t)qrow, (uint32_t)bh, a.drop.off,
+                                                     a.drop.k0, a.drop.k1, a.drop.thr);
 #pragma unroll
-                    for (int g = 0; g < 4; ++g) {
-                        const uint32_t bits = keep4(g0 + kb * 8 + g, (uint32_t)qrow, (uint32_t)bh, a.drop.off,
-                                                    a.drop.k0, a.drop.k1, a.drop.thr);
-#pragma unroll
-                        for (int e = 0; e < 4; ++e)
-                            if (!((bits >> e) & 1u)) p[kb][g * 4 + e] = 0.0f;
-                    }
+                    for (int r = 0; r < 16; ++r)
+                        if (!((bits >> r) & 1u)) p[kb][r] = 0.0f;
+                }
             }
             // ---- O^T += V_j^T P^T: k-slot kk of step (kb, u) is key
             // 32kb + 16(kk/EV) + u*EV + kk%EV, the lane half's own keys
@@ -325,7 +325,7 @@ hipError_t launch_t(const FwdArgs& a, hipStream_t s) {
 
 template <class T>
 hipError_t launch_d(const FwdArgs& a, int d, hipStream_t s) {
-    const bool drop = a.drop.thr != 0;
+    const bool drop = a.drop.on != 0;
     if (d == 64) return drop ? launch_t<T, 64, true>(a, s) : launch_t<T, 64, false>(a, s);
     return drop ? launch_t<T, 128, true>(a, s) : launch_t<T, 128, false>(a, s);
 }

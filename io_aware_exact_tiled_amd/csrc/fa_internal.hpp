@@ -46,7 +46,8 @@ struct MaskArgs {
 };
 
 struct DropArgs {
-    uint32_t thr;         // drop iff r < thr; 0 = no dropout
+    uint32_t on;          // 1 iff p > 0 (kept entries scaled, mask applied)
+    uint32_t thr;         // drop iff the element's 16-bit uniform u < thr
     float keep_scale;     // 1 / (1 - p)
     uint32_t k0, k1;      // Philox key (seed low, high)
     uint32_t off;         // Philox counter word 3

@@ -41,7 +41,7 @@ def test_library_exports_every_declared_symbol():
 
 def test_scalars():
     L = _lib()
-    assert L.fa_abi_version() == 5
+    assert L.fa_abi_version() == 6
     for code in list(lib_mod.STATUS) + [-99]:
         assert isinstance(L.fa_status_string(code), bytes)
     br, bc = ctypes.c_int32(), ctypes.c_int32()
