@@ -216,8 +216,8 @@ def attn_bwd_rows_cols(q, k, v, do, scale, rows, cols, lse_all, D_all,
         dP = (do[b, h, rows] @ v[b, g].T) * Z * keep_scale
         D = (P * dP).sum(axis=1)
         dq[b, h] = sc * ((P * (dP - D[:, None])) @ k[b, g])
-        # dK, dV columns: all query rows, selected keys
-        for s in range(0, N, chunk):
+        # dK, dV columns: all query rows, selected keys (none: nothing to add)
+        for s in range(0, N if len(cols) else 0, chunk):
             r = np.arange(s, min(s + chunk, N))
             Sc = sc * (q[b, h, r] @ k[b, g, cols].T)
             Ac = validity(r, N, causal, kl, block_mask)[:, cols]
