@@ -19,8 +19,10 @@
 //                S = Q K^T, dP = dO V^T, dV += P^T dO, dK += dS^T Q.
 //   3. bwd_dq:   one workgroup (4 waves) per 128 query rows; each wave owns 32
 //                rows (one per lane column, with its LSE_i and D_i in
-//                registers) and walks the key tiles of 32 that hold a valid
-//                pair: S^T = K Q^T, dP^T = V dO^T, dQ^T += K^T dS^T.
+//                registers) and walks the key tiles of 64 that hold a valid
+//                pair, each as two blocks of 32 in turn (one barrier and one
+//                tile load per 64 keys): S^T = K Q^T, dP^T = V dO^T,
+//                dQ^T += K^T dS^T.
 // dQ is therefore produced without atomics and without a dS round trip
 // through memory, at the price of recomputing S and dP once more (seven
 // products per pair instead of five).  Both loops prefetch the next tile into
@@ -445,7 +447,8 @@ template <class T, int D, bool DROP>
 __global__ __launch_bounds__(256, sizeof(T) == 4 ? 1 : 2) void bwd_dq_kernel(BwdArgs a) {
     typedef Mma<T> MM;
     constexpr int E = MM::E;
-    constexpr int BR = BWD_DQ_BR, BC = BWD_DQ_BC;   // 128 query rows, 32-key tiles
+    constexpr int BR = BWD_DQ_BR, BC = BWD_DQ_BC;   // 128 query rows, 64-key tiles
+    constexpr int NSB = BC / 32;                     // 32-key blocks per staged tile, walked in turn
     constexpr int KS = D / (2 * E);
     constexpr int DB = D / 32;
     constexpr int PU = 16 / E;
@@ -522,10 +525,14 @@ __global__ __launch_bounds__(256, sizeof(T) == 4 ? 1 : 2) void bwd_dq_kernel(Bwd
         const int jn = tile_at(j + 1);
         if (jn >= 0) load_tile(jn, buf ^ 1);
 
-        if (!(causal && kv0 > qw0 + 31)) {
-            const T* k = sK + buf * TK;
-            const T* v = sV + buf * TK;
-            // S^T = K Q^T, dP_hat^T = V dO^T: lane holds query qrow, keys kv0 + 16hl + r
+#pragma unroll 1
+        for (int sb = 0; sb < NSB; ++sb) {   // in turn: the registers of one block at a time
+          const int kb0 = kv0 + sb * 32;   // this 32-key block of the staged tile
+          // skip blocks past the valid keys or above the diagonal for all of this wave's rows
+          if (kb0 < kend && !(causal && kb0 > qw0 + 31)) {
+            const T* k = sK + buf * TK + sb * 32 * D;
+            const T* v = sV + buf * TK + sb * 32 * D;
+            // S^T = K Q^T, dP_hat^T = V dO^T: lane holds query qrow, keys kb0 + 16hl + r
             // (chain 0: S, chain 1: dP; operands read ahead)
             f32x16 sd[2] = {zero16(), zero16()};
             __builtin_amdgcn_s_setprio(1);
@@ -534,12 +541,12 @@ __global__ __launch_bounds__(256, sizeof(T) == 4 ? 1 : 2) void bwd_dq_kernel(Bwd
                 [&](int c, int ks) { return c ? of[ks] : qf[ks]; });
             __builtin_amdgcn_s_setprio(0);
             const f32x16 s = sd[0], dp = sd[1];
-            const bool edge = (kv0 + BC > kend) || (causal && kv0 + BC - 1 > qw0);
+            const bool edge = (kb0 + 32 > kend) || (causal && kb0 + 31 > qw0);
             float ds[16];
             uint32_t keep = 0xFFFFu;
             if constexpr (DROP) {
-                // keys kv0 + 16hl + r; lanes l and l ^ 1 hold rows qrow, qrow ^ 1 and share calls
-                const uint32_t g0 = (uint32_t)(kv0 + hl * 16) >> 2;
+                // keys kb0 + 16hl + r; lanes l and l ^ 1 hold rows qrow, qrow ^ 1 and share calls
+                const uint32_t g0 = (uint32_t)(kb0 + hl * 16) >> 2;
                 keep = keep16_row(g0, (uint32_t)qrow, (uint32_t)bh, a.drop.off, a.drop.k0, a.drop.k1, a.drop.thr);
             }
             float p[16];
@@ -548,7 +555,7 @@ __global__ __launch_bounds__(256, sizeof(T) == 4 ? 1 : 2) void bwd_dq_kernel(Bwd
             if (__builtin_expect(edge, 0)) {
 #pragma unroll
                 for (int r = 0; r < 16; ++r) {
-                    const int key = kv0 + hl * 16 + r;
+                    const int key = kb0 + hl * 16 + r;
                     if (key >= kend || (causal && key > qrow)) p[r] = 0.0f;
                 }
             }
@@ -568,6 +575,7 @@ __global__ __launch_bounds__(256, sizeof(T) == 4 ? 1 : 2) void bwd_dq_kernel(Bwd
                 tr_chain<T, D, 1, true, 2>(dq, k, tro, [&](int, int u) { return bs[u]; }, lane);
                 __builtin_amdgcn_s_setprio(0);
             }
+        }
         }
         __builtin_amdgcn_s_waitcnt(0);   // this wave's DMA into the other buffer has landed
         __syncthreads();

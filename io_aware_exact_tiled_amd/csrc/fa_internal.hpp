@@ -27,7 +27,7 @@ constexpr int BWD_KV_SMALL_N = 2048;      // d = 128 causal N at or below this: 
 constexpr int BWD_KV_BR16 = 64;  // 16-bit inputs
 constexpr int BWD_KV_BR32 = 32;  // fp32 inputs (LDS budget of the double buffer)
 constexpr int BWD_DQ_BR = 128;
-constexpr int BWD_DQ_BC = 32;
+constexpr int BWD_DQ_BC = 64;   // staged per step; the math walks 32-key blocks
 // How many MFMA steps ahead the LDS operands of the S (and dP) products are
 // read.  Deeper read-ahead hides more LDS latency but costs registers: at
 // d = 64 one step keeps the forward at 4 waves per SIMD and two keep the dQ
