@@ -81,6 +81,8 @@ def parse():
     ap.add_argument("--cpu-rows", type=int, default=6144,
                     help="leading causal rows per head the oracle baseline computes")
     ap.add_argument("--sweep", action="store_true", help="also time the N sweep (extra JSON lines)")
+    ap.add_argument("--graph", action="store_true",
+                    help="also time the step captured in a HIP graph (graph_ms_per_step; value stays eager)")
     ap.add_argument("--io-ablation", action="store_true",
                     help="also run the key/value-outer forward beside the query-outer one at N = 2K, 4K, 8K "
                          "(extra JSON lines with the HBM bytes each order implies)")
@@ -183,7 +185,7 @@ def dominant_roofline(w, pairs, kernel_ms):
     return roofline, kern
 
 
-def time_workload(w, steps, warmup, ev):
+def time_workload(w, steps, warmup, ev, graph=False):
     import torch
     import io_aware_exact_tiled_amd as fa
     import workloads as W
@@ -238,9 +240,33 @@ def time_workload(w, steps, warmup, ev):
     bwd_pass_ms = [ev.ms(sm[i], s1[i]) for i in range(steps)]
     for e in f0 + f1 + b0 + b1 + bm + s0 + sm + s1:
         ev.destroy(e)
+    graph_ms = None
+    if graph:
+        # the same step captured once in a HIP graph and replayed: what the step
+        # costs without per-launch host overhead (the library calls only launch
+        # kernels, so they are capturable)
+        side = torch.cuda.Stream(dev)
+        side.wait_stream(torch.cuda.current_stream(dev))
+        with torch.cuda.stream(side):
+            step()
+        torch.cuda.current_stream(dev).wait_stream(side)
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            step()
+        for _ in range(warmup):
+            g.replay()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(steps):
+            g.replay()
+        e1.record()
+        e1.synchronize()
+        graph_ms = e0.elapsed_time(e1) / steps
+        del g
     pairs = valid_pairs(x, w)
     return dict(x=x, pairs=pairs, wall_s=wall, fwd_ms=fwd_ms, bwd_main_ms=bwd_ms, kv_ms=kv_ms, dq_ms=dq_ms,
-                step_ms=step_ms, fwd_pass_ms=fwd_pass_ms, bwd_pass_ms=bwd_pass_ms)
+                step_ms=step_ms, fwd_pass_ms=fwd_pass_ms, bwd_pass_ms=bwd_pass_ms, graph_ms=graph_ms)
 
 
 def standard_attention(q, k, v, do, scale, causal, p, events=None):
@@ -513,6 +539,9 @@ def decode_report(w, args, ev):
                      "avg_launch_ms": round(split_avg, 5), "bytes_per_launch": rd},
         "wall_s": round(r["wall_s"], 3),
     }
+    if r["graph_ms"] is not None:
+        out["graph_ms_per_step"] = round(r["graph_ms"], 4)
+        out["graph_tflops"] = round((fwd_flop + bwd_flop) / (r["graph_ms"] * 1e-3) / 1e12, 2)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline_decode(w, rd + wr)
     print(json.dumps(out), flush=True)
@@ -624,7 +653,7 @@ def main():
     if w.decode_q is not None:
         decode_report(w, args, ev)
         return
-    r = time_workload(w, args.steps, args.warmup, ev)
+    r = time_workload(w, args.steps, args.warmup, ev, graph=args.graph)
     fwd_flop = 4.0 * w.d * r["pairs"]
     bwd_flop = 10.0 * w.d * r["pairs"]
     med = lambda a: float(np.median(a))
@@ -662,6 +691,9 @@ def main():
         "roofline": roofline,
         "wall_s": round(r["wall_s"], 3),
     }
+    if r["graph_ms"] is not None:
+        out["graph_ms_per_step"] = round(r["graph_ms"], 4)
+        out["graph_tflops"] = round((fwd_flop + bwd_flop) / (r["graph_ms"] * 1e-3) / 1e12, 2)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(w, args.cpu_rows)
     print(json.dumps(out), flush=True)
