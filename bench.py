@@ -539,9 +539,6 @@ def decode_report(w, args, ev):
                      "avg_launch_ms": round(split_avg, 5), "bytes_per_launch": rd},
         "wall_s": round(r["wall_s"], 3),
     }
-    if r["graph_ms"] is not None:
-        out["graph_ms_per_step"] = round(r["graph_ms"], 4)
-        out["graph_tflops"] = round((fwd_flop + bwd_flop) / (r["graph_ms"] * 1e-3) / 1e12, 2)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline_decode(w, rd + wr)
     print(json.dumps(out), flush=True)
