@@ -128,8 +128,8 @@ typedef struct {
 
 /* Bytes of device workspace fa_fwd needs.  bf16: the forward multiplies P
  * (rounded to fp16, whose significand is 3 bits longer than bf16's) with an
- * fp16 copy of V scaled by a power of two per (b, h), V * 2^-e_bh, with e_bh
- * chosen from the largest finite |V| of that head so that it lands in
+ * fp16 copy of V * 2^-e_bh per (b, h): e_bh = 0 while the head's largest
+ * finite |V| lies in [2^-6, 2^15), else the power of two that brings it into
  * [2^14, 2^15); every bf16 value of magnitude >= 2^(e_bh - 17) converts
  * exactly.  The workspace holds that copy (B*H*N*d fp16) plus 4-byte
  * per-head statistics, each part rounded up to 256 bytes.  fp16 and fp32

@@ -30,11 +30,12 @@
 //    with the gfx950 LDS transpose read.
 //  * bf16 inputs: P is rounded to fp16 (11-bit significand) rather than bf16
 //    (8 bits) for the P*V product, so V must be fp16 as well.  A pre-pass
-//    converts V once per call: it finds e_bh from the largest finite |V| of
-//    each (b, h) such that that value times 2^-e_bh lies in [2^14, 2^15),
-//    writes V * 2^-e_bh in fp16 to the workspace, and the epilogue multiplies
-//    O by 2^e_bh.  Every bf16 value of magnitude at least 2^(e_bh - 17)
-//    converts exactly; smaller ones are off by at most 2^(e_bh - 25).
+//    writes V * 2^-e_bh in fp16 to the workspace once per call, with e_bh = 0
+//    while the largest finite |V| of the (b, h) lies in [2^-6, 2^15) and
+//    otherwise the power of two that brings it into [2^14, 2^15); the
+//    epilogue multiplies O by 2^e_bh.  Every bf16 value of magnitude at
+//    least 2^(e_bh - 17) converts exactly; smaller ones are off by at most
+//    2^(e_bh - 25).
 #include "fa_device.hpp"
 #include "fa_internal.hpp"
 
@@ -55,43 +56,28 @@ __device__ inline uint32_t block_max256(uint32_t m) {
 }  // namespace
 
 // ---------------------------------------------------------------------------
-// bf16 V -> fp16 pre-pass.  Workgroup w handles chunk w % nch of (b, h) =
-// w / nch.  The first kernel writes each chunk's largest finite |V| as bf16
-// magnitude bits (monotone in the value); the second reduces the chunks of
-// its (b, h), picks the exponent and converts its chunk.
-__global__ __launch_bounds__(256) void v16_absmax_kernel(V16Args a) {
-    const int tid = threadIdx.x;
-    const size_t bh = blockIdx.x / a.nch, ch = blockIdx.x % a.nch;
-    const size_t beg = ch * a.chunk;
-    const size_t end = beg + a.chunk < a.per_head ? beg + a.chunk : a.per_head;
-    const uint16_t* src = static_cast<const uint16_t*>(a.v) + bh * a.per_head;
-    uint32_t m = 0;
-    for (size_t i = beg + (size_t)tid * 8; i < end; i += 256 * 8) {
-        const u32x4 w = *reinterpret_cast<const u32x4*>(src + i);
-#pragma unroll
-        for (int k = 0; k < 4; ++k) {
-            const uint32_t lo = w[k] & 0x7fffu, hi = (w[k] >> 16) & 0x7fffu;
-            if (lo < 0x7f80u) m = max(m, lo);   // exponent field all ones: inf or NaN
-            if (hi < 0x7f80u) m = max(m, hi);
-        }
-    }
-    m = block_max256(m);
-    if (tid == 0) a.part[bh * a.nch + ch] = m;
+// bf16 V -> fp16 pre-pass: two kernels over one grid, workgroup w taking chunk
+// w % nch of (b, h) = w / nch.  The first converts its chunk unscaled and, in
+// the same read, records the chunk's largest finite |V| as bf16 magnitude
+// bits (monotone in the value).  The second reduces the maxima of its (b, h)
+// and picks the exponent e_bh: 0 while the largest |V| lies in [2^-6, 2^15)
+// -- nothing overflows, and values that fp16 holds only as subnormals are
+// then more than 2^8 below the largest, with absolute error <= 2^-25 --
+// else the power of two that brings the largest into [2^14, 2^15).  Only
+// heads with e_bh != 0 are converted again, as V * 2^-e_bh.
+__device__ inline int v16_exponent(uint32_t M) {
+    if (M == 0) return 0;
+    const int F = (int)(M >> 7);   // bf16 exponent field: the largest is in [2^(F-127), 2^(F-126))
+    if (F >= 121 && F < 142) return 0;
+    return F - 141;                // F = 0 (a subnormal, >= 2^-133) included
 }
 
-__global__ __launch_bounds__(256) void v16_convert_kernel(V16Args a) {
-    const int tid = threadIdx.x;
-    const size_t bh = blockIdx.x / a.nch, ch = blockIdx.x % a.nch;
-    const uint32_t M = block_max256(tid < a.nch ? a.part[bh * a.nch + tid] : 0u);
-    // the largest finite |V| lies in [2^(F-127), 2^(F-126)) for its bf16
-    // exponent field F (F = 0: a subnormal, below 2^-126 and at least 2^-133)
-    const int e = M == 0 ? 0 : (int)(M >> 7) - 141;
-    if (ch == 0 && tid == 0) a.vexp[bh] = e;
+__device__ inline void v16_convert_chunk(const V16Args& a, size_t bh, size_t ch, int e) {
     const size_t beg = ch * a.chunk;
     const size_t end = beg + a.chunk < a.per_head ? beg + a.chunk : a.per_head;
     const uint16_t* src = static_cast<const uint16_t*>(a.v) + bh * a.per_head;
     f16* dst = a.v16 + bh * a.per_head;
-    for (size_t i = beg + (size_t)tid * 8; i < end; i += 256 * 8) {
+    for (size_t i = beg + (size_t)threadIdx.x * 8; i < end; i += 256 * 8) {
         const u32x4 w = *reinterpret_cast<const u32x4*>(src + i);
         f16x8 h;
 #pragma unroll
@@ -101,6 +87,39 @@ __global__ __launch_bounds__(256) void v16_convert_kernel(V16Args a) {
         }
         *reinterpret_cast<f16x8*>(dst + i) = h;
     }
+}
+
+__global__ __launch_bounds__(256) void v16_convert_kernel(V16Args a) {
+    const int tid = threadIdx.x;
+    const size_t bh = blockIdx.x / a.nch, ch = blockIdx.x % a.nch;
+    const size_t beg = ch * a.chunk;
+    const size_t end = beg + a.chunk < a.per_head ? beg + a.chunk : a.per_head;
+    const uint16_t* src = static_cast<const uint16_t*>(a.v) + bh * a.per_head;
+    f16* dst = a.v16 + bh * a.per_head;
+    uint32_t m = 0;
+    for (size_t i = beg + (size_t)tid * 8; i < end; i += 256 * 8) {
+        const u32x4 w = *reinterpret_cast<const u32x4*>(src + i);
+        f16x8 h;
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            const uint32_t lo = w[k] & 0x7fffu, hi = (w[k] >> 16) & 0x7fffu;
+            if (lo < 0x7f80u) m = max(m, lo);   // exponent field all ones: inf or NaN
+            if (hi < 0x7f80u) m = max(m, hi);
+            h[2 * k] = (f16)__uint_as_float(w[k] << 16);
+            h[2 * k + 1] = (f16)__uint_as_float(w[k] & 0xffff0000u);
+        }
+        *reinterpret_cast<f16x8*>(dst + i) = h;
+    }
+    m = block_max256(m);
+    if (tid == 0) a.part[bh * a.nch + ch] = m;
+}
+
+__global__ __launch_bounds__(256) void v16_rescale_kernel(V16Args a) {
+    const int tid = threadIdx.x;
+    const size_t bh = blockIdx.x / a.nch, ch = blockIdx.x % a.nch;
+    const int e = v16_exponent(block_max256(tid < a.nch ? a.part[bh * a.nch + tid] : 0u));
+    if (ch == 0 && tid == 0) a.vexp[bh] = e;
+    if (e != 0) v16_convert_chunk(a, bh, ch, e);   // else the unscaled copy stands
 }
 
 // ---------------------------------------------------------------------------
@@ -346,9 +365,9 @@ hipError_t launch_fwd(FwdArgs a, fa_dtype dt, int d, void* workspace, hipStream_
         p.chunk = L.chunk;
         void* args[] = {(void*)&p};
         const dim3 grid((unsigned)((size_t)a.B * a.Hkv * L.nch));
-        hipError_t e = hipLaunchKernel((const void*)&v16_absmax_kernel, grid, dim3(256), args, 0, s);
+        hipError_t e = hipLaunchKernel((const void*)&v16_convert_kernel, grid, dim3(256), args, 0, s);
         if (e != hipSuccess) return e;
-        e = hipLaunchKernel((const void*)&v16_convert_kernel, grid, dim3(256), args, 0, s);
+        e = hipLaunchKernel((const void*)&v16_rescale_kernel, grid, dim3(256), args, 0, s);
         if (e != hipSuccess) return e;
         a.v = p.v16;
         a.vexp = p.vexp;
