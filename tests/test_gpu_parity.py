@@ -91,6 +91,8 @@ GQA_CASES = [
     (8, 2, 384, 128, "bf16", True, None, True, 0.0),
     (4, 2, 130, 128, "fp32", True, None, False, 0.0),
     (6, 3, 513, 64, "bf16", True, "mixed", False, 0.2),
+    # eight-wave dK/dV kernel (d = 128, non-causal) with dropout and two query heads per K/V head
+    (4, 2, 300, 128, "bf16", False, None, False, 0.2),
 ]
 
 
