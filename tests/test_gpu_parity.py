@@ -355,3 +355,12 @@ def test_kv_outer_forward_matrix(case):
     O, L = oracle.attn_fwd(q, k, v, 1.0 / np.sqrt(d), causal=causal)
     res = dict(o=check_o(o, O, dt, "O(stored)", stored=True), lse=check_lse(lse, L, dt))
     print(f"[ok] kv-outer {case} {res}", flush=True)
+
+
+@pytest.mark.parametrize("B,H,d", [(8, 2, 64), (4, 6, 128)])
+def test_rank_order_dispatch_small_causal(B, H, d):
+    """B*H a multiple of 8: causal launches walk each XCD's heads rank by rank
+    (the heaviest tile of every head first); ragged N = 300 so tiles differ
+    in cost and the last ones are partial."""
+    x = W.random_case(B, H, 300, d, dtype="bf16", seed=B * 100 + H + d, causal=True)
+    run_and_check(x, label=f"rank order B{B} H{H} d{d}")
