@@ -200,7 +200,7 @@ def time_workload(w, steps, warmup, ev, graph=False):
     lse = torch.empty(w.B, w.H, w.N, dtype=torch.float32, device=dev)
     grads = (torch.empty_like(q), torch.empty_like(k), torch.empty_like(v))
     ws = torch.empty(fa.bwd_workspace_bytes(w.B, w.H, w.N, w.d), dtype=torch.uint8, device=dev)
-    fws = torch.empty(max(1, fa.fwd_workspace_bytes(w.B, w.H, w.N, w.d, q.dtype)), dtype=torch.uint8, device=dev)
+    fws = torch.empty(max(1, fa.fwd_workspace_bytes(w.B, w.Hkv, w.N, w.d, q.dtype)), dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream(dev).cuda_stream
     n_ev = steps
     f0 = [ev.create() for _ in range(n_ev)]

@@ -4,7 +4,7 @@
  *
  * The operation is exact attention per (batch b, head h):
  *     S = scale * Q K^T,   P = softmax over keys of S with invalid scores at -inf,
- *     O = (P o Z / (1 - p)) V
+ *     O = (P o Z * s) V,   Z the keep bits, s the keep scale (below)
  * computed tile by tile with an online softmax so that no N x N matrix ever
  * reaches device memory (FlashAttention summary, xyznot.com/vi/paper/2205.14135,
  * "Method": block scores S_ij, block statistics, merged (m, l), rescaled O_i;
@@ -25,9 +25,11 @@
  *     counter = (j >> 2, i >> 1, b*H + h, (uint32) rng_offset),
  *     key     = ((uint32) seed, (uint32)(seed >> 32)),
  * element (i, j) reads 32-bit word (j & 3), its low 16 bits u for even i and
- * its high 16 bits for odd i, and is kept iff u >= min(floor(p * 2^16),
+ * its high 16 bits for odd i, and is kept iff u >= thr = min(floor(p * 2^16),
  * 2^16 - 1) with p taken as float.  For p > 0 kept entries are scaled by
- * 1 / (1 - p).  The softmax statistics (and LSE) use the undropped P.
+ * 2^16 / (2^16 - thr), the inverse of the exact keep probability, so that
+ * the expected dropped O equals the undropped one (inverted dropout).  The
+ * softmax statistics (and LSE) use the undropped P.
  *
  * Conventions for every entry point:
  *  - Pointers are device memory owned by the caller (allocated by whatever
@@ -66,9 +68,12 @@
 extern "C" {
 #endif
 
-#define FA_ABI_VERSION 6
+#define FA_ABI_VERSION 7
 
-typedef enum { FA_F32 = 0, FA_F16 = 1, FA_BF16 = 2 } fa_dtype;
+/* FA_DTYPE_RANGE_ only widens the enum's range to 32 bits, so that any value
+ * a caller passes can be read (and rejected with FA_ERR_DTYPE) without
+ * undefined behaviour in the C++ implementation; it is not a dtype. */
+typedef enum { FA_F32 = 0, FA_F16 = 1, FA_BF16 = 2, FA_DTYPE_RANGE_ = 0x7fffffff } fa_dtype;
 
 typedef enum {
     FA_OK = 0,
@@ -103,12 +108,15 @@ typedef struct {
     uint64_t rng_offset;        /* Philox counter word 3 (low 32 bits used)      */
     uint32_t flags;             /* FA_FLAG_*                                      */
     uint8_t* tile_visits;       /* device uint8[B][H][ceil(N/Br)][ceil(N/Bc)] with
-                                   (Br, Bc) = fa_tile_shape(pass 0) for fa_fwd and
-                                   fa_tile_shape(pass 1) (the dK/dV kernel) for
-                                   fa_bwd; every entry is written (1 = tile
-                                   visited) when FA_FLAG_RECORD_TILES is set     */
+                                   (Br, Bc) = fa_tile_shape(pass 0, N, causal) for
+                                   fa_fwd and fa_tile_shape(pass 1, N, causal)
+                                   (the dK/dV kernel as launched for this N and
+                                   mask) for fa_bwd; every entry is written
+                                   (1 = tile visited) when FA_FLAG_RECORD_TILES
+                                   is set.  Recording does not change which
+                                   kernel runs.                                  */
     uint8_t* tile_visits2;      /* fa_bwd only: the dQ kernel's map, shape from
-                                   fa_tile_shape(pass 2); may be NULL            */
+                                   fa_tile_shape(pass 2, N, causal); may be NULL */
     hipEvent_t main_begin;      /* profiling: when both are non-NULL they are    */
     hipEvent_t main_end;        /* recorded on `stream` right before and right
                                    after the pass's main kernels (the forward
@@ -128,22 +136,25 @@ typedef struct {
 
 /* Bytes of device workspace fa_fwd needs.  bf16: the forward multiplies P
  * (rounded to fp16, whose significand is 3 bits longer than bf16's) with an
- * fp16 copy of V * 2^-e_bh per (b, h): e_bh = 0 while the head's largest
- * finite |V| lies in [2^-6, 2^15), else the power of two that brings it into
- * [2^14, 2^15); every bf16 value of magnitude >= 2^(e_bh - 17) converts
- * exactly.  The workspace holds that copy (B*H*N*d fp16) plus 4-byte
- * per-head statistics, each part rounded up to 256 bytes.  fp16 and fp32
- * need none: 0.  Returns 0 for invalid sizes or dtypes. */
-size_t fa_fwd_workspace_bytes(int32_t B, int32_t H, int32_t N, int32_t d, fa_dtype dtype);
+ * fp16 copy of V * 2^-e_bh per (b, K/V head h): e_bh = 0 while the head's
+ * largest finite |V| lies in [2^-6, 2^15), else the power of two that brings
+ * it into [2^14, 2^15); every bf16 value of magnitude >= 2^(e_bh - 17)
+ * converts exactly.  The workspace holds that copy (B*Hkv*N*d fp16) plus
+ * 4-byte per-head statistics, each part rounded up to 256 bytes.  Hkv is
+ * the number of K/V heads (opts->kv_heads, or H without grouped-query
+ * attention); the value for the query head count H >= Hkv is an upper
+ * bound.  fp16 and fp32 need none: 0.  Returns 0 for invalid sizes or
+ * dtypes. */
+size_t fa_fwd_workspace_bytes(int32_t B, int32_t Hkv, int32_t N, int32_t d, fa_dtype dtype);
 
 /* Forward pass.  Q, K, V: [B][H][N][d] of `dtype`.  O: [B][H][N][d] of
  * `dtype`, or fp32 when opts->o_fp32 is set.  LSE: float [B][H][N].
  * causal: nonzero for the lower-triangular mask.  dropout_p in [0, 1); seed
  * selects the Philox key.  block_mask: device uint8[ceil(N/128)][ceil(N/128)],
  * shared by all (b, h), nonzero = compute; NULL = dense.  workspace: device
- * memory of at least fa_fwd_workspace_bytes(B, H, N, d, dtype) bytes,
- * 256-byte aligned (may be NULL when that is 0); its contents on return are
- * unspecified. */
+ * memory of at least fa_fwd_workspace_bytes(B, Hkv, N, d, dtype) bytes
+ * (Hkv: the K/V heads), 256-byte aligned (may be NULL when that is 0); its
+ * contents on return are unspecified. */
 fa_status fa_fwd(const void* Q, const void* K, const void* V, void* O, float* LSE,
                  int32_t B, int32_t H, int32_t N, int32_t d, fa_dtype dtype,
                  float scale, int32_t causal, float dropout_p, uint64_t seed,
@@ -224,11 +235,19 @@ fa_status fa_dropout_keep_mask(uint64_t seed, uint64_t rng_offset, float dropout
                                int32_t B, int32_t H, int32_t N, uint8_t* keep,
                                hipStream_t stream);
 
-/* Tile shape (rows Br of queries, columns Bc of keys) a kernel uses for head
- * dim d and dtype: pass 0 = forward, 1 = backward dK/dV kernel, 2 = backward
- * dQ kernel; these index the tile-visit maps.  Both divide 128, so a tile lies
- * inside one block of the 128 x 128 block mask. */
-fa_status fa_tile_shape(int32_t d, fa_dtype dtype, int32_t pass, int32_t* Br, int32_t* Bc);
+/* Tile shape (rows Br of queries, columns Bc of keys) of the kernel that
+ * fa_fwd (pass 0) or fa_bwd (pass 1: the dK/dV kernel; pass 2: the dQ kernel)
+ * launches for head dim d, dtype, sequence length N and the causal flag;
+ * these index the tile-visit maps.  The dK/dV kernel has two configurations
+ * (64 keys x 32 query rows for 16-bit inputs at d = 64 and for causal
+ * d = 128 up to N = 2048; else 128 keys x 64 rows, fp32 x 32 rows), so its
+ * shape depends on N and causal.  Both divide 128, so a tile lies inside one
+ * block of the 128 x 128 block mask (summary, "Block-Sparse
+ * FlashAttention": a tile is skipped iff it holds no valid pair).  Errors:
+ * FA_ERR_NULL, FA_ERR_HEAD_DIM, FA_ERR_DTYPE, FA_ERR_SHAPE (N < 1),
+ * FA_ERR_OPTS (unknown pass). */
+fa_status fa_tile_shape(int32_t d, fa_dtype dtype, int32_t pass, int32_t N, int32_t causal, int32_t* Br,
+                        int32_t* Bc);
 
 /* Static description of a status code. */
 const char* fa_status_string(fa_status s);

@@ -62,7 +62,7 @@ def _stream(dev: torch.device) -> ctypes.c_void_p:
 
 
 def _opts(B, H, N, d, pass_, key_lens, rng_offset, o_fp32, record_tiles, reverse_kv, device, dtype_code,
-          events=None, kv_heads=0):
+          events=None, kv_heads=0, causal=False):
     opts = FaOpts()
     opts.kv_heads = 0 if kv_heads == H else int(kv_heads)
     if events is not None:
@@ -81,7 +81,7 @@ def _opts(B, H, N, d, pass_, key_lens, rng_offset, o_fp32, record_tiles, reverse
     if record_tiles:
         maps = []
         for p in ((0,) if pass_ == 0 else (1, 2)):
-            br, bc = tile_shape(d, dtype_code, p)
+            br, bc = tile_shape(d, dtype_code, p, N, causal)
             maps.append(torch.full((B, H, -(-N // br), -(-N // bc)), 7, dtype=torch.uint8, device=device))
         opts.tile_visits = maps[0].data_ptr()
         if len(maps) > 1:
@@ -103,8 +103,10 @@ def _mask_ptr(block_mask, device, N):
     return bm, bm.data_ptr()
 
 
-def fwd_workspace_bytes(B, H, N, d, dtype: torch.dtype) -> int:
-    return int(_lib.lib().fa_fwd_workspace_bytes(B, H, N, d, _DT[dtype]))
+def fwd_workspace_bytes(B, Hkv, N, d, dtype: torch.dtype) -> int:
+    """Forward workspace bytes; Hkv = the K/V heads (H without grouped-query
+    attention)."""
+    return int(_lib.lib().fa_fwd_workspace_bytes(B, Hkv, N, d, _DT[dtype]))
 
 
 def fwd(q, k, v, *, causal=False, dropout_p=0.0, seed=0, rng_offset=0, key_lens=None, block_mask=None,
@@ -123,9 +125,9 @@ def fwd(q, k, v, *, causal=False, dropout_p=0.0, seed=0, rng_offset=0, key_lens=
                                                 device=q.device)
     l = lse if lse is not None else torch.empty((B, H, N), dtype=torch.float32, device=q.device)
     opts, keep, tiles = _opts(B, H, N, d, 0, key_lens, rng_offset, o_fp32, record_tiles, reverse_kv,
-                              q.device, dt, events, hkv)
+                              q.device, dt, events, hkv, causal)
     bm, bmp = _mask_ptr(block_mask, q.device, N)
-    need = fwd_workspace_bytes(B, H, N, d, q.dtype)
+    need = fwd_workspace_bytes(B, hkv, N, d, q.dtype)
     ws = workspace
     if ws is None and need:
         ws = torch.empty(need, dtype=torch.uint8, device=q.device)
@@ -165,7 +167,7 @@ def bwd(q, k, v, o, do, lse, *, causal=False, dropout_p=0.0, seed=0, rng_offset=
     need = bwd_workspace_bytes(B, H, N, d)
     ws = workspace if workspace is not None else torch.empty(need, dtype=torch.uint8, device=q.device)
     opts, keep, tiles = _opts(B, H, N, d, 1, key_lens, rng_offset, o_fp32, record_tiles, False, q.device, dt,
-                              events, hkv)
+                              events, hkv, causal)
     bm, bmp = _mask_ptr(block_mask, q.device, N)
     code = _lib.lib().fa_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), do.data_ptr(),
                              lse.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), B, H, N, d, dt,
@@ -259,9 +261,12 @@ def dropout_keep_mask(seed, rng_offset, p, B, H, N, device="cuda"):
     return keep
 
 
-def tile_shape(d: int, dtype_code: int, pass_: int):
+def tile_shape(d: int, dtype_code: int, pass_: int, N: int, causal: bool):
+    """(Br, Bc) of the kernel fa_fwd (pass 0) or fa_bwd (1: dK/dV, 2: dQ)
+    launches for this head dim, dtype, N and causal flag."""
     br, bc = ctypes.c_int32(), ctypes.c_int32()
-    check(_lib.lib().fa_tile_shape(d, dtype_code, pass_, ctypes.byref(br), ctypes.byref(bc)), "fa_tile_shape")
+    check(_lib.lib().fa_tile_shape(d, dtype_code, pass_, N, 1 if causal else 0, ctypes.byref(br),
+                                   ctypes.byref(bc)), "fa_tile_shape")
     return br.value, bc.value
 
 

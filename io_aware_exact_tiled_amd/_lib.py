@@ -84,7 +84,7 @@ def lib():
         L.fa_fwd_kv_outer_workspace_bytes.restype = sz
         L.fa_dropout_keep_mask.argtypes = [u64, u64, f32, i32, i32, i32, vp, vp]
         L.fa_dropout_keep_mask.restype = i32
-        L.fa_tile_shape.argtypes = [i32, i32, i32, ctypes.POINTER(i32), ctypes.POINTER(i32)]
+        L.fa_tile_shape.argtypes = [i32, i32, i32, i32, i32, ctypes.POINTER(i32), ctypes.POINTER(i32)]
         L.fa_tile_shape.restype = i32
         L.fa_status_string.argtypes = [i32]
         L.fa_status_string.restype = ctypes.c_char_p

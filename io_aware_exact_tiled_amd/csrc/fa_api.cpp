@@ -77,7 +77,9 @@ fa::DropArgs drop_args(float p, uint64_t seed, const fa_opts* opts) {
     fa::DropArgs d;
     d.on = p > 0.0f ? 1u : 0u;
     d.thr = drop_threshold(p);
-    d.keep_scale = d.on ? (float)(1.0 / (1.0 - (double)p)) : 1.0f;
+    // kept entries are scaled by the inverse of the exact keep probability
+    // (2^16 - thr) / 2^16, so the dropped product is unbiased
+    d.keep_scale = d.on ? (float)(65536.0 / (65536.0 - (double)d.thr)) : 1.0f;
     d.k0 = (uint32_t)(seed & 0xFFFFFFFFu);
     d.k1 = (uint32_t)(seed >> 32);
     d.off = opts ? (uint32_t)(opts->rng_offset & 0xFFFFFFFFu) : 0u;
@@ -112,23 +114,30 @@ const char* fa_status_string(fa_status s) {
 
 const char* fa_last_hip_error(void) { return g_hip_error; }
 
-fa_status fa_tile_shape(int32_t d, fa_dtype dtype, int32_t pass, int32_t* Br, int32_t* Bc) {
+fa_status fa_tile_shape(int32_t d, fa_dtype dtype, int32_t pass, int32_t N, int32_t causal, int32_t* Br,
+                        int32_t* Bc) {
     if (!Br || !Bc) return FA_ERR_NULL;
     if (d != 64 && d != 128) return FA_ERR_HEAD_DIM;
     if (!valid_dtype(dtype)) return FA_ERR_DTYPE;
+    if (N < 1) return FA_ERR_SHAPE;
     if (pass == 0) { *Br = fa::FWD_BR; *Bc = fa::FWD_BC; return FA_OK; }
     if (pass == 1) {
-        *Br = dtype == FA_F32 ? fa::BWD_KV_BR32 : fa::BWD_KV_BR16;
-        *Bc = fa::BWD_KV_BC;
+        if (fa::bwd_kv_small(dtype, d, N, causal)) {
+            *Br = fa::BWD_KV_SMALL_BR;
+            *Bc = fa::BWD_KV_SMALL_BC;
+        } else {
+            *Br = dtype == FA_F32 ? fa::BWD_KV_BR32 : fa::BWD_KV_BR16;
+            *Bc = fa::BWD_KV_BC;
+        }
         return FA_OK;
     }
     if (pass == 2) { *Br = fa::BWD_DQ_BR; *Bc = fa::BWD_DQ_BC; return FA_OK; }
     return FA_ERR_OPTS;
 }
 
-size_t fa_fwd_workspace_bytes(int32_t B, int32_t H, int32_t N, int32_t d, fa_dtype dtype) {
-    if (check_shape(B, H, N, d) != FA_OK || !valid_dtype(dtype)) return 0;
-    return dtype == FA_BF16 ? fa::fwd_workspace_layout(B, H, N, d).bytes : 0;
+size_t fa_fwd_workspace_bytes(int32_t B, int32_t Hkv, int32_t N, int32_t d, fa_dtype dtype) {
+    if (check_shape(B, Hkv, N, d) != FA_OK || !valid_dtype(dtype)) return 0;
+    return dtype == FA_BF16 ? fa::fwd_workspace_layout(B, Hkv, N, d).bytes : 0;
 }
 
 fa_status fa_fwd(const void* Q, const void* K, const void* V, void* O, float* LSE, int32_t B, int32_t H,
@@ -140,11 +149,12 @@ fa_status fa_fwd(const void* Q, const void* K, const void* V, void* O, float* LS
     if (st != FA_OK) return st;
     if (!aligned16(Q) || !aligned16(K) || !aligned16(V) || !aligned16(O) || !aligned16(LSE))
         return FA_ERR_ALIGN;
-    const size_t need = fa_fwd_workspace_bytes(B, H, N, d, dtype);
-    if (need && (!workspace || workspace_bytes < need || (reinterpret_cast<uintptr_t>(workspace) & 255u)))
-        return FA_ERR_WORKSPACE;
     const int32_t hkv = kv_heads(H, opts);
     if (!hkv) return FA_ERR_OPTS;
+    // the bf16 V copy covers the K/V heads only
+    const size_t need = fa_fwd_workspace_bytes(B, hkv, N, d, dtype);
+    if (need && (!workspace || workspace_bytes < need || (reinterpret_cast<uintptr_t>(workspace) & 255u)))
+        return FA_ERR_WORKSPACE;
     fa::FwdArgs a;
     a.q = Q; a.k = K; a.v = V; a.o = O; a.lse = LSE;
     a.B = B; a.H = H; a.N = N; a.Hkv = hkv;

@@ -605,18 +605,18 @@ hipError_t launch_t(const BwdArgs& a, hipStream_t s) {
     hipError_t e = hipLaunchKernel((const void*)&bwd_pre_kernel<T, D>, dim3((unsigned)((rows + RPB - 1) / RPB)),
                                    dim3(256), args, 0, s);
     if (e != hipSuccess) return e;
-    // the dK/dV configuration (16-bit inputs): 64-key workgroups at d = 64
+    // the dK/dV configuration: 64-key workgroups for 16-bit inputs at d = 64
     // and for causal sequences up to BWD_KV_SMALL_N, where they were measured
-    // faster (never while tile visits are recorded: that map has 128-key tiles)
-    const bool small = sizeof(T) == 2 && !a.tile_visits && (D == 64 || (a.mask.causal && a.N <= BWD_KV_SMALL_N));
-    const int kbc = small ? BWD_KV_BC / 2 : BWD_KV_BC;
+    // faster (a recorded tile map has that configuration's tile shape)
+    const bool small = bwd_kv_small(sizeof(T) == 4 ? FA_F32 : FA_BF16, D, a.N, a.mask.causal);
+    const int kbc = small ? BWD_KV_SMALL_BC : BWD_KV_BC;
     const int kv_total = ((a.N + kbc - 1) / kbc) * a.Hkv * a.B;
     const int dq_total = ((a.N + BWD_DQ_BR - 1) / BWD_DQ_BR) * a.H * a.B;
     if (a.ev_begin && (e = hipEventRecord(a.ev_begin, s)) != hipSuccess) return e;
     const dim3 kv_grid((unsigned)(8 * ((kv_total + 7) / 8)));
     const void* kv_fn = (const void*)&bwd_kv_kernel<T, D, DROP, 8, BwdTiles<T>::KV_BR>;
     if constexpr (sizeof(T) == 2) {
-        if (small) kv_fn = (const void*)&bwd_kv_kernel<T, D, DROP, 4, 32>;
+        if (small) kv_fn = (const void*)&bwd_kv_kernel<T, D, DROP, 4, BWD_KV_SMALL_BR>;
     }
     e = hipLaunchKernel(kv_fn, kv_grid, dim3(small ? 256 : 512), args, 0, s);
     if (e != hipSuccess) return e;

@@ -353,7 +353,7 @@ hipError_t launch_d(const FwdArgs& a, int d, hipStream_t s) {
 hipError_t launch_fwd(FwdArgs a, fa_dtype dt, int d, void* workspace, hipStream_t s) {
     a.vexp = nullptr;
     if (dt == FA_BF16) {
-        const FwdWorkspace L = fwd_workspace_layout(a.B, a.H, a.N, d);
+        const FwdWorkspace L = fwd_workspace_layout(a.B, a.Hkv, a.N, d);   // the K/V heads' V
         char* ws = static_cast<char*>(workspace);
         V16Args p;
         p.v = a.v;

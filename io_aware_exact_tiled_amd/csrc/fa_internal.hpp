@@ -14,11 +14,10 @@ namespace fa {
 // rows (4 waves x 32) and walks key tiles of FWD_BC.  Backward dK/dV kernel: a
 // workgroup owns BWD_KV_BC keys (8 waves: 4 key blocks of 32 x 2 roles) and
 // walks query tiles of BwdTiles<T>::KV_BR rows -- or, for 16-bit inputs at
-// d = 64 and for short causal sequences, half that (4 waves, 64 keys,
-// 32-row query tiles; not while tile visits are recorded).  Backward dQ
-// kernel: a workgroup owns BWD_DQ_BR
-// query rows and walks key tiles of BWD_DQ_BC.  All divide the 128-token
-// block-mask tile.
+// d = 64 and for short causal sequences (bwd_kv_small), 4 waves owning 64
+// keys that walk 32-row query tiles.  Backward dQ kernel: a workgroup owns
+// BWD_DQ_BR query rows and walks key tiles of BWD_DQ_BC.  All divide the
+// 128-token block-mask tile.
 constexpr int MASK_TILE = 128;   // block-mask granularity (tokens)
 constexpr int FWD_BR = 128;
 constexpr int FWD_BC = 64;
@@ -37,6 +36,16 @@ template <int D> constexpr int BWD_PF = D == 64 ? 2 : 3;
 template <class T> struct BwdTiles {
     static constexpr int KV_BR = sizeof(T) == 4 ? BWD_KV_BR32 : BWD_KV_BR16;
 };
+constexpr int BWD_KV_SMALL_BC = 64;   // keys per workgroup of the four-wave dK/dV configuration
+constexpr int BWD_KV_SMALL_BR = 32;   // its query rows per step
+
+// The dK/dV configuration fa_bwd launches: the four-wave one for 16-bit
+// inputs at d = 64 and for causal d = 128 sequences up to BWD_KV_SMALL_N
+// (where a lone 8-wave workgroup per CU leaves its prologue and epilogue
+// exposed), else the eight-wave one.
+inline bool bwd_kv_small(fa_dtype dt, int d, int N, int causal) {
+    return dt != FA_F32 && (d == 64 || (causal && N <= BWD_KV_SMALL_N));
+}
 
 struct MaskArgs {
     int causal;
@@ -48,7 +57,7 @@ struct MaskArgs {
 struct DropArgs {
     uint32_t on;          // 1 iff p > 0 (kept entries scaled, mask applied)
     uint32_t thr;         // drop iff the element's 16-bit uniform u < thr
-    float keep_scale;     // 1 / (1 - p)
+    float keep_scale;     // 2^16 / (2^16 - thr): the inverse of the keep probability
     uint32_t k0, k1;      // Philox key (seed low, high)
     uint32_t off;         // Philox counter word 3
 };

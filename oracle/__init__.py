@@ -26,6 +26,6 @@ multipliers come from the SC'11 paper without a known-answer vector here).
 from .attention import (attn_fwd, attn_bwd, attn_bwd_rows_cols, attn_stats, kv_head, decode_fwd,  # noqa: F401
                         tiled_fwd, kv_outer_fwd, attn_bwd_jacobian, validity, safe_softmax,
                         as_f64, scale_f32)
-from .philox import (philox4x32_10, philox4_scalar, keep_mask,  # noqa: F401
+from .philox import (philox4x32_10, philox4_scalar, keep_mask, keep_scale,  # noqa: F401
                      dropout_threshold)
 from .tiles import expected_tiles, tile_has_valid, valid_pair_count  # noqa: F401

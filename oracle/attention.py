@@ -21,11 +21,12 @@ What it computes is the plain definition that tiled exact attention reaches
   recomputation).  A row with no valid key has P = 0, O = 0, LSE = -inf.
 * dropout on P after the softmax and before the product with V (explainer,
   kernel fusion: matmul, mask, softmax, dropout, matmul), inverted scaling
-  1/(1-p); l and LSE use the undropped P.
+  by s = 1 / P(keep) (`philox.keep_scale`: 2^16 / (2^16 - thr), the
+  keep rule's exact probability); l and LSE use the undropped P.
 * O = P_hat V.
 * backward (the pages say only that S and P are recomputed; the gradients
   follow from the definition with the softmax Jacobian diag(p) - p p^T):
-      dP_hat = dO V^T,  dV = P_hat^T dO,  dP = dP_hat * Z / (1-p),
+      dP_hat = dO V^T,  dV = P_hat^T dO,  dP = dP_hat * Z * s,
       D_i = sum_j P_ij dP_ij,  dS = P * (dP - D),
       dQ = scale dS K,  dK = scale dS^T Q.
 
@@ -53,7 +54,7 @@ from __future__ import annotations
 
 import numpy as np
 
-from .philox import keep_mask
+from .philox import keep_mask, keep_scale
 
 MASK_TILE = 128
 
@@ -140,7 +141,7 @@ def attn_fwd(q, k, v, scale, causal=False, key_lens=None, block_mask=None,
             P, lse, _, _ = safe_softmax(S, A)
             if dropout_p > 0.0:
                 Z = keep_mask(seed, rng_offset, dropout_p, b, h, H, r, np.arange(N))
-                P = P * Z / (1.0 - float(np.float32(dropout_p)))
+                P = P * Z * keep_scale(dropout_p)
             O[b, h, s:s + chunk] = P @ v[b, g]
             LSE[b, h, s:s + chunk] = lse
     return O, LSE
@@ -153,7 +154,7 @@ def attn_bwd(q, k, v, do, scale, causal=False, key_lens=None, block_mask=None,
     q, k, v, do = as_f64(q), as_f64(k), as_f64(v), as_f64(do)
     B, H, N, d = q.shape
     sc = scale_f32(scale)
-    keep_scale = 1.0 / (1.0 - float(np.float32(dropout_p))) if dropout_p > 0 else 1.0
+    ks = keep_scale(dropout_p)
     dq = np.zeros_like(q)
     dk = np.zeros_like(k)
     dv = np.zeros_like(v)
@@ -171,10 +172,10 @@ def attn_bwd(q, k, v, do, scale, causal=False, key_lens=None, block_mask=None,
                 Z = keep_mask(seed, rng_offset, dropout_p, b, h, H, r, np.arange(N))
             else:
                 Z = np.ones_like(P, dtype=bool)
-            P_hat = P * Z * keep_scale
+            P_hat = P * Z * ks
             dP_hat = do[b, h, r] @ v[b, g].T
             dv[b, g] += P_hat.T @ do[b, h, r]
-            dP = dP_hat * Z * keep_scale
+            dP = dP_hat * Z * ks
             D = (P * dP).sum(axis=1)
             dS = P * (dP - D[:, None])
             dq[b, h, r] = sc * (dS @ k[b, g])
@@ -197,7 +198,7 @@ def attn_bwd_rows_cols(q, k, v, do, scale, rows, cols, lse_all, D_all,
     q, k, v, do = as_f64(q), as_f64(k), as_f64(v), as_f64(do)
     B, H, N, d = q.shape
     sc = scale_f32(scale)
-    keep_scale = 1.0 / (1.0 - float(np.float32(dropout_p))) if dropout_p > 0 else 1.0
+    ks = keep_scale(dropout_p)
     rows = np.asarray(rows)
     cols = np.asarray(cols)
     Hkv = k.shape[1]
@@ -213,7 +214,7 @@ def attn_bwd_rows_cols(q, k, v, do, scale, rows, cols, lse_all, D_all,
         P, _, _, _ = safe_softmax(S, A)
         Z = (keep_mask(seed, rng_offset, dropout_p, b, h, H, rows, np.arange(N))
              if dropout_p > 0 else np.ones_like(P, dtype=bool))
-        dP = (do[b, h, rows] @ v[b, g].T) * Z * keep_scale
+        dP = (do[b, h, rows] @ v[b, g].T) * Z * ks
         D = (P * dP).sum(axis=1)
         dq[b, h] = sc * ((P * (dP - D[:, None])) @ k[b, g])
         # dK, dV columns: all query rows, selected keys (none: nothing to add)
@@ -226,8 +227,8 @@ def attn_bwd_rows_cols(q, k, v, do, scale, rows, cols, lse_all, D_all,
             Pc = np.where(live, np.exp(np.where(live, Sc - lse[:, None], -np.inf)), 0.0)
             Zc = (keep_mask(seed, rng_offset, dropout_p, b, h, H, r, cols)
                   if dropout_p > 0 else np.ones_like(Pc, dtype=bool))
-            dv[b, g] += (Pc * Zc * keep_scale).T @ do[b, h, r]
-            dPc = (do[b, h, r] @ v[b, g, cols].T) * Zc * keep_scale
+            dv[b, g] += (Pc * Zc * ks).T @ do[b, h, r]
+            dPc = (do[b, h, r] @ v[b, g, cols].T) * Zc * ks
             dSc = Pc * (dPc - D_all[b, h, r][:, None])
             dk[b, g] += sc * (dSc.T @ q[b, h, r])
     return dq, dk, dv
@@ -240,7 +241,7 @@ def attn_stats(q, k, v, do, scale, causal=False, key_lens=None, block_mask=None,
     q, k, v, do = as_f64(q), as_f64(k), as_f64(v), as_f64(do)
     B, H, N, d = q.shape
     sc = scale_f32(scale)
-    keep_scale = 1.0 / (1.0 - float(np.float32(dropout_p))) if dropout_p > 0 else 1.0
+    ks = keep_scale(dropout_p)
     LSE = np.zeros((B, H, N))
     Dall = np.zeros((B, H, N))
     Hkv = k.shape[1]
@@ -254,7 +255,7 @@ def attn_stats(q, k, v, do, scale, causal=False, key_lens=None, block_mask=None,
             P, lse, _, _ = safe_softmax(S, A)
             Z = (keep_mask(seed, rng_offset, dropout_p, b, h, H, r, np.arange(N))
                  if dropout_p > 0 else np.ones_like(P, dtype=bool))
-            dP = (do[b, h, r] @ v[b, g].T) * Z * keep_scale
+            dP = (do[b, h, r] @ v[b, g].T) * Z * ks
             LSE[b, h, r] = lse
             Dall[b, h, r] = (P * dP).sum(axis=1)
     return LSE, Dall
@@ -375,7 +376,7 @@ def attn_bwd_jacobian(q, k, v, do, scale, causal=False, key_lens=None,
     q, k, v, do = as_f64(q), as_f64(k), as_f64(v), as_f64(do)
     B, H, N, d = q.shape
     sc = scale_f32(scale)
-    ks = 1.0 / (1.0 - float(np.float32(dropout_p))) if dropout_p > 0 else 1.0
+    ks = keep_scale(dropout_p)
     dq = np.zeros_like(q)
     dk = np.zeros_like(k)
     dv = np.zeros_like(v)

@@ -29,7 +29,10 @@ for the even row of the pair and the high half for the odd one:
   w = output word (j & 3),  u = (w >> 16) if i is odd else (w & 0xFFFF)
   keep iff u >= thr,  thr = min(floor(float32(p) * 2^16), 2^16 - 1)
 so the drop probability is thr / 2^16, within 2^-16 of p.  Kept entries are
-scaled by 1 / (1 - p) whenever p > 0.
+scaled by the inverse of the exact keep probability, 2^16 / (2^16 - thr),
+whenever p > 0 (inverted dropout: each scaled keep bit has expectation 1, so
+the expected dropped O equals the undropped one; the explainer names dropout
+among the operations fused after the softmax but not its scaling).
 """
 
 from __future__ import annotations
@@ -89,6 +92,14 @@ def dropout_threshold(p: float) -> int:
     Computed from the float32 value of p, as the kernels receive it."""
     p32 = float(np.float32(p))
     return min(int(np.floor(p32 * 2.0 ** 16)), 2 ** 16 - 1)
+
+
+def keep_scale(p: float) -> float:
+    """Factor applied to kept entries: 1 / P(keep) = 2^16 / (2^16 - thr)
+    for p > 0, else 1 (no dropout)."""
+    if p <= 0:
+        return 1.0
+    return 2.0 ** 16 / (2.0 ** 16 - dropout_threshold(p))
 
 
 def keep_mask(seed: int, rng_offset: int, p: float, b: int, h: int, H: int,

@@ -22,8 +22,8 @@ int main(void) {
     o.struct_size = sizeof(fa_opts);
 
     CHECK(fa_abi_version() == FA_ABI_VERSION);
-    CHECK(fa_tile_shape(128, FA_BF16, 0, &br, &bc) == FA_OK && br > 0 && bc > 0 && 128 % br == 0 && 128 % bc == 0);
-    CHECK(fa_tile_shape(96, FA_BF16, 0, &br, &bc) == FA_ERR_HEAD_DIM);
+    CHECK(fa_tile_shape(128, FA_BF16, 0, 4096, 1, &br, &bc) == FA_OK && br > 0 && bc > 0 && 128 % br == 0 && 128 % bc == 0);
+    CHECK(fa_tile_shape(96, FA_BF16, 0, 4096, 1, &br, &bc) == FA_ERR_HEAD_DIM);
     CHECK(fa_status_string(FA_ERR_SHAPE) != NULL);
 
     /* forward / backward: NULL pointer, bad head dim, bad dropout, bad opts size */

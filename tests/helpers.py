@@ -13,10 +13,14 @@ Tolerances (inputs in bf16/fp16 unless stated):
      of dP - D, two evaluations of one O(1) sum).
 """
 
+import multiprocessing
+import os
+
 import numpy as np
 import torch
 
 import oracle
+import workloads as W
 
 O_TOL = {torch.bfloat16: 2e-3, torch.float16: 2e-3, torch.float32: 1e-4}
 LSE_TOL = {torch.bfloat16: 1e-3, torch.float16: 1e-3, torch.float32: 1e-4}
@@ -79,3 +83,42 @@ def oracle_kw(x):
 def fa_kw(x):
     return dict(causal=x["causal"], key_lens=cuda(x["key_lens"]), block_mask=cuda(x["block_mask"]),
                 dropout_p=x["dropout_p"], seed=x["seed"], rng_offset=x["rng_offset"], scale=x["scale"])
+
+
+_WORKER_INPUTS = {}
+
+
+def _kv_grads_worker(job):
+    """dK, dV of the sampled key rows `cols` for the K/V heads in `kv` (each
+    with all the query heads that read it), from a fresh draw of workload w's
+    inputs: every row's LSE and D first (attn_stats), then the score columns."""
+    import threadpoolctl
+    w, kv, cols = job
+    with threadpoolctl.threadpool_limits(2):
+        if _WORKER_INPUTS.get("w") != w:          # one draw per worker process
+            _WORKER_INPUTS.update(w=w, x=W.make_inputs(w))
+        x = _WORKER_INPUTS["x"]
+        okw = oracle_kw(x)
+        G = w.H // w.Hkv
+        heads = [(b, g * G + hh) for b, g in kv for hh in range(G)]
+        Ls, Ds = oracle.attn_stats(x["q"], x["k"], x["v"], x["do"], x["scale"], heads=heads, **okw)
+        _, rk, rv = oracle.attn_bwd_rows_cols(x["q"], x["k"], x["v"], x["do"], x["scale"], np.arange(1), cols,
+                                              Ls, Ds, pairs=heads, **okw)
+    return kv, rk[[b for b, _ in kv], [g for _, g in kv]], rv[[b for b, _ in kv], [g for _, g in kv]]
+
+
+def oracle_kv_grads(w, cols, workers=None):
+    """Oracle dK, dV [B, Hkv, len(cols), d] at the sampled key rows of every
+    K/V head of workload w, one K/V head per task over a pool of fresh
+    processes (spawned: they never touch the GPU)."""
+    jobs = [(w, [(b, g)], cols) for b in range(w.B) for g in range(w.Hkv)]
+    workers = workers or max(1, min(8, (os.cpu_count() or 2) // 2, len(jobs)))
+    rk = np.zeros((w.B, w.Hkv, len(cols), w.d))
+    rv = np.zeros_like(rk)
+    ctx = multiprocessing.get_context("spawn")
+    with ctx.Pool(workers) as pool:
+        for n, (kv, k_, v_) in enumerate(pool.imap_unordered(_kv_grads_worker, jobs)):
+            for t, (b, g) in enumerate(kv):
+                rk[b, g], rv[b, g] = k_[t], v_[t]
+            print(f"  oracle dK/dV: {n + 1}/{len(jobs)} K/V heads", flush=True)
+    return rk, rv

@@ -41,21 +41,44 @@ def test_library_exports_every_declared_symbol():
 
 def test_scalars():
     L = _lib()
-    assert L.fa_abi_version() == 6
+    assert L.fa_abi_version() == 7
     for code in list(lib_mod.STATUS) + [-99]:
         assert isinstance(L.fa_status_string(code), bytes)
     br, bc = ctypes.c_int32(), ctypes.c_int32()
     for d in (64, 128):
         for dt in (0, 1, 2):
             for p in (0, 1, 2):
-                assert L.fa_tile_shape(d, dt, p, ctypes.byref(br), ctypes.byref(bc)) == 0
-                assert 128 % br.value == 0 and 128 % bc.value == 0
-    assert L.fa_tile_shape(96, 2, 0, ctypes.byref(br), ctypes.byref(bc)) == -3
-    assert L.fa_tile_shape(64, 7, 0, ctypes.byref(br), ctypes.byref(bc)) == -4
+                for N, causal in ((1, 0), (2048, 1), (2049, 1), (4096, 0)):
+                    assert L.fa_tile_shape(d, dt, p, N, causal, ctypes.byref(br), ctypes.byref(bc)) == 0
+                    assert 128 % br.value == 0 and 128 % bc.value == 0
+    assert L.fa_tile_shape(96, 2, 0, 64, 0, ctypes.byref(br), ctypes.byref(bc)) == -3
+    assert L.fa_tile_shape(64, 7, 0, 64, 0, ctypes.byref(br), ctypes.byref(bc)) == -4
+    assert L.fa_tile_shape(64, 2, 0, 0, 0, ctypes.byref(br), ctypes.byref(bc)) == -2
     assert L.fa_bwd_workspace_bytes(1, 2, 256, 64) == 2048
     assert L.fa_bwd_workspace_bytes(1, 1, 3, 64) == 256
-    assert L.fa_tile_shape(64, 2, 3, ctypes.byref(br), ctypes.byref(bc)) == -10
+    assert L.fa_tile_shape(64, 2, 3, 64, 0, ctypes.byref(br), ctypes.byref(bc)) == -10
     assert L.fa_bwd_workspace_bytes(0, 1, 3, 64) == 0
+
+
+@pytest.mark.parametrize("d,dt,N,causal,want", [
+    # the four-wave dK/dV configuration: 16-bit inputs at d = 64 (any N, mask),
+    # and causal d = 128 up to N = 2048
+    (64, 2, 16384, 0, (32, 64)), (64, 1, 512, 1, (32, 64)), (128, 2, 2048, 1, (32, 64)),
+    # the eight-wave one: 128 keys x 64 query rows (fp32: 32 rows)
+    (128, 2, 2049, 1, (64, 128)), (128, 1, 1024, 0, (64, 128)), (128, 2, 16384, 1, (64, 128)),
+    (64, 0, 256, 0, (32, 128)), (128, 0, 100, 1, (32, 128))])
+def test_tile_shape_names_the_launched_dkdv_kernel(d, dt, N, causal, want):
+    """fa_tile_shape(pass 1) is the tile of the dK/dV configuration fa_bwd
+    launches for (d, dtype, N, causal); forward and dQ tiles do not depend on
+    N or the mask."""
+    L = _lib()
+    br, bc = ctypes.c_int32(), ctypes.c_int32()
+    assert L.fa_tile_shape(d, dt, 1, N, causal, ctypes.byref(br), ctypes.byref(bc)) == 0
+    assert (br.value, bc.value) == want
+    assert L.fa_tile_shape(d, dt, 0, N, causal, ctypes.byref(br), ctypes.byref(bc)) == 0
+    assert (br.value, bc.value) == (128, 64)
+    assert L.fa_tile_shape(d, dt, 2, N, causal, ctypes.byref(br), ctypes.byref(bc)) == 0
+    assert (br.value, bc.value) == (128, 64)
 
 
 P = 0x10000  # a 256-byte aligned fake device address: never dereferenced on these paths
@@ -126,6 +149,21 @@ def test_fwd_workspace_validation():
     assert fwd(L, ws=None) == -8
     assert fwd(L, ws_bytes=need - 1) == -8
     assert fwd(L, ws=P + 16) == -8                  # not 256-byte aligned
+
+
+def test_fwd_workspace_counts_kv_heads():
+    """Grouped-query attention: the bf16 V copy covers the K/V heads only, so
+    the sizer takes Hkv; fa_fwd checks against that size (one byte less is
+    rejected before any launch), and the query-head value is an upper bound."""
+    L = _lib()
+    B, H, Hkv, N, d = 2, 8, 2, 1000, 128
+    need_kv = L.fa_fwd_workspace_bytes(B, Hkv, N, d, 2)
+    need_q = L.fa_fwd_workspace_bytes(B, H, N, d, 2)
+    assert need_kv >= align256(B * Hkv * N * d * 2) and need_q >= 3 * need_kv
+    o = lib_mod.FaOpts()
+    o.struct_size = ctypes.sizeof(lib_mod.FaOpts)
+    o.kv_heads = Hkv
+    assert fwd(L, B=B, H=H, N=N, d=d, opts=ctypes.byref(o), ws_bytes=need_kv - 1) == -8
 
 
 def test_kv_heads_validation():
@@ -238,22 +276,3 @@ def test_header_compiles_as_c_and_links(tmp_path):
     run = subprocess.run([exe], capture_output=True, text=True, timeout=60)
     assert run.returncode == 0, run.stdout + run.stderr
     assert "c abi ok" in run.stdout
-
-
-def test_ceiling_probe_builds_for_gfx950(tmp_path):
-    """bench_ceiling.hip (the MFMA ceiling probe quoted beside the roofline)
-    still compiles for gfx950 with the library's flags; its device code
-    issues the 32x32x16 MFMAs and 16-byte LDS reads it is meant to time."""
-    import shutil
-    hipcc = shutil.which("hipcc") or "/opt/rocm/bin/hipcc"
-    if not os.path.exists(hipcc):
-        pytest.skip("hipcc not available")
-    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
-    asm = str(tmp_path / "ceiling.s")
-    cmd = [hipcc, "-O3", "--offload-arch=gfx950", "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-           "--cuda-device-only", "-S", os.path.join(root, "bench_ceiling.hip"), "-o", asm]
-    build = subprocess.run(cmd, capture_output=True, text=True)
-    assert build.returncode == 0, build.stderr
-    text = open(asm).read()
-    assert "v_mfma_f32_32x32x16_bf16" in text and "v_mfma_f32_32x32x16_f16" in text
-    assert "ds_read_b128" in text and "v_exp_f32" in text

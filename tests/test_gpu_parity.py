@@ -120,7 +120,8 @@ def test_grouped_query_tile_visits():
     dq, dk, dv, tb = fa.bwd(q, k, v, o, do, lse, record_tiles=True, **fa_kw(x))
     okw = oracle_kw(x)
     for pass_, t in ((1, tb[0]), (2, tb[1])):
-        br, bc = fa.tile_shape(64, 2, pass_)
+        br, bc = fa.tile_shape(64, 2, pass_, N, True)
+        assert t.shape[2:] == (-(-N // br), -(-N // bc))
         want = oracle.expected_tiles(N, br, bc, 1, okw["causal"], okw["key_lens"], okw["block_mask"])
         got = t.cpu().numpy()
         for h in range(4):
@@ -216,25 +217,70 @@ def test_dropout_keep_mask_bit_exact():
                 assert np.array_equal(keep[b, h].astype(bool), want), (seed, off, p, b, h)
 
 
-@pytest.mark.parametrize("case", [
-    dict(N=1000, causal=True), dict(N=1000, causal=False, kl=True), dict(N=700, causal=True, sparse=True),
-    dict(N=384, causal=False, sparse=True, kl=True)])
+TILE_CASES = [
+    # (N, d, dtype, causal, key_lens, sparse); the dK/dV kernel each one runs
+    (1000, 64, "bf16", True, False, False),     # four-wave dK/dV (32 x 64 tiles)
+    (1000, 64, "bf16", False, True, False),
+    (700, 64, "bf16", True, False, True),
+    (384, 64, "bf16", False, True, True),
+    (777, 64, "fp16", True, True, True),
+    (300, 64, "fp32", True, True, True),         # fp32: eight waves, 32 x 128
+    (2048, 128, "bf16", True, False, True),      # causal d = 128 up to 2048: four waves
+    (1100, 128, "fp16", True, True, False),
+    (2300, 128, "bf16", True, False, True),      # causal d = 128 past 2048: eight waves, 64 x 128
+    (640, 128, "bf16", False, True, True),
+    (500, 128, "fp16", False, False, True),
+    (257, 128, "fp32", False, True, True),
+]
+
+
+@pytest.mark.parametrize("case", TILE_CASES, ids=lambda c: "N%d-d%d-%s-c%d-kl%d-sp%d" % c)
 def test_tile_visits_bit_exact(case):
-    N = case["N"]
-    x = W.random_case(2, 2, N, 64, dtype="bf16", seed=N, causal=case["causal"],
-                      sparse_density=0.3 if case.get("sparse") else None)
-    if case.get("kl"):
+    """Every kernel's set of visited tiles, at the tile shape fa_tile_shape
+    names for this (d, dtype, N, causal), equals the exact set of tiles that
+    hold a valid pair (summary, "Block-Sparse FlashAttention"; tutorial 10.2),
+    for each kernel configuration fa_bwd can launch; the gradients recorded
+    alongside still match the oracle (recording does not change the kernel)."""
+    N, d, dtype, causal, kl, sparse = case
+    print(f"[case] tile visits {case}", flush=True)
+    x = W.random_case(2, 2, N, d, dtype=dtype, seed=N + d, causal=causal,
+                      sparse_density=0.3 if sparse else None)
+    if kl:
         x["key_lens"] = torch.tensor([N // 5, N - 1], dtype=torch.int32)
     q, k, v, do = (cuda(x[n]) for n in ("q", "k", "v", "do"))
     o, lse, tf = fa.fwd(q, k, v, record_tiles=True, **fa_kw(x))
     dq, dk, dv, tb = fa.bwd(q, k, v, o, do, lse, record_tiles=True, **fa_kw(x))
+    ref = fa.bwd(q, k, v, o, do, lse, **fa_kw(x))
+    torch.cuda.synchronize()
+    for a, b in zip((dq, dk, dv), ref):
+        assert torch.equal(a, b)
     okw = oracle_kw(x)
+    code = {"bf16": 2, "fp16": 1, "fp32": 0}[dtype]
     for pass_, t in ((0, tf), (1, tb[0]), (2, tb[1])):
-        br, bc = fa.tile_shape(64, 2, pass_)
+        br, bc = fa.tile_shape(d, code, pass_, N, causal)
+        assert t.shape[2:] == (-(-N // br), -(-N // bc))
         want = oracle.expected_tiles(N, br, bc, 2, okw["causal"], okw["key_lens"], okw["block_mask"])
         got = t.cpu().numpy()
         for h in range(2):
             assert np.array_equal(got[:, h], want), f"pass {pass_} head {h}"
+    print(f"[ok] tile visits {case}", flush=True)
+
+
+def test_grouped_query_exact_workspace():
+    """The bf16 forward workspace covers the K/V heads only: a buffer of
+    exactly fwd_workspace_bytes(B, Hkv, ...) bytes (Hkv = H / 4) gives the
+    oracle's O."""
+    B, H, hkv, N, d = 2, 8, 2, 300, 128
+    x = W.random_case(B, H, N, d, dtype="bf16", seed=77, causal=True, kv_heads=hkv)
+    q, k, v = (cuda(x[n]) for n in ("q", "k", "v"))
+    need = fa.fwd_workspace_bytes(B, hkv, N, d, torch.bfloat16)
+    assert need < fa.fwd_workspace_bytes(B, H, N, d, torch.bfloat16)
+    ws = torch.empty(need, dtype=torch.uint8, device="cuda")
+    o, lse = fa.fwd(q, k, v, causal=True, o_fp32=True, workspace=ws)
+    torch.cuda.synchronize()
+    O, L = oracle.attn_fwd(x["q"], x["k"], x["v"], x["scale"], causal=True)
+    check_o(o, O, torch.bfloat16)
+    check_lse(lse, L, torch.bfloat16)
 
 
 def test_forward_is_deterministic_and_order_free():

@@ -1,10 +1,10 @@
 """GPU parity at the full sizes of the workloads, through the C ABI and
 in the launch configuration bench.py times.  Where the fp64 oracle cannot
 cover every output in seconds (the 16K-token workloads) it checks sampled
-query rows (O, LSE, dQ: each needs only that row's full score row) and, for
-two K/V heads, sampled key rows (dK, dV: each needs the full score columns
+query rows (O, LSE, dQ: each needs only that row's full score row) and
+sampled key rows (dK, dV: each needs the full score columns
 of every query head that reads that K/V head, plus every row's LSE and D
-from a chunked fp64 pass)."""
+from a chunked fp64 pass, for every K/V head, spread over a process pool)."""
 
 import numpy as np
 import pytest
@@ -12,7 +12,7 @@ import torch
 
 import oracle
 import workloads as W
-from helpers import check_grad, check_lse, check_o, cuda, f64, fa_kw, oracle_kw
+from helpers import check_grad, check_lse, check_o, cuda, f64, fa_kw, oracle_kv_grads, oracle_kw
 
 pytestmark = pytest.mark.gpu
 
@@ -45,7 +45,8 @@ def test_workload_full_oracle(name):
     print(f"[ok] {name} {res}", flush=True)
 
 
-@pytest.mark.parametrize("name", ["long", "sparse", "gqa"])
+@pytest.mark.timeout(900)
+@pytest.mark.parametrize("name", ["long", "long_noncausal", "sparse", "gqa"])
 def test_workload_sampled_oracle(name):
     w = W.WORKLOADS[name]
     print(f"[case] {name} sampled", flush=True)
@@ -57,23 +58,27 @@ def test_workload_sampled_oracle(name):
     O, L = oracle.attn_fwd(x["q"], x["k"], x["v"], x["scale"], rows=rows, **okw)
     res = dict(o=check_o(o32[:, :, rows], O, dtype), lse=check_lse(lse[:, :, rows], L, dtype),
                o_stored=check_o(o[:, :, rows], O, dtype, "O(stored)", stored=True))
-    # dQ on the sampled rows of every head; dK, dV on sampled keys of two K/V
-    # heads (summed over the query heads that read them)
-    G = w.H // w.Hkv
-    kvh = [(0, 0), (w.B - 1, w.Hkv - 1)]
-    heads = [(b, g * G + hh) for b, g in kvh for hh in range(G)]
-    cols = W.sample_rows(w.N, 128, w.seed + 1)
-    Ls, Ds = oracle.attn_stats(x["q"], x["k"], x["v"], x["do"], x["scale"], heads=heads, **okw)
+    print(f"  forward ok {res}", flush=True)
+    # dQ on the sampled rows of every head (each needs only its own score row;
+    # the LSE and D arguments are not read for dQ)
+    zeros = np.zeros((w.B, w.H, w.N))
     rq, _, _ = oracle.attn_bwd_rows_cols(x["q"], x["k"], x["v"], x["do"], x["scale"], rows,
-                                         np.array([], dtype=np.int64), Ls, Ds, **okw)
+                                         np.array([], dtype=np.int64), zeros, zeros, **okw)
     res["dq"] = check_grad(dq[:, :, rows], rq, dtype, "dQ(rows)")
-    _, rk, rv = oracle.attn_bwd_rows_cols(x["q"], x["k"], x["v"], x["do"], x["scale"], rows[:1], cols,
-                                          Ls, Ds, pairs=heads, **okw)
-    for b, g in kvh:
-        res[f"dk{b}.{g}"] = check_grad(dk[b:b + 1, g:g + 1, cols], rk[b:b + 1, g:g + 1], dtype, f"dK(b{b} g{g})")
-        res[f"dv{b}.{g}"] = check_grad(dv[b:b + 1, g:g + 1, cols], rv[b:b + 1, g:g + 1], dtype, f"dV(b{b} g{g})")
-    # the LSE and D the oracle used for the columns are its own, all rows
-    print(f"[ok] {name} {res}", flush=True)
+    print(f"  dQ ok {res['dq']:.3e}", flush=True)
+    # dK, dV on 256 sampled keys of every K/V head (summed over the query
+    # heads that read it), element by element; each needs every row's LSE and
+    # D from the oracle's own full pass
+    cols = W.sample_rows(w.N, 256, w.seed + 1)
+    rk, rv = oracle_kv_grads(w, cols)
+    dk_s, dv_s = dk[:, :, cols], dv[:, :, cols]
+    for b in range(w.B):
+        for g in range(w.Hkv):
+            res[f"dk{b}.{g}"] = check_grad(dk_s[b:b + 1, g:g + 1], rk[b:b + 1, g:g + 1], dtype, f"dK(b{b} g{g})")
+            res[f"dv{b}.{g}"] = check_grad(dv_s[b:b + 1, g:g + 1], rv[b:b + 1, g:g + 1], dtype, f"dV(b{b} g{g})")
+    print(f"[ok] {name} worst dK {max(v for k, v in res.items() if k.startswith('dk')):.3e} "
+          f"worst dV {max(v for k, v in res.items() if k.startswith('dv')):.3e} {dict(list(res.items())[:4])}",
+          flush=True)
 
 
 def test_decode_workload_full_oracle():

@@ -414,6 +414,24 @@ def test_dropout_zero_is_dense():
     assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
 
 
+def test_dropout_scale_closed_form():
+    """Q = 0 makes every valid weight 1/n; with V = I (N = d) the dropped
+    forward is O_ij = s Z_ij / n exactly, s = 2^16 / (2^16 - thr) the keep
+    scale: this pins dropout's placement after the softmax and before PV, its
+    scale, and that the softmax normaliser ignores the mask (p = 0.1, where
+    1/(1 - p) would differ)."""
+    N = 16
+    q = np.zeros((1, 2, N, N))
+    k = np.random.default_rng(3).standard_normal((1, 2, N, N))
+    v = np.broadcast_to(np.eye(N), (1, 2, N, N)).copy()
+    O, L = oracle.attn_fwd(q, k, v, 0.5, dropout_p=0.1, seed=21, rng_offset=2)
+    s = 65536 / (65536 - 6553)
+    for h in range(2):
+        Z = oracle.keep_mask(21, 2, 0.1, 0, h, 2, np.arange(N), np.arange(N))
+        np.testing.assert_allclose(O[0, h], s * Z / N, rtol=0, atol=1e-15)
+        np.testing.assert_allclose(L[0, h], np.log(N), rtol=0, atol=1e-14)
+
+
 def test_dropout_is_unbiased_and_lse_undropped():
     """E_Z[O] = O at p = 0 (inverted dropout), statistically over seeds; LSE
     ignores the mask."""

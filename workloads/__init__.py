@@ -85,6 +85,8 @@ WORKLOADS = {
     # long-context causal, d = 128; "N(0, 0.5)" read as variance 0.5
     "long": Workload("long", 1, 16, 16384, 128, "bf16", seed=4,
                      std=math.sqrt(0.5), causal=True, sample_rows=256),
+    # the d = 128, N >= 4K regime without the causal mask (every tile dense)
+    "long_noncausal": Workload("long_noncausal", 1, 16, 8192, 128, "bf16", seed=8, sample_rows=256),
     # block-sparse, 128x128 tiles, band of 3 + random to density 0.1
     "sparse": Workload("sparse", 1, 8, 16384, 64, "bf16", seed=5,
                        sparse_density=0.1, sample_rows=256),
