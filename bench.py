@@ -43,7 +43,9 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.json")
 CSRC = os.path.join(ROOT, "io_aware_exact_tiled_amd", "csrc")
 KERNEL_SOURCES = {"fwd_kernel": "fa_fwd.hip", "bwd_kv_kernel": "fa_bwd.hip", "bwd_dq_kernel": "fa_bwd.hip",
-                  "decode_split_kernel": "fa_decode.hip"}
+                  "bwd_pre_kernel": "fa_bwd.hip", "v16_convert_kernel": "fa_fwd.hip",
+                  "v16_rescale_kernel": "fa_fwd.hip", "decode_split_kernel": "fa_decode.hip",
+                  "decode_merge_kernel": "fa_decode.hip", "fwd_kvo_kernel": "fa_kvouter.hip"}
 
 
 def kernel_sources_sha256(kernel: str) -> str:
@@ -59,14 +61,14 @@ def kernel_sources_sha256(kernel: str) -> str:
 
 def measured_traffic(kernel: str, workload: str):
     """HBM bytes per launch from the committed counter summary, or None when
-    it is missing, was taken on another workload, or predates the kernel's
+    there is none for this workload and kernel or it predates the kernel's
     current sources."""
     try:
         with open(TRAFFIC_FILE) as fh:
-            e = json.load(fh)["kernels"][kernel]
-    except (OSError, KeyError, ValueError):
+            e = json.load(fh)["workloads"][workload][kernel]
+    except (OSError, KeyError, ValueError, TypeError):
         return None
-    if e.get("workload") != workload or e.get("sources_sha256") != kernel_sources_sha256(kernel):
+    if e.get("sources_sha256") != kernel_sources_sha256(kernel):
         return None
     return int(e["fetch_bytes"] + e["write_bytes"])
 
@@ -89,6 +91,11 @@ def parse():
     ap.add_argument("--compare-standard", action="store_true",
                     help="also time standard attention (five separate ops on vendor GEMMs) against this "
                          "library at N = 1K, 2K, 4K (extra JSON lines)")
+    ap.add_argument("--profile", metavar="DIR",
+                    help="run rocprofv3 (kernel trace + four counter passes) on the workload as child processes, "
+                         "writing raw output to DIR, then write the summaries under profiles/")
+    ap.add_argument("--profile-report", metavar="DIR",
+                    help="only reduce an existing --profile DIR into the summaries under profiles/")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="first run one plain device-to-device copy of MIB MiB (a known-size kernel "
                          "that hardware byte counters can be scaled by)")
@@ -625,8 +632,271 @@ def cpu_baseline(w, rows):
                         f"time by (N/R)^2 (not measured)"}
 
 
+# ---------------------------------------------------------------------------
+# rocprofv3 harness.  `bench.py --profile DIR --workload W` runs one kernel
+# trace and four counter passes of the workload as child processes (this
+# process never touches the GPU), then reduces their CSV output into the
+# summaries under profiles/: per-kernel launch times, HBM bytes scaled by a
+# plain device copy of known size, the clock, the MFMA busy fraction and the
+# LDS / VALU instruction mix (the figures the IO model of the method is
+# checked with: FlashAttention summary, "complexity"; Self-Attention tutorial
+# section 12.4, HBM accesses).  `--profile-report DIR` redoes only the
+# reduction from an existing DIR.
+
+PROFILES = os.path.join(ROOT, "profiles")
+PROFILE_TAGS = {"long": "long_causal_d128", "gpt2": "gpt2_causal_d64", "bert": "bert_fp16_padding_dropout",
+                "sparse": "block_sparse_d64", "gqa": "gqa_causal_d128", "decode": "decode",
+                "long_noncausal": "noncausal_d128_n8192", "tiny": "tiny_d64"}
+PMC_PASSES = (
+    ("fetch", ("FETCH_SIZE",)),
+    ("write", ("WRITE_SIZE",)),
+    ("sq1", ("SQ_WAVE_CYCLES", "SQ_BUSY_CYCLES", "SQ_INSTS_VALU", "SQ_INSTS_MFMA", "SQ_INSTS_LDS",
+             "SQ_INSTS_VALU_TRANS_F32", "SQ_VALU_MFMA_BUSY_CYCLES", "GRBM_GUI_ACTIVE")),
+    ("sq2", ("SQ_LDS_BANK_CONFLICT", "SQ_LDS_IDX_ACTIVE", "SQ_ACTIVE_INST_LDS", "SQ_WAIT_INST_LDS",
+             "SQ_ACTIVE_INST_VALU", "SQ_WAIT_ANY", "SQ_VALU_MFMA_COEXEC_CYCLES", "SQ_LDS_DATA_FIFO_FULL")),
+)
+PROFILE_KERNELS = ("fwd_kvo_kernel", "fwd_kernel", "bwd_kv_kernel", "bwd_dq_kernel", "bwd_pre_kernel",
+                   "v16_convert_kernel", "v16_rescale_kernel", "decode_split_kernel", "decode_merge_kernel",
+                   "copyBuffer")
+CALIBRATE_MIB = 256
+XCDS = 8
+SIMDS = 1024
+
+
+def short_kernel(name: str) -> str:
+    for k in PROFILE_KERNELS:
+        if k in name:
+            return k
+    return name[:40]
+
+
+def profile_commands(workload: str, steps: int, rocprof: str = "rocprofv3", python: str = sys.executable):
+    """(pass name, argv, output dir relative to DIR) of the trace pass and the
+    counter passes, each running this script on the workload."""
+    me = os.path.abspath(__file__)
+    cmds = [("trace", [rocprof, "--kernel-trace", "--stats", "-f", "csv", "-d", "{DIR}/trace", "-o", "run", "--",
+                       python, me, "--workload", workload, "--steps", str(steps), "--no-cpu-baseline"])]
+    regex = "|".join(PROFILE_KERNELS)
+    for name, counters in PMC_PASSES:
+        cmds.append((name, [rocprof, "--pmc", *counters, "--kernel-include-regex", regex, "-f", "csv", "-d",
+                            "{DIR}/" + name, "-o", "run", "--", python, me, "--workload", workload, "--steps", "2",
+                            "--warmup", "1", "--no-cpu-baseline", "--calibrate-copy", str(CALIBRATE_MIB)]))
+    return cmds
+
+
+def run_profile(out_dir: str, workload: str, steps: int, timeout_s: int = 240) -> None:
+    """Run the passes one after another as child processes (each in its own
+    process group, killed whole if it outlives timeout_s); stop at the first
+    failure."""
+    import signal
+    import subprocess
+    os.makedirs(out_dir, exist_ok=True)
+    env = dict(os.environ, TMPDIR=os.environ.get("TMPDIR", "/tmp"))
+    for name, argv in profile_commands(workload, steps):
+        argv = [a.replace("{DIR}", out_dir) for a in argv]
+        print(f"[profile] {name}: {' '.join(argv)}", flush=True)
+        with open(os.path.join(out_dir, name + ".out"), "w") as fo, \
+                open(os.path.join(out_dir, name + ".log"), "w") as fe:
+            p = subprocess.Popen(argv, stdout=fo, stderr=fe, cwd="/tmp", env=env, start_new_session=True)
+            try:
+                rc = p.wait(timeout=timeout_s)
+            except subprocess.TimeoutExpired:
+                os.killpg(p.pid, signal.SIGKILL)
+                p.wait()
+                raise SystemExit(f"[profile] {name}: killed after {timeout_s} s")
+        ok = _last_json(os.path.join(out_dir, name + ".out")) is not None
+        # rocprofv3 may end with a fault of its own after the program finished
+        # and its results are complete: accept that when the JSON line is there
+        if rc != 0 and not ok:
+            raise SystemExit(f"[profile] {name}: exit status {rc}; see {name}.log")
+        print(f"[profile] {name}: done (exit {rc})", flush=True)
+
+
+def _last_json(path):
+    try:
+        with open(path) as fh:
+            lines = [l for l in fh.read().splitlines() if l.startswith("{")]
+    except OSError:
+        return None
+    return json.loads(lines[-1]) if lines else None
+
+
+def _find_csv(d: str, suffix: str):
+    for root, _, files in os.walk(d):
+        for f in sorted(files):
+            if f.endswith(suffix):
+                return os.path.join(root, f)
+    return None
+
+
+def read_counters(path: str) -> dict:
+    """{kernel: {counter: value per dispatch}} from a rocprofv3 counter CSV:
+    the mean over the kernel's dispatches (for the calibration copy, the
+    largest copy dispatch: input uploads are copies too), plus _dur_ns, the
+    mean dispatch duration."""
+    import collections
+    import csv
+    vals = collections.defaultdict(lambda: collections.defaultdict(list))
+    for r in csv.DictReader(open(path)):
+        k = short_kernel(r["Kernel_Name"])
+        vals[k][r["Counter_Name"]].append(float(r["Counter_Value"]))
+        vals[k]["_dur_ns_" + r["Counter_Name"]].append(float(r["End_Timestamp"]) - float(r["Start_Timestamp"]))
+    out = {}
+    for k, d in vals.items():
+        red = max if k == "copyBuffer" else (lambda v: sum(v) / len(v))
+        out[k] = {c: red(v) for c, v in d.items() if not c.startswith("_dur_ns_")}
+        durs = [x for c, v in d.items() if c.startswith("_dur_ns_") for x in v]
+        out[k]["_dur_ns"] = sum(durs) / len(durs)
+    return out
+
+
+def derived_metrics(C: dict, copy_mib: float = CALIBRATE_MIB) -> dict:
+    """Per kernel: HBM read/write bytes per dispatch (FETCH_SIZE, WRITE_SIZE in
+    KiB, each scaled so the calibration copy reads and writes copy_mib MiB),
+    clock (GRBM_GUI_ACTIVE per XCD over the dispatch time), MFMA busy (busy
+    cycles over the cycles all 1024 SIMDs had), VALU and LDS instructions per
+    MFMA, LDS bank conflicts over LDS-active cycles, and the two scales."""
+    cp = C.get("copyBuffer", {})
+    fscale = copy_mib * 1024 / cp["FETCH_SIZE"] if cp.get("FETCH_SIZE") else None
+    wscale = copy_mib * 1024 / cp["WRITE_SIZE"] if cp.get("WRITE_SIZE") else None
+    out = {"_fetch_scale": fscale, "_write_scale": wscale}
+    nan = float("nan")
+    for k, d in C.items():
+        if k == "copyBuffer":
+            continue
+        m = {}
+        if fscale and "FETCH_SIZE" in d:
+            m["read_bytes"] = d["FETCH_SIZE"] * fscale * 1024
+        if wscale and "WRITE_SIZE" in d:
+            m["write_bytes"] = d["WRITE_SIZE"] * wscale * 1024
+        gui = d.get("GRBM_GUI_ACTIVE", 0) / XCDS
+        mf = d.get("SQ_INSTS_MFMA", 0)
+        m["clock_ghz"] = gui / d["_dur_ns"] if gui and d.get("_dur_ns") else nan
+        m["mfma_busy_pct"] = (100 * d["SQ_VALU_MFMA_BUSY_CYCLES"] / SIMDS / gui
+                              if gui and "SQ_VALU_MFMA_BUSY_CYCLES" in d else nan)
+        m["valu_per_mfma"] = (d["SQ_INSTS_VALU"] - mf) / mf if mf and "SQ_INSTS_VALU" in d else nan
+        m["lds_per_mfma"] = d["SQ_INSTS_LDS"] / mf if mf and "SQ_INSTS_LDS" in d else nan
+        m["lds_conflict_pct"] = (100 * d["SQ_LDS_BANK_CONFLICT"] / d["SQ_LDS_IDX_ACTIVE"]
+                                 if d.get("SQ_LDS_IDX_ACTIVE") else nan)
+        out[k] = m
+    return out
+
+
+def profile_report(out_dir: str, workload: str, tag=None, profiles_dir: str = PROFILES) -> dict:
+    """Reduce the passes under out_dir into profiles_dir/<tag>_kernel_trace.md,
+    profiles_dir/<tag>_counters.md and the workload's entry of
+    profiles_dir/hbm_traffic.json (bytes per launch of each kernel, with the
+    SHA-256 of its sources, so that bench.py reports them only while the
+    kernel is unchanged).  Returns the derived metrics."""
+    import csv
+    tag = tag or PROFILE_TAGS.get(workload, workload)
+    os.makedirs(profiles_dir, exist_ok=True)
+    cmds = {n: " ".join(a).replace(sys.executable, "python").replace(os.path.abspath(__file__), "bench.py")
+            for n, a in profile_commands(workload, 20)}
+    written = []
+    stats = _find_csv(os.path.join(out_dir, "trace"), "kernel_stats.csv")
+    if stats:
+        rows = list(csv.DictReader(open(stats)))
+        bj = _last_json(os.path.join(out_dir, "trace.out"))
+        t = [f"# Kernel trace: workload `{workload}`", "",
+             "Made by `python bench.py --profile <dir> --workload " + workload + "` (run from the repository "
+             "root; the passes run in /tmp with TMPDIR=/tmp), whose trace pass is:", "",
+             "    " + cmds["trace"].replace("{DIR}", "<dir>"), "",
+             "| kernel | calls | avg us | min us | max us | % of GPU time |", "|---|---|---|---|---|---|"]
+        for r in rows:
+            t.append("| %s | %s | %.1f | %.1f | %.1f | %.2f |" % (
+                short_kernel(r["Name"]), r["Calls"], float(r["AverageNs"]) / 1e3, float(r["MinNs"]) / 1e3,
+                float(r["MaxNs"]) / 1e3, float(r["Percentage"])))
+        if bj:
+            rf = bj.get("roofline", {})
+            avg = {short_kernel(r["Name"]): float(r["AverageNs"]) / 1e6 for r in rows}
+            t += ["", "bench.py's JSON line from the same run: value %s %s, %s ms per step." % (
+                bj.get("value"), bj.get("unit"), bj.get("ms_per_step"))]
+            if rf.get("kernel"):
+                t.append("Dominant kernel %s: %.4f ms average launch by HIP events, trace average %.4f ms; "
+                         "%s %s = %.1f %% of %s %s." % (
+                             rf["kernel"], rf.get("avg_launch_ms", float("nan")),
+                             avg.get(rf["kernel"], float("nan")), rf.get("achieved"), rf.get("unit"),
+                             100 * rf.get("frac", float("nan")), rf.get("peak"), rf.get("unit")))
+            if "fwd_ms" in bj:
+                t.append("Event medians: forward pass %s ms, backward pass %s ms (dK/dV kernel %s ms, dQ kernel "
+                         "%s ms)." % (bj["fwd_ms"], bj["bwd_ms"], bj.get("bwd_kv_ms"), bj.get("bwd_dq_ms")))
+        path = os.path.join(profiles_dir, f"{tag}_kernel_trace.md")
+        open(path, "w").write("\n".join(t) + "\n")
+        written.append(path)
+    C = {}
+    for name, _ in PMC_PASSES:
+        f = _find_csv(os.path.join(out_dir, name), "counter_collection.csv")
+        if f:
+            for k, d in read_counters(f).items():
+                dur = d.pop("_dur_ns")
+                C.setdefault(k, {}).update(d)
+                if name == "sq1" or "_dur_ns" not in C[k]:
+                    C[k]["_dur_ns"] = dur   # the clock uses the pass that read GRBM_GUI_ACTIVE
+    if not C:
+        return {}
+    M = derived_metrics(C)
+    ks = [k for k in PROFILE_KERNELS if k in C]
+    names = sorted({c for k in ks for c in C[k] if not c.startswith("_")})
+    o = [f"# Hardware counters: workload `{workload}`", "",
+         "Made by `python bench.py --profile <dir> --workload " + workload + "`: one rocprofv3 run per counter "
+         "group (each pass also runs a plain device copy of %d MiB, the calibration dispatch):" % CALIBRATE_MIB, ""]
+    o += ["    " + cmds[n].replace("{DIR}", "<dir>") for n, _ in PMC_PASSES]
+    o += ["", "Values per dispatch (mean over the run's dispatches of the kernel; for the copy, the "
+          "calibration dispatch).", "", "| counter | " + " | ".join(ks) + " |", "|---|" + "---|" * len(ks)]
+    for c in names:
+        o.append(f"| {c} | " + " | ".join("%.4g" % C[k].get(c, float("nan")) for k in ks) + " |")
+    fs, wsc = M["_fetch_scale"], M["_write_scale"]
+    if fs and wsc:
+        o += ["", "Byte calibration: the %d MiB copy reads FETCH_SIZE = %.0f KiB and WRITE_SIZE = %.0f KiB, so "
+              "HBM bytes = FETCH_SIZE x %.3f KiB and WRITE_SIZE x %.3f KiB." % (
+                  CALIBRATE_MIB, C["copyBuffer"]["FETCH_SIZE"], C["copyBuffer"]["WRITE_SIZE"], fs, wsc)]
+    o += ["", "| kernel | HBM read MiB | HBM write MiB | clock GHz | MFMA busy % | MFMA % of 2.4 GHz peak | "
+          "VALU instr / MFMA | LDS instr / MFMA | LDS bank conflicts % |", "|---|---|---|---|---|---|---|---|---|"]
+    for k in ks:
+        if k == "copyBuffer":
+            continue
+        m = M[k]
+        o.append("| %s | %.1f | %.1f | %.2f | %.1f | %.1f | %.2f | %.2f | %.1f |" % (
+            k, m.get("read_bytes", float("nan")) / 2**20, m.get("write_bytes", float("nan")) / 2**20,
+            m["clock_ghz"], m["mfma_busy_pct"], m["mfma_busy_pct"] * m["clock_ghz"] / 2.4, m["valu_per_mfma"],
+            m["lds_per_mfma"], m["lds_conflict_pct"]))
+    o += ["", "clock = GRBM_GUI_ACTIVE / %d XCDs / dispatch time; MFMA busy = SQ_VALU_MFMA_BUSY_CYCLES / (%d SIMDs "
+          "x GRBM_GUI_ACTIVE / %d XCDs).  The 2.5 PFLOP/s dense bf16 peak assumes 2.4 GHz, so the fraction of that "
+          "peak the matrix cores can reach at the measured clock is busy x clock / 2.4 GHz." % (XCDS, SIMDS, XCDS)]
+    path = os.path.join(profiles_dir, f"{tag}_counters.md")
+    open(path, "w").write("\n".join(o) + "\n")
+    written.append(path)
+    traffic = {k: {"fetch_bytes": int(M[k]["read_bytes"]), "write_bytes": int(M[k]["write_bytes"]),
+                   "sources_sha256": kernel_sources_sha256(k), "counters": os.path.basename(path)}
+               for k in ks if k in KERNEL_SOURCES and "read_bytes" in M[k] and "write_bytes" in M[k]}
+    if traffic:
+        tf = os.path.join(profiles_dir, "hbm_traffic.json")
+        try:
+            old = json.load(open(tf))
+            old.setdefault("workloads", {})
+        except (OSError, ValueError):
+            old = {"workloads": {}}
+        old.pop("kernels", None)
+        old["note"] = ("HBM bytes per launch by workload and kernel (FETCH_SIZE and WRITE_SIZE scaled by a plain "
+                       "%d MiB device copy), made by bench.py --profile; sources_sha256 covers the kernel's source "
+                       "file and the two shared headers when the counters were taken." % CALIBRATE_MIB)
+        old["workloads"][workload] = traffic
+        json.dump(old, open(tf, "w"), indent=1, sort_keys=True)
+        written.append(tf)
+    for p in written:
+        print(f"[profile] wrote {os.path.relpath(p, ROOT) if p.startswith(ROOT) else p}", flush=True)
+    return M
+
+
 def main():
     args = parse()
+    if args.profile or args.profile_report:
+        # the passes run as child processes: this one never touches the GPU
+        if args.profile:
+            run_profile(os.path.abspath(args.profile), args.workload, args.steps)
+        profile_report(os.path.abspath(args.profile or args.profile_report), args.workload)
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU: the library has no multi-GPU path (each (b, h) head is "
               "independent, so a multi-GPU run would shard the heads with no communication). Run with --gpus 1.",

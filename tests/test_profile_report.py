@@ -1,0 +1,71 @@
+"""bench.py's rocprofv3 harness on the CPU: the reduction of a small committed
+fixture of rocprofv3 CSV output (tests/golden/rocprof: a kernel-stats file,
+the bench line of the traced run, and one file per counter pass, with round
+numbers) into the profile summaries, and the shape of the passes it runs."""
+
+import json
+import os
+
+import pytest
+
+import bench
+
+FIX = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden", "rocprof")
+
+
+def test_counter_reduction_and_copy_calibration(tmp_path):
+    M = bench.profile_report(FIX, "long", tag="fixture", profiles_dir=str(tmp_path))
+    # the 256 MiB calibration copy reads FETCH_SIZE = 131072 KiB (half) and
+    # WRITE_SIZE = 262144 KiB: scales 2 and 1; the small upload copy is ignored
+    assert M["_fetch_scale"] == pytest.approx(2.0) and M["_write_scale"] == pytest.approx(1.0)
+    f = M["fwd_kernel"]
+    assert f["read_bytes"] == pytest.approx((200000 + 210000) / 2 * 2 * 1024)
+    assert f["write_bytes"] == pytest.approx(66560 * 1024)
+    # 14.4e6 GRBM cycles over 8 XCDs in 1 ms: 1.8 GHz; 921.6e6 busy cycles of
+    # 1024 SIMDs x 1.8e6: 50 %; 6e6 VALU incl. 1e6 MFMA: 5 VALU per MFMA
+    assert f["clock_ghz"] == pytest.approx(1.8) and f["mfma_busy_pct"] == pytest.approx(50.0)
+    assert f["valu_per_mfma"] == pytest.approx(5.0) and f["lds_per_mfma"] == pytest.approx(1.5)
+    assert f["lds_conflict_pct"] == pytest.approx(1.0)
+    k = M["bwd_kv_kernel"]
+    assert k["read_bytes"] == pytest.approx(710000 * 2 * 1024) and k["write_bytes"] == pytest.approx(131072 * 1024)
+    assert k["clock_ghz"] == pytest.approx(1.8) and k["mfma_busy_pct"] == pytest.approx(40.0)
+    assert k["valu_per_mfma"] == pytest.approx(4.0) and k["lds_conflict_pct"] == 0.0
+    # the summaries and the traffic entry for this workload
+    trace = (tmp_path / "fixture_kernel_trace.md").read_text()
+    assert "| bwd_kv_kernel | 20 | 2000.0 |" in trace and "trace average 2.0000 ms" in trace
+    counters = (tmp_path / "fixture_counters.md").read_text()
+    assert "| fwd_kernel | 400.4 | 65.0 | 1.80 | 50.0 | 37.5 | 5.00 | 1.50 | 1.0 |" in counters
+    assert "--pmc FETCH_SIZE" in counters and "--calibrate-copy 256" in counters
+    t = json.loads((tmp_path / "hbm_traffic.json").read_text())["workloads"]["long"]
+    assert t["fwd_kernel"]["fetch_bytes"] == 410000 * 1024 and t["fwd_kernel"]["write_bytes"] == 66560 * 1024
+    assert t["bwd_kv_kernel"]["sources_sha256"] == bench.kernel_sources_sha256("bwd_kv_kernel")
+
+
+def test_traffic_is_read_back_only_for_current_sources(tmp_path, monkeypatch):
+    bench.profile_report(FIX, "gpt2", tag="fixture", profiles_dir=str(tmp_path))
+    monkeypatch.setattr(bench, "TRAFFIC_FILE", str(tmp_path / "hbm_traffic.json"))
+    assert bench.measured_traffic("fwd_kernel", "gpt2") == 410000 * 1024 + 66560 * 1024
+    assert bench.measured_traffic("fwd_kernel", "long") is None          # another workload
+    d = json.loads((tmp_path / "hbm_traffic.json").read_text())
+    d["workloads"]["gpt2"]["fwd_kernel"]["sources_sha256"] = "0" * 64   # the kernel changed since
+    (tmp_path / "hbm_traffic.json").write_text(json.dumps(d))
+    assert bench.measured_traffic("fwd_kernel", "gpt2") is None
+
+
+def test_profile_passes_respect_counter_limits():
+    """One trace pass without counters, then counter passes of at most 8 SQ,
+    2 GRBM and 4 TCC counters (FETCH_SIZE takes 3, WRITE_SIZE 2), none
+    combined with a trace domain; the program follows '--' directly."""
+    cmds = bench.profile_commands("long", 20, python="python")
+    assert [n for n, _ in cmds] == ["trace", "fetch", "write", "sq1", "sq2"]
+    for name, argv in cmds:
+        i = argv.index("--")
+        assert argv[i + 1] == "python"
+        if name == "trace":
+            assert "--pmc" not in argv and "--kernel-trace" in argv
+            continue
+        counters = argv[argv.index("--pmc") + 1:argv.index("--kernel-include-regex")]
+        assert not {"--sys-trace", "-s", "--runtime-trace", "-r", "--kernel-trace"} & set(argv)
+        assert sum(c.startswith("SQ_") for c in counters) <= 8
+        assert sum(c.startswith("GRBM_") for c in counters) <= 2
+        assert 3 * counters.count("FETCH_SIZE") + 2 * counters.count("WRITE_SIZE") <= 4
