@@ -86,7 +86,8 @@ typedef enum {
     FA_ERR_ALIGN = -7,      /* a tensor base address is not 16-byte aligned         */
     FA_ERR_WORKSPACE = -8,  /* workspace NULL, too small or misaligned              */
     FA_ERR_HIP = -9,        /* a HIP launch failed (see fa_last_hip_error)          */
-    FA_ERR_OPTS = -10       /* opts->struct_size unknown or flags invalid           */
+    FA_ERR_OPTS = -10,      /* opts->struct_size unknown or flags invalid           */
+    FA_ERR_SCRATCH = -11    /* fa_bwd_noalloc: D needs more than FA_BWD_SCRATCH_BYTES */
 } fa_status;
 
 enum {
@@ -179,6 +180,26 @@ fa_status fa_bwd(const void* Q, const void* K, const void* V, const void* O,
                  float scale, int32_t causal, float dropout_p, uint64_t seed,
                  const uint8_t* block_mask, const fa_opts* opts,
                  void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* For callers that cannot allocate device memory (code under HIP graph
+ * capture, serving loops, harnesses that forbid allocation): fa_bwd with the
+ * same arguments and contract but no workspace argument.  The D vector
+ * (4 bytes per query row, B*H*N rows) lives in a static device array of
+ * FA_BWD_SCRATCH_BYTES that the library holds on each GPU it runs on until
+ * the process ends, so B*H*N may be at most FA_BWD_SCRATCH_BYTES / 4
+ * (4,194,304 rows), else FA_ERR_SCRATCH is returned before anything is
+ * enqueued.  The call allocates nothing: it looks the array's device address
+ * up once per device (FA_ERR_HIP if that fails) and launches fa_bwd's
+ * kernels.  Every call on one GPU shares that GPU's array: two calls whose
+ * work overlaps on one GPU (on different streams, or from different threads
+ * without ordering) race and may give wrong gradients; calls ordered on one
+ * stream are safe.  Each call writes all of D before reading it. */
+#define FA_BWD_SCRATCH_BYTES ((size_t)16 << 20)
+fa_status fa_bwd_noalloc(const void* Q, const void* K, const void* V, const void* O,
+                         const void* dO, const float* LSE, void* dQ, void* dK, void* dV,
+                         int32_t B, int32_t H, int32_t N, int32_t d, fa_dtype dtype,
+                         float scale, int32_t causal, float dropout_p, uint64_t seed,
+                         const uint8_t* block_mask, const fa_opts* opts, hipStream_t stream);
 
 /* Decode attention over a key/value cache (Self-Attention tutorial, section
  * 11.2: the decode phase, one new token -- or a few -- per step against the

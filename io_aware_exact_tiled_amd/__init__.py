@@ -146,11 +146,13 @@ def bwd_workspace_bytes(B, H, N, d) -> int:
 
 def bwd(q, k, v, o, do, lse, *, causal=False, dropout_p=0.0, seed=0, rng_offset=0, key_lens=None,
         block_mask=None, scale: Optional[float] = None, record_tiles=False, workspace=None, grads=None,
-        events=None):
+        events=None, no_alloc=False):
     """Backward pass.  Returns (dQ, dK, dV) in q's dtype (dK, dV with k's
     shape: summed over the query heads that share a K/V head), plus, when
     record_tiles is set, the (dK/dV kernel, dQ kernel) tile-visit maps.
-    O may be fp32 (if the forward wrote it so) or q's dtype."""
+    O may be fp32 (if the forward wrote it so) or q's dtype.  no_alloc: call
+    fa_bwd_noalloc (the library's static scratch instead of a workspace;
+    B*H*N up to FA_BWD_SCRATCH_BYTES / 4)."""
     hkv = _check_qkv(q, k, v, do)
     B, H, N, d = q.shape
     scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
@@ -164,16 +166,18 @@ def bwd(q, k, v, o, do, lse, *, causal=False, dropout_p=0.0, seed=0, rng_offset=
         dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
     else:
         dq, dk, dv = grads
-    need = bwd_workspace_bytes(B, H, N, d)
-    ws = workspace if workspace is not None else torch.empty(need, dtype=torch.uint8, device=q.device)
     opts, keep, tiles = _opts(B, H, N, d, 1, key_lens, rng_offset, o_fp32, record_tiles, False, q.device, dt,
                               events, hkv, causal)
     bm, bmp = _mask_ptr(block_mask, q.device, N)
-    code = _lib.lib().fa_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), do.data_ptr(),
-                             lse.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), B, H, N, d, dt,
-                             scale, 1 if causal else 0, float(dropout_p), int(seed), bmp, ctypes.byref(opts),
-                             ws.data_ptr(), ws.numel(), _stream(q.device))
-    check(code, "fa_bwd")
+    ptrs = (q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), do.data_ptr(), lse.data_ptr(), dq.data_ptr(),
+            dk.data_ptr(), dv.data_ptr(), B, H, N, d, dt, scale, 1 if causal else 0, float(dropout_p), int(seed),
+            bmp, ctypes.byref(opts))
+    if no_alloc:
+        check(_lib.lib().fa_bwd_noalloc(*ptrs, _stream(q.device)), "fa_bwd_noalloc")
+    else:
+        need = bwd_workspace_bytes(B, H, N, d)
+        ws = workspace if workspace is not None else torch.empty(need, dtype=torch.uint8, device=q.device)
+        check(_lib.lib().fa_bwd(*ptrs, ws.data_ptr(), ws.numel(), _stream(q.device)), "fa_bwd")
     del keep, bm
     return (dq, dk, dv, tiles) if record_tiles else (dq, dk, dv)
 

@@ -15,15 +15,16 @@ LIB_PATH = os.path.join(HERE, "libfa.so")
 FA_F32, FA_F16, FA_BF16 = 0, 1, 2
 FA_FLAG_RECORD_TILES = 1 << 0
 FA_FLAG_REVERSE_KV = 1 << 1
+FA_BWD_SCRATCH_BYTES = 16 << 20   # the static scratch of fa_bwd_noalloc
 
 STATUS = {
     0: "FA_OK", -1: "FA_ERR_NULL", -2: "FA_ERR_SHAPE", -3: "FA_ERR_HEAD_DIM", -4: "FA_ERR_DTYPE",
     -5: "FA_ERR_DROPOUT", -6: "FA_ERR_SCALE", -7: "FA_ERR_ALIGN", -8: "FA_ERR_WORKSPACE",
-    -9: "FA_ERR_HIP", -10: "FA_ERR_OPTS",
+    -9: "FA_ERR_HIP", -10: "FA_ERR_OPTS", -11: "FA_ERR_SCRATCH",
 }
 
 # every symbol include/fa.h declares
-EXPORTS = ("fa_fwd", "fa_fwd_workspace_bytes", "fa_bwd", "fa_bwd_workspace_bytes", "fa_decode",
+EXPORTS = ("fa_fwd", "fa_fwd_workspace_bytes", "fa_bwd", "fa_bwd_workspace_bytes", "fa_bwd_noalloc", "fa_decode",
            "fa_decode_workspace_bytes", "fa_fwd_kv_outer", "fa_fwd_kv_outer_workspace_bytes",
            "fa_dropout_keep_mask", "fa_tile_shape",
            "fa_status_string", "fa_last_hip_error", "fa_abi_version")
@@ -71,6 +72,9 @@ def lib():
         L.fa_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, f32, i32, f32, u64,
                              vp, ctypes.POINTER(FaOpts), vp, sz, vp]
         L.fa_bwd.restype = i32
+        L.fa_bwd_noalloc.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, f32, i32, f32,
+                                     u64, vp, ctypes.POINTER(FaOpts), vp]
+        L.fa_bwd_noalloc.restype = i32
         L.fa_bwd_workspace_bytes.argtypes = [i32, i32, i32, i32]
         L.fa_bwd_workspace_bytes.restype = sz
         L.fa_decode.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32, f32, i32, vp, vp, vp, sz, vp]

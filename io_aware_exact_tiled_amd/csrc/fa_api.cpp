@@ -91,6 +91,46 @@ constexpr float LOG2E = 1.4426950408889634f;
 
 }  // namespace
 
+namespace fa {
+
+fa_status set_hip_error(hipError_t e) { return hip_fail(e); }
+
+// Everything fa_bwd checks except the workspace, and the argument block it
+// launches with (delta left for the caller to point at D's storage).
+fa_status bwd_prepare(const void* Q, const void* K, const void* V, const void* O, const void* dO,
+                      const float* LSE, void* dQ, void* dK, void* dV, int32_t B, int32_t H, int32_t N, int32_t d,
+                      fa_dtype dtype, float scale, int32_t causal, float dropout_p, uint64_t seed,
+                      const uint8_t* block_mask, const fa_opts* opts, BwdArgs* out) {
+    if (!Q || !K || !V || !O || !dO || !LSE || !dQ || !dK || !dV) return FA_ERR_NULL;
+    fa_status st = check_common(B, H, N, d, dtype, scale, dropout_p, opts);
+    if (st != FA_OK) return st;
+    if (opts && (opts->flags & FA_FLAG_REVERSE_KV)) return FA_ERR_OPTS;
+    if (!aligned16(Q) || !aligned16(K) || !aligned16(V) || !aligned16(O) || !aligned16(dO) ||
+        !aligned16(LSE) || !aligned16(dQ) || !aligned16(dK) || !aligned16(dV))
+        return FA_ERR_ALIGN;
+    const int32_t hkv = kv_heads(H, opts);
+    if (!hkv) return FA_ERR_OPTS;
+    BwdArgs& a = *out;
+    a.q = Q; a.k = K; a.v = V; a.o = O; a.dout = dO; a.lse = LSE;
+    a.dq = dQ; a.dk = dK; a.dv = dV;
+    a.delta = nullptr;
+    a.B = B; a.H = H; a.N = N; a.Hkv = hkv;
+    a.scale = scale;
+    a.scale_log2 = scale * LOG2E;
+    a.o_f32 = (opts && opts->o_fp32) ? 1 : 0;
+    a.mask = mask_args(N, causal, block_mask, opts);
+    a.drop = drop_args(dropout_p, seed, opts);
+    const bool rec = opts && (opts->flags & FA_FLAG_RECORD_TILES);
+    a.tile_visits = rec ? opts->tile_visits : nullptr;
+    a.tile_visits2 = rec ? opts->tile_visits2 : nullptr;
+    a.ev_begin = (opts && opts->main_end) ? opts->main_begin : nullptr;
+    a.ev_end = (opts && opts->main_begin) ? opts->main_end : nullptr;
+    a.ev_mid = (a.ev_begin && a.ev_end) ? opts->main_mid : nullptr;
+    return FA_OK;
+}
+
+}  // namespace fa
+
 extern "C" {
 
 int32_t fa_abi_version(void) { return FA_ABI_VERSION; }
@@ -108,6 +148,7 @@ const char* fa_status_string(fa_status s) {
         case FA_ERR_WORKSPACE: return "workspace is NULL, too small or not 256-byte aligned";
         case FA_ERR_HIP: return "HIP launch failed";
         case FA_ERR_OPTS: return "invalid fa_opts (struct_size or flags)";
+        case FA_ERR_SCRATCH: return "problem too large for the static scratch of fa_bwd_noalloc";
     }
     return "unknown status";
 }
@@ -260,34 +301,14 @@ fa_status fa_bwd(const void* Q, const void* K, const void* V, const void* O, con
                  void* dQ, void* dK, void* dV, int32_t B, int32_t H, int32_t N, int32_t d, fa_dtype dtype,
                  float scale, int32_t causal, float dropout_p, uint64_t seed, const uint8_t* block_mask,
                  const fa_opts* opts, void* workspace, size_t workspace_bytes, hipStream_t stream) {
-    if (!Q || !K || !V || !O || !dO || !LSE || !dQ || !dK || !dV) return FA_ERR_NULL;
-    fa_status st = check_common(B, H, N, d, dtype, scale, dropout_p, opts);
+    fa::BwdArgs a;
+    fa_status st = fa::bwd_prepare(Q, K, V, O, dO, LSE, dQ, dK, dV, B, H, N, d, dtype, scale, causal, dropout_p,
+                                   seed, block_mask, opts, &a);
     if (st != FA_OK) return st;
-    if (opts && (opts->flags & FA_FLAG_REVERSE_KV)) return FA_ERR_OPTS;
-    if (!aligned16(Q) || !aligned16(K) || !aligned16(V) || !aligned16(O) || !aligned16(dO) ||
-        !aligned16(LSE) || !aligned16(dQ) || !aligned16(dK) || !aligned16(dV))
-        return FA_ERR_ALIGN;
     const size_t need = fa_bwd_workspace_bytes(B, H, N, d);
     if (!workspace || workspace_bytes < need || (reinterpret_cast<uintptr_t>(workspace) & 255u))
         return FA_ERR_WORKSPACE;
-    const int32_t hkv = kv_heads(H, opts);
-    if (!hkv) return FA_ERR_OPTS;
-    fa::BwdArgs a;
-    a.q = Q; a.k = K; a.v = V; a.o = O; a.dout = dO; a.lse = LSE;
-    a.dq = dQ; a.dk = dK; a.dv = dV;
     a.delta = static_cast<float*>(workspace);
-    a.B = B; a.H = H; a.N = N; a.Hkv = hkv;
-    a.scale = scale;
-    a.scale_log2 = scale * LOG2E;
-    a.o_f32 = (opts && opts->o_fp32) ? 1 : 0;
-    a.mask = mask_args(N, causal, block_mask, opts);
-    a.drop = drop_args(dropout_p, seed, opts);
-    const bool rec = opts && (opts->flags & FA_FLAG_RECORD_TILES);
-    a.tile_visits = rec ? opts->tile_visits : nullptr;
-    a.tile_visits2 = rec ? opts->tile_visits2 : nullptr;
-    a.ev_begin = (opts && opts->main_end) ? opts->main_begin : nullptr;
-    a.ev_end = (opts && opts->main_begin) ? opts->main_end : nullptr;
-    a.ev_mid = (a.ev_begin && a.ev_end) ? opts->main_mid : nullptr;
     const hipError_t e = fa::launch_bwd(a, dtype, d, stream);
     return e == hipSuccess ? FA_OK : hip_fail(e);
 }

@@ -193,6 +193,15 @@ inline size_t decode_workspace_bytes(int B, int H, int Hkv, int Nq, int Nk, int 
 // events: null or three events (before the chunk kernel, between, after the merge)
 hipError_t launch_decode(const DecodeArgs& a, fa_dtype dt, int d, const hipEvent_t* ev, hipStream_t s);
 
+// Validation and argument block shared by fa_bwd and fa_bwd_noalloc (every
+// check but the workspace's; a->delta is left null), and the thread-local
+// error text behind FA_ERR_HIP (fa_api.cpp).
+fa_status bwd_prepare(const void* Q, const void* K, const void* V, const void* O, const void* dO,
+                      const float* LSE, void* dQ, void* dK, void* dV, int32_t B, int32_t H, int32_t N, int32_t d,
+                      fa_dtype dtype, float scale, int32_t causal, float dropout_p, uint64_t seed,
+                      const uint8_t* block_mask, const fa_opts* opts, BwdArgs* a);
+fa_status set_hip_error(hipError_t e);
+
 hipError_t launch_fwd(FwdArgs a, fa_dtype dt, int d, void* workspace, hipStream_t s);
 hipError_t launch_bwd(const BwdArgs& a, fa_dtype dt, int d, hipStream_t s);
 hipError_t launch_keep_mask(uint32_t k0, uint32_t k1, uint32_t off, uint32_t thr,

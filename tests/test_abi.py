@@ -276,3 +276,18 @@ def test_header_compiles_as_c_and_links(tmp_path):
     run = subprocess.run([exe], capture_output=True, text=True, timeout=60)
     assert run.returncode == 0, run.stdout + run.stderr
     assert "c abi ok" in run.stdout
+
+
+def test_bwd_noalloc_validation_on_the_host():
+    """fa_bwd_noalloc validates like fa_bwd and rejects a problem whose D
+    (4 bytes per query row) exceeds its static scratch with FA_ERR_SCRATCH,
+    all before any device call."""
+    L = _lib()
+    rows = lib_mod.FA_BWD_SCRATCH_BYTES // 4
+    args = [P] * 9
+    assert L.fa_bwd_noalloc(*args, 1, 1, rows + 1, 64, 2, 0.125, 0, 0.0, 0, None, None, None) == -11
+    assert L.fa_bwd_noalloc(*args, 2, 4, rows // 8 + 1, 128, 1, 0.125, 1, 0.0, 0, None, None, None) == -11
+    assert L.fa_bwd_noalloc(None, *args[1:], 1, 1, 64, 64, 2, 0.125, 0, 0.0, 0, None, None, None) == -1
+    assert L.fa_bwd_noalloc(*args, 1, 1, 64, 96, 2, 0.125, 0, 0.0, 0, None, None, None) == -3
+    assert L.fa_bwd_noalloc(*args, 1, 1, 64, 64, 2, 0.125, 0, 1.5, 0, None, None, None) == -5
+    assert b"static scratch" in L.fa_status_string(-11)
