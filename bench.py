@@ -863,7 +863,9 @@ def profile_report(out_dir: str, workload: str, tag=None, profiles_dir: str = PR
             m["lds_per_mfma"], m["lds_conflict_pct"]))
     o += ["", "clock = GRBM_GUI_ACTIVE / %d XCDs / dispatch time; MFMA busy = SQ_VALU_MFMA_BUSY_CYCLES / (%d SIMDs "
           "x GRBM_GUI_ACTIVE / %d XCDs).  The 2.5 PFLOP/s dense bf16 peak assumes 2.4 GHz, so the fraction of that "
-          "peak the matrix cores can reach at the measured clock is busy x clock / 2.4 GHz." % (XCDS, SIMDS, XCDS)]
+          "peak the matrix cores can reach at the measured clock is busy x clock / 2.4 GHz.  The clock is only "
+          "meaningful for dispatches much longer than the profiler's per-dispatch overhead (tens of microseconds): "
+          "for short ones GRBM_GUI_ACTIVE also counts cycles outside the dispatch." % (XCDS, SIMDS, XCDS)]
     path = os.path.join(profiles_dir, f"{tag}_counters.md")
     open(path, "w").write("\n".join(o) + "\n")
     written.append(path)

@@ -235,9 +235,10 @@ def attn_bwd_rows_cols(q, k, v, do, scale, rows, cols, lse_all, D_all,
 
 
 def attn_stats(q, k, v, do, scale, causal=False, key_lens=None, block_mask=None,
-               dropout_p=0.0, seed=0, rng_offset=0, heads=None, chunk=512):
-    """LSE [B,H,N] and D [B,H,N] over all rows (D_i = sum_j P_ij dP_ij).
-    `heads` restricts the work to a list of (b, h) pairs (others left 0)."""
+               dropout_p=0.0, seed=0, rng_offset=0, heads=None, chunk=512, rows=None):
+    """LSE [B,H,N] and D [B,H,N] (D_i = sum_j P_ij dP_ij) over all rows, or
+    over the query rows in `rows` (the others left 0).  `heads` restricts the
+    work to a list of (b, h) pairs (others left 0)."""
     q, k, v, do = as_f64(q), as_f64(k), as_f64(v), as_f64(do)
     B, H, N, d = q.shape
     sc = scale_f32(scale)
@@ -245,11 +246,12 @@ def attn_stats(q, k, v, do, scale, causal=False, key_lens=None, block_mask=None,
     LSE = np.zeros((B, H, N))
     Dall = np.zeros((B, H, N))
     Hkv = k.shape[1]
+    rows = np.arange(N) if rows is None else np.asarray(rows)
     for b, h in _pairs(B, H, heads):
         kl = _key_len(key_lens, b)
         g = kv_head(h, H, Hkv)
-        for s in range(0, N, chunk):
-            r = np.arange(s, min(s + chunk, N))
+        for s in range(0, len(rows), chunk):
+            r = rows[s:s + chunk]
             S = _rows_scores(q[b, h], k[b, g], r, sc)
             A = validity(r, N, causal, kl, block_mask)
             P, lse, _, _ = safe_softmax(S, A)

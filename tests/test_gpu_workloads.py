@@ -95,12 +95,14 @@ def test_decode_workload_full_oracle():
     print(f"[ok] decode {res}", flush=True)
 
 
+@pytest.mark.timeout(600)
 def test_long_sequence_beyond_64k():
     """N past 2^16 (N^2 past 2^32), ragged, causal, dropout, one K/V head for
-    two query heads: O, LSE and dQ on sampled rows against the oracle, and
-    for dK the identity sum_j dK_j = scale sum_i (sum_j dS_ij) Q_i = 0 (each
-    row's dS sums to D_i - D_i sum_j P_ij = 0, dropout included), which a
-    skipped tile or a wrong sign anywhere in the backward breaks."""
+    two query heads: O, LSE and dQ on sampled rows against the oracle; dK and
+    dV element by element on the last 256 keys; and for all of dK the
+    identity sum_j dK_j = scale sum_i (sum_j dS_ij) Q_i = 0 (each row's dS
+    sums to D_i - D_i sum_j P_ij = 0, dropout included), which a skipped
+    tile or a wrong sign anywhere in the backward breaks."""
     N = 65536 + 77
     print(f"[case] N={N} causal dropout MQA", flush=True)
     x = W.random_case(1, 2, N, 128, dtype="bf16", seed=65613, causal=True, dropout_p=0.1,
@@ -121,4 +123,13 @@ def test_long_sequence_beyond_64k():
     res["sum_dk"] = float((col_sum / col_mass).max())
     assert res["sum_dk"] <= 2e-3, f"sum_j dK_j / sum_j |dK_j| = {res['sum_dk']:.3e}"
     assert np.isfinite(f64(dv)).all()
+    # dK, dV element by element on the last 256 keys (past 2^16): under the
+    # causal mask only the last 256 rows see them, so the oracle's LSE and D
+    # of those rows suffice
+    tail = np.arange(N - 256, N)
+    Ls, Ds = oracle.attn_stats(x["q"], x["k"], x["v"], x["do"], x["scale"], rows=tail, **okw)
+    _, rk, rv = oracle.attn_bwd_rows_cols(x["q"], x["k"], x["v"], x["do"], x["scale"], rows[:1], tail, Ls, Ds,
+                                          **okw)
+    res["dk_tail"] = check_grad(dk[:, :, tail], rk, dtype, "dK(last 256 keys)")
+    res["dv_tail"] = check_grad(dv[:, :, tail], rv, dtype, "dV(last 256 keys)")
     print(f"[ok] N={N} {res}", flush=True)

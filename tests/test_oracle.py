@@ -399,6 +399,15 @@ def test_sampled_rows_and_columns_match_full_pass():
     assert np.allclose(Or, O[:, :, rows], atol=1e-13) and np.allclose(Lr, L[:, :, rows], atol=1e-13)
     Ls, Ds = oracle.attn_stats(q, k, v, do, 0.3, **kw)
     assert np.allclose(Ls, L, atol=1e-13) and np.allclose(Ds, D, atol=1e-12)
+    sub = np.array([3, 150, 298, 299])
+    Lr2, Dr2 = oracle.attn_stats(q, k, v, do, 0.3, rows=sub, **kw)
+    assert np.allclose(Lr2[:, :, sub], L[:, :, sub], atol=1e-13) and np.allclose(Dr2[:, :, sub], D[:, :, sub], atol=1e-12)
+    assert not Lr2[:, :, 4].any() and not Dr2[:, :, 4].any()
+    # causal: the last keys are seen only by the last rows, so those rows' stats suffice for them
+    tail = np.arange(250, 300)
+    Lt, Dt = oracle.attn_stats(q, k, v, do, 0.3, rows=tail, **kw)
+    _, tk, tv = oracle.attn_bwd_rows_cols(q, k, v, do, 0.3, rows[:1], tail, Lt, Dt, **kw)
+    assert np.allclose(tk, dk[:, :, tail], atol=1e-12) and np.allclose(tv, dv[:, :, tail], atol=1e-12)
     sq, sk, sv = oracle.attn_bwd_rows_cols(q, k, v, do, 0.3, rows, cols, Ls, Ds, **kw)
     assert np.allclose(sq, dq[:, :, rows], atol=1e-12)
     assert np.allclose(sk, dk[:, :, cols], atol=1e-12)
