@@ -7,8 +7,8 @@
 // gradients follow from the definition with the softmax Jacobian:
 //     D_i = sum_k dO_ik O_ik                          pre-pass
 //     P   = exp(S - LSE_i)                            recomputed per tile
-//     dV_j = sum_i (P o Z / (1-p))_ij dO_i
-//     dP   = (dO V^T) o Z / (1-p),   dS = P o (dP - D)
+//     dV_j = sum_i (P o Z s)_ij dO_i       (Z keep bits, s = 1 / P(keep))
+//     dP   = (dO V^T) o Z s,   dS = P o (dP - D)
 //     dK_j = scale sum_i dS_ij Q_i,  dQ_i = scale sum_j dS_ij K_j
 //
 // Kernels, in launch order on the caller's stream:
@@ -103,9 +103,9 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(BwdArgs a) {
 // dK, dV: key-stationary, with specialised waves.  NW waves per workgroup,
 // two per block of 32 keys (waves w and w + NW/2 share a SIMD):
 //   A (w < NW/2):  holds K_j; S = Q K^T, P = exp(S - LSE) with the masks,
-//                  hands P to its partner through LDS, dV_j += (P o Z/(1-p))^T dO.
+//                  hands P to its partner through LDS, dV_j += (P o Z s)^T dO.
 //   B (w >= NW/2): holds V_j; dP = dO V^T, then with P from its partner
-//                  dS = P o (dP o Z/(1-p) - D), dK_j += dS^T Q.
+//                  dS = P o (dP o Z s - D), dK_j += dS^T Q.
 // NW = 8 (128 keys per workgroup, one workgroup per CU) for long sequences;
 // NW = 4 with 32-row query steps (64 keys, 48 KB of LDS: two workgroups per
 // CU) for short ones, where a lone workgroup per CU leaves its prologue and
@@ -131,7 +131,7 @@ __global__ __launch_bounds__(NW * 64, NW == 8 ? 1 : 2) void bwd_kv_kernel(BwdArg
     constexpr int DB = D / 32;
     constexpr int QU = 16 / E;                    // MFMA steps over 16 queries of a lane half
     constexpr int TQ = BR * D;                    // elements per staged tensor
-    constexpr int NX = DROP ? 2 : 1;              // hand-off planes: P (and P o Z / (1-p))
+    constexpr int NX = DROP ? 2 : 1;              // hand-off planes: P (and P o Z s)
     // The eight-wave configuration with 16-bit inputs hands P over already
     // packed as the dV operand (QU 16-byte fragments per 32-row block): half
     // the hand-off bytes in the LDS-bound long-sequence case.  The four-wave
@@ -368,7 +368,7 @@ __global__ __launch_bounds__(NW * 64, NW == 8 ? 1 : 2) void bwd_kv_kernel(BwdArg
                 const int qr0 = qb * 32 + hl * 16;
                 float ds[16];
                 if constexpr (PACKED) {
-                    // P (and Pd = P o Z/(1-p)) of the 16 queries from the packed fragments
+                    // P (and Pd = P o Z s) of the 16 queries from the packed fragments
                     float pv[16], pdv[16];
 #pragma unroll
                     for (int u = 0; u < QU; ++u) {
@@ -397,7 +397,7 @@ __global__ __launch_bounds__(NW * 64, NW == 8 ? 1 : 2) void bwd_kv_kernel(BwdArg
                         const f32x4 p4 = *xslot(0, qb, g);
                         const f32x4 d4 = *reinterpret_cast<const f32x4*>(dl + qr0 + 4 * g);
                         if constexpr (DROP) {
-                            // dS = P dP_hat Z/(1-p) - P D = Pd dP_hat - P D
+                            // dS = P dP_hat Z s - P D = Pd dP_hat - P D
                             const f32x4 pd4 = *xslot(1, qb, g);
 #pragma unroll
                             for (int e = 0; e < 4; ++e) ds[4 * g + e] = pd4[e] * sp[qb][4 * g + e] - p4[e] * d4[e];
