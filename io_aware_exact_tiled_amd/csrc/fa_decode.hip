@@ -191,7 +191,11 @@ __global__ __launch_bounds__(256, 2) void decode_split_kernel(DecodeArgs a) {
 
     // ---- merge the four waves' partials in LDS
     __syncthreads();                                   // every wave is done with its V tiles
-    float* sO = reinterpret_cast<float*>(sV);          // [wave][32 rows][D]
+    // [wave][32 rows][D] floats; row r's columns are rotated by 4 (r % 32)
+    // floats so that the 32 rows a store or a load touches at once fall in
+    // different banks (unrotated, rows D floats apart share one bank)
+    float* sO = reinterpret_cast<float*>(sV);
+    auto so_at = [&](int row, int col) { return sO + row * D + ((col + 4 * (row & 31)) & (D - 1)); };
     const float l_tot = pair_sum(l_run);
     if (hl == 0) {
         sM[wave * 32 + ln] = m_run;
@@ -200,8 +204,10 @@ __global__ __launch_bounds__(256, 2) void decode_split_kernel(DecodeArgs a) {
 #pragma unroll
     for (int db = 0; db < DB; ++db)
 #pragma unroll
-        for (int q = 0; q < 16; ++q)
-            sO[(wave * 32 + ln) * D + db * 32 + 8 * (q / 4) + 4 * hl + (q % 4)] = oacc[db][q];
+        for (int g4 = 0; g4 < 4; ++g4) {
+            const f32x4 v4 = {oacc[db][4 * g4], oacc[db][4 * g4 + 1], oacc[db][4 * g4 + 2], oacc[db][4 * g4 + 3]};
+            *reinterpret_cast<f32x4*>(so_at(wave * 32 + ln, db * 32 + 8 * g4 + 4 * hl)) = v4;
+        }
     __syncthreads();
     {
         constexpr int TPR = 8;                         // threads per row
@@ -224,14 +230,15 @@ __global__ __launch_bounds__(256, 2) void decode_split_kernel(DecodeArgs a) {
             float* op = a.opart + (row * a.S + s) * D + col0;
 #pragma unroll
             for (int j = 0; j < CPT; j += 4) {
-                f32x4 v4;
+                f32x4 v4 = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    float acc = 0.0f;
+                for (int w = 0; w < 4; ++w) {
+                    const f32x4 x = *reinterpret_cast<const f32x4*>(so_at(w * 32 + n, col0 + j));
 #pragma unroll
-                    for (int w = 0; w < 4; ++w) acc += cw[w] * sO[(w * 32 + n) * D + col0 + j + e];
-                    v4[e] = acc * inv;
+                    for (int e = 0; e < 4; ++e) v4[e] += cw[w] * x[e];
                 }
+#pragma unroll
+                for (int e = 0; e < 4; ++e) v4[e] *= inv;
                 *reinterpret_cast<f32x4*>(op + j) = v4;
             }
             if (col0 == 0) a.lpart[row * a.S + s] = lsum > 0.0f ? M + log2f(lsum) : -INFINITY;
