@@ -138,6 +138,8 @@ DECODE_CASES = [
     (2, 4, 1, 2, 4097, 64, "bf16", False, (4097, 2048)),
     (1, 2, 1, 1, 16384, 64, "bf16", True, (16000,)),      # 128 chunks: two batches in the merge
     (1, 4, 1, 3, 2600, 128, "fp16", True, (2599,)),       # 21 chunks
+    (4, 8, 2, 2, 900, 128, "fp16", True, (500, 500, 200, 500)),   # equal lengths
+    (70, 4, 2, 1, 300, 64, "bf16", True, tuple((i * 37) % 300 + 1 for i in range(70))),  # many short sequences
 ]
 
 
