@@ -96,6 +96,9 @@ def parse():
                          "writing raw output to DIR, then write the summaries under profiles/")
     ap.add_argument("--profile-report", metavar="DIR",
                     help="only reduce an existing --profile DIR into the summaries under profiles/")
+    ap.add_argument("--profile-mode", default="workload", choices=("workload", "io-ablation", "compare-standard"),
+                    help="what --profile runs: the workload (trace + counters), --io-ablation (trace + byte "
+                         "counters) or --compare-standard (trace)")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="first run one plain device-to-device copy of MIB MiB (a known-size kernel "
                          "that hardware byte counters can be scaled by)")
@@ -670,12 +673,29 @@ def short_kernel(name: str) -> str:
     return name[:40]
 
 
-def profile_commands(workload: str, steps: int, rocprof: str = "rocprofv3", python: str = sys.executable):
-    """(pass name, argv, output dir relative to DIR) of the trace pass and the
-    counter passes, each running this script on the workload."""
+PROFILE_MODES = ("workload", "io-ablation", "compare-standard")
+
+
+def profile_commands(workload: str, steps: int, rocprof: str = "rocprofv3", python: str = sys.executable,
+                     mode: str = "workload"):
+    """(pass name, argv) of the trace pass and the counter passes, each
+    running this script: on the workload (mode "workload"); with
+    --io-ablation (the key/value-outer forward against the query-outer one:
+    a trace and the two byte passes); or with --compare-standard (a trace of
+    this library against the separate-op baseline)."""
     me = os.path.abspath(__file__)
-    cmds = [("trace", [rocprof, "--kernel-trace", "--stats", "-f", "csv", "-d", "{DIR}/trace", "-o", "run", "--",
-                       python, me, "--workload", workload, "--steps", str(steps), "--no-cpu-baseline"])]
+    trace = [rocprof, "--kernel-trace", "--stats", "-f", "csv", "-d", "{DIR}/trace", "-o", "run", "--", python, me]
+    if mode == "io-ablation":
+        cmds = [("trace", trace + ["--steps", "8", "--warmup", "2", "--no-cpu-baseline", "--io-ablation"])]
+        for name, counters in PMC_PASSES[:2]:
+            cmds.append((name, [rocprof, "--pmc", *counters, "--kernel-include-regex",
+                                "fwd_kvo_kernel|fwd_kernel|copyBuffer", "-f", "csv", "-d", "{DIR}/" + name, "-o",
+                                "run", "--", python, me, "--steps", "4", "--warmup", "1", "--no-cpu-baseline",
+                                "--io-ablation", "--calibrate-copy", str(CALIBRATE_MIB)]))
+        return cmds
+    if mode == "compare-standard":
+        return [("trace", trace + ["--steps", "6", "--warmup", "2", "--no-cpu-baseline", "--compare-standard"])]
+    cmds = [("trace", trace + ["--workload", workload, "--steps", str(steps), "--no-cpu-baseline"])]
     regex = "|".join(PROFILE_KERNELS)
     for name, counters in PMC_PASSES:
         cmds.append((name, [rocprof, "--pmc", *counters, "--kernel-include-regex", regex, "-f", "csv", "-d",
@@ -684,7 +704,7 @@ def profile_commands(workload: str, steps: int, rocprof: str = "rocprofv3", pyth
     return cmds
 
 
-def run_profile(out_dir: str, workload: str, steps: int, timeout_s: int = 240) -> None:
+def run_profile(out_dir: str, workload: str, steps: int, timeout_s: int = 240, mode: str = "workload") -> None:
     """Run the passes one after another as child processes (each in its own
     process group, killed whole if it outlives timeout_s); stop at the first
     failure."""
@@ -692,7 +712,7 @@ def run_profile(out_dir: str, workload: str, steps: int, timeout_s: int = 240) -
     import subprocess
     os.makedirs(out_dir, exist_ok=True)
     env = dict(os.environ, TMPDIR=os.environ.get("TMPDIR", "/tmp"))
-    for name, argv in profile_commands(workload, steps):
+    for name, argv in profile_commands(workload, steps, mode=mode):
         argv = [a.replace("{DIR}", out_dir) for a in argv]
         print(f"[profile] {name}: {' '.join(argv)}", flush=True)
         with open(os.path.join(out_dir, name + ".out"), "w") as fo, \
@@ -780,6 +800,109 @@ def derived_metrics(C: dict, copy_mib: float = CALIBRATE_MIB) -> dict:
                                  if d.get("SQ_LDS_IDX_ACTIVE") else nan)
         out[k] = m
     return out
+
+
+def _dispatch_counters(path: str, kernel: str, counter: str) -> list:
+    """The values of one counter for one kernel's dispatches, in dispatch order."""
+    import csv
+    rows = [r for r in csv.DictReader(open(path))
+            if short_kernel(r["Kernel_Name"]) == kernel and r["Counter_Name"] == counter]
+    rows.sort(key=lambda r: int(r["Dispatch_Id"]))
+    return [float(r["Counter_Value"]) for r in rows]
+
+
+def io_ablation_report(out_dir: str, profiles_dir: str = PROFILES) -> str:
+    """profiles_dir/kv_outer_io_ablation.md from an io-ablation profile: per
+    configuration the times and byte models bench.py printed in the trace
+    pass, and the HBM bytes the counter passes measured for fwd_kvo_kernel
+    (copy-calibrated, the mean over the configuration's dispatches; the
+    configurations run in the order bench.py prints them)."""
+    import collections
+    lines = []
+    with open(os.path.join(out_dir, "trace.out")) as fh:
+        for l in fh:
+            if l.startswith("{") and '"io_ablation"' in l:
+                lines.append(json.loads(l))
+    f_csv = _find_csv(os.path.join(out_dir, "fetch"), "counter_collection.csv")
+    w_csv = _find_csv(os.path.join(out_dir, "write"), "counter_collection.csv")
+    C = {}
+    for f in (f_csv, w_csv):
+        for k, d in read_counters(f).items():
+            C.setdefault(k, {}).update({c: v for c, v in d.items() if c != "_dur_ns"})
+    M = derived_metrics(C)
+    fs, wsc = M["_fetch_scale"], M["_write_scale"]
+    fetch = _dispatch_counters(f_csv, "fwd_kvo_kernel", "FETCH_SIZE")
+    write = _dispatch_counters(w_csv, "fwd_kvo_kernel", "WRITE_SIZE")
+    n = len(lines)
+    per = len(fetch) // n if n else 0
+    assert n and per and len(fetch) == per * n and len(write) == per * n, (n, len(fetch), len(write))
+    cmds = {k: " ".join(a).replace(sys.executable, "python").replace(os.path.abspath(__file__), "bench.py")
+            .replace("{DIR}", "<dir>") for k, a in profile_commands("long", 8, mode="io-ablation")}
+    t = ["# IO ablation: key/value-outer forward against the query-outer one", "",
+         "Causal, bf16, B=1, H=16, d=128.  The key/value-outer kernel (fwd_kvo_kernel) keeps K_j, V_j in LDS and "
+         "moves the running O (fp32), m, l of every query block through device memory at every key tile, as the "
+         "explainer's step-by-step algorithm does; the query-outer fwd_kernel keeps them in registers.", "",
+         "Made by `python bench.py --profile <dir> --profile-mode io-ablation`, whose passes are:", ""]
+    t += ["    " + cmds[k] for k in ("trace", "fetch", "write")]
+    t += ["", "Byte counters scaled by the %d MiB device copy of the same run: FETCH_SIZE x %.3f KiB, WRITE_SIZE x "
+          "%.3f KiB.  Kernel bytes = what fwd_kvo_kernel's loop loads and stores (bench.py kv_outer_bytes); model = "
+          "the pages' order with 128-row query blocks (pinned to the oracle's counts); measured = mean over the "
+          "run's %d dispatches per configuration." % (CALIBRATE_MIB, fs, wsc, per), "",
+          "| N | key tile | groups / head | kv-outer ms | q-outer ms | kernel read / write MiB | model read / write MiB "
+          "| measured read / write MiB | measured / kernel |", "|---|---|---|---|---|---|---|---|---|"]
+    for i, d in enumerate(lines):
+        rd = sum(fetch[i * per:(i + 1) * per]) / per * fs / 1024
+        wr = sum(write[i * per:(i + 1) * per]) / per * wsc / 1024
+        own = d["kv_outer_read_MiB"] + d["kv_outer_write_MiB"]
+        t.append("| %d | %d | %d | %.4f | %.4f | %.1f / %.1f | %.1f / %.1f | %.1f / %.1f | %.2f |" % (
+            d["N"], d["block_cols"], d["groups_per_head"], d["kv_outer_ms"], d["q_outer_ms"],
+            d["kv_outer_read_MiB"], d["kv_outer_write_MiB"], d["model_read_MiB"], d["model_write_MiB"], rd, wr,
+            (rd + wr) / own))
+    q = M.get("fwd_kernel", {})
+    if "read_bytes" in q:
+        t += ["", "The query-outer fwd_kernel's dispatches in the same passes (mean over all three N): HBM read "
+              "%.1f MiB, write %.1f MiB." % (q["read_bytes"] / 2**20, q["write_bytes"] / 2**20)]
+    path = os.path.join(profiles_dir, "kv_outer_io_ablation.md")
+    open(path, "w").write("\n".join(t) + "\n")
+    return path
+
+
+def compare_standard_report(out_dir: str, profiles_dir: str = PROFILES, top: int = 16) -> str:
+    """profiles_dir/standard_attention_compare_kernel_trace.md from a
+    compare-standard profile: the kernels with the most GPU time over the run
+    and the comparison lines bench.py printed."""
+    import csv
+    rows = list(csv.DictReader(open(_find_csv(os.path.join(out_dir, "trace"), "kernel_stats.csv"))))
+    rows.sort(key=lambda r: -float(r["TotalDurationNs"]))
+    comp = []
+    with open(os.path.join(out_dir, "trace.out")) as fh:
+        for l in fh:
+            if l.startswith("{") and '"compare"' in l:
+                comp.append(json.loads(l))
+    cmd = " ".join(profile_commands("long", 6, mode="compare-standard")[0][1]).replace(sys.executable, "python") \
+        .replace(os.path.abspath(__file__), "bench.py").replace("{DIR}", "<dir>")
+    t = ["# Kernel trace: this library against standard attention (five separate ops on vendor GEMMs)", "",
+         "Causal, dropout 0.1, bf16, H=16, d=64, B*N = 16384 tokens at N = 1024, 2048, 4096 (plus the default long "
+         "workload that bench.py times first).", "",
+         "Made by `python bench.py --profile <dir> --profile-mode compare-standard`, whose trace pass is:", "",
+         "    " + cmd, "", "Top kernels by total GPU time over the whole run:", "",
+         "| kernel | calls | avg us | total ms | % of GPU time |", "|---|---|---|---|---|"]
+    for r in rows[:top]:
+        name = short_kernel(r["Name"]) if short_kernel(r["Name"]) in PROFILE_KERNELS else r["Name"][:90]
+        t.append("| %s | %s | %.1f | %.2f | %.2f |" % (name, r["Calls"], float(r["AverageNs"]) / 1e3,
+                                                     float(r["TotalDurationNs"]) / 1e6, float(r["Percentage"])))
+    t += ["", "bench.py's comparison lines from the same run (times by HIP events, medians; extra memory = the "
+          "peak a step adds over the resident inputs):", "",
+          "| N | B | this library fwd / bwd ms | standard fwd / bwd ms | speed-up fwd / bwd / step | extra MiB "
+          "(ratio) |", "|---|---|---|---|---|---|"]
+    for d in comp:
+        t.append("| %d | %d | %.3f / %.3f | %.3f / %.3f | %.1f / %.1f / %.1f | %.0f vs %.0f (%.0fx) |" % (
+            d["N"], d["B"], d["ours_fwd_ms"], d["ours_bwd_ms"], d["std_fwd_ms"], d["std_bwd_ms"], d["speedup_fwd"],
+            d["speedup_bwd"], d["speedup_step"], d["ours_peak_extra_MiB"], d["std_peak_extra_MiB"],
+            d["memory_ratio"]))
+    path = os.path.join(profiles_dir, "standard_attention_compare_kernel_trace.md")
+    open(path, "w").write("\n".join(t) + "\n")
+    return path
 
 
 def profile_report(out_dir: str, workload: str, tag=None, profiles_dir: str = PROFILES) -> dict:
@@ -895,9 +1018,15 @@ def main():
     args = parse()
     if args.profile or args.profile_report:
         # the passes run as child processes: this one never touches the GPU
+        out = os.path.abspath(args.profile or args.profile_report)
         if args.profile:
-            run_profile(os.path.abspath(args.profile), args.workload, args.steps)
-        profile_report(os.path.abspath(args.profile or args.profile_report), args.workload)
+            run_profile(out, args.workload, args.steps, mode=args.profile_mode)
+        if args.profile_mode == "io-ablation":
+            print("[profile] wrote", os.path.relpath(io_ablation_report(out), ROOT), flush=True)
+        elif args.profile_mode == "compare-standard":
+            print("[profile] wrote", os.path.relpath(compare_standard_report(out), ROOT), flush=True)
+        else:
+            profile_report(out, args.workload)
         return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU: the library has no multi-GPU path (each (b, h) head is "

@@ -69,3 +69,25 @@ def test_profile_passes_respect_counter_limits():
         assert sum(c.startswith("SQ_") for c in counters) <= 8
         assert sum(c.startswith("GRBM_") for c in counters) <= 2
         assert 3 * counters.count("FETCH_SIZE") + 2 * counters.count("WRITE_SIZE") <= 4
+
+
+def test_io_ablation_reduction(tmp_path):
+    """Per configuration: the mean of its dispatches' byte counters, scaled by
+    the copy (fetch x2, write x1), against the kernel's own byte model."""
+    path = bench.io_ablation_report(os.path.join(FIX + "_io"), profiles_dir=str(tmp_path))
+    text = open(path).read()
+    # config 1: fetch mean 2000 KiB x 2 = 3.9 MiB, write 512 KiB = 0.5 MiB; (3.9 + 0.5) / (4 + 1) = 0.88
+    assert "| 2048 | 64 | 1 | 1.5000 | 0.0500 | 4.0 / 1.0 | 3.0 / 0.5 | 3.9 / 0.5 | 0.88 |" in text
+    # config 2: fetch mean 5000 KiB x 2 = 9.8 MiB, write 1 MiB; 10.8 / 12 = 0.90
+    assert "| 4096 | 64 | 1 | 6.0000 | 0.1000 | 10.0 / 2.0 | 8.0 / 1.0 | 9.8 / 1.0 | 0.90 |" in text
+    assert "--profile-mode io-ablation" in text
+
+
+@pytest.mark.parametrize("mode", ["io-ablation", "compare-standard"])
+def test_profile_modes_run_the_ablations(mode):
+    cmds = bench.profile_commands("long", 8, python="python", mode=mode)
+    assert cmds[0][0] == "trace" and ("--" + mode) in cmds[0][1]
+    for name, argv in cmds[1:]:
+        assert argv[argv.index("--") + 1] == "python" and ("--" + mode) in argv
+        counters = argv[argv.index("--pmc") + 1:argv.index("--kernel-include-regex")]
+        assert 3 * counters.count("FETCH_SIZE") + 2 * counters.count("WRITE_SIZE") <= 4
