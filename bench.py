@@ -858,10 +858,23 @@ def io_ablation_report(out_dir: str, profiles_dir: str = PROFILES) -> str:
             d["N"], d["block_cols"], d["groups_per_head"], d["kv_outer_ms"], d["q_outer_ms"],
             d["kv_outer_read_MiB"], d["kv_outer_write_MiB"], d["model_read_MiB"], d["model_write_MiB"], rd, wr,
             (rd + wr) / own))
-    q = M.get("fwd_kernel", {})
-    if "read_bytes" in q:
-        t += ["", "The query-outer fwd_kernel's dispatches in the same passes (mean over all three N): HBM read "
-              "%.1f MiB, write %.1f MiB." % (q["read_bytes"] / 2**20, q["write_bytes"] / 2**20)]
+    # the query-outer forward: per N, the same number of dispatches as each
+    # configuration, the last fwd_kernel dispatches of the run (the timed
+    # workload bench.py runs first comes before them)
+    Ns = sorted({d["N"] for d in lines})
+    qf = _dispatch_counters(f_csv, "fwd_kernel", "FETCH_SIZE")
+    qw = _dispatch_counters(w_csv, "fwd_kernel", "WRITE_SIZE")
+    if len(qf) >= per * len(Ns) and len(qw) >= per * len(Ns):
+        qf, qw = qf[len(qf) - per * len(Ns):], qw[len(qw) - per * len(Ns):]
+        t += ["", "The query-outer fwd_kernel on the same inputs (mean over its %d dispatches per N):" % per, "",
+              "| N | q-outer ms | measured read / write MiB | Q, K, V in and O, LSE out, MiB |", "|---|---|---|---|"]
+        for i, N in enumerate(Ns):
+            d = next(x for x in lines if x["N"] == N)
+            rd = sum(qf[i * per:(i + 1) * per]) / per * fs / 1024
+            wr = sum(qw[i * per:(i + 1) * per]) / per * wsc / 1024
+            least = d.get("q_outer_min_MiB")
+            t.append("| %d | %.4f | %.1f / %.1f | %s |" % (N, d["q_outer_ms"], rd, wr,
+                                                          "-" if least is None else "%.1f" % least))
     path = os.path.join(profiles_dir, "kv_outer_io_ablation.md")
     open(path, "w").write("\n".join(t) + "\n")
     return path

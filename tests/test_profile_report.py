@@ -81,6 +81,11 @@ def test_io_ablation_reduction(tmp_path):
     # config 2: fetch mean 5000 KiB x 2 = 9.8 MiB, write 1 MiB; 10.8 / 12 = 0.90
     assert "| 4096 | 64 | 1 | 6.0000 | 0.1000 | 10.0 / 2.0 | 8.0 / 1.0 | 9.8 / 1.0 | 0.90 |" in text
     assert "--profile-mode io-ablation" in text
+    # the query-outer forward: the last 3 fwd_kernel dispatches per N (the
+    # earlier workload's dispatch is not among them); fetch (256, 512, 768)
+    # KiB -> mean 512 x 2 = 1.0 MiB, write 512 KiB = 0.5 MiB
+    assert "| 2048 | 0.0500 | 1.0 / 0.5 | - |" in text
+    assert "| 4096 | 0.1000 | 2.0 / 1.0 | - |" in text
 
 
 @pytest.mark.parametrize("mode", ["io-ablation", "compare-standard"])
