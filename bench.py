@@ -83,6 +83,8 @@ def parse():
     ap.add_argument("--cpu-rows", type=int, default=6144,
                     help="leading causal rows per head the oracle baseline computes")
     ap.add_argument("--sweep", action="store_true", help="also time the N sweep (extra JSON lines)")
+    ap.add_argument("--sweep-md", metavar="PATH", default=None,
+                    help="with --sweep: also write the sweep as a markdown table to PATH")
     ap.add_argument("--graph", action="store_true",
                     help="also time the step captured in a HIP graph (graph_ms_per_step; value stays eager)")
     ap.add_argument("--io-ablation", action="store_true",
@@ -1113,6 +1115,7 @@ def main():
     if args.io_ablation:
         io_ablation(ev, max(2, args.steps // 4), 1)
     if args.sweep:
+        rows = []
         for d in (64, 128):
             for causal in (False, True):
                 for N in (1024, 2048, 4096, 8192, 16384):
@@ -1120,11 +1123,35 @@ def main():
                     rr = time_workload(ws, max(3, args.steps // 2), 2, ev)
                     ff, bf = 4.0 * d * rr["pairs"], 10.0 * d * rr["pairs"]
                     fm, bm = med(rr["fwd_pass_ms"]), med(rr["bwd_pass_ms"])
-                    print(json.dumps({"sweep": True, "B": ws.B, "H": 16, "N": N, "d": d, "causal": causal,
-                                      "fwd_ms": round(fm, 4), "bwd_ms": round(bm, 4),
-                                      "fwd_tflops": round(ff / fm / 1e9, 1), "bwd_tflops": round(bf / bm / 1e9, 1),
-                                      "fwd_pct": round(100 * ff / fm / 1e9 / peak, 2),
-                                      "bwd_pct": round(100 * bf / bm / 1e9 / peak, 2)}), flush=True)
+                    rows.append({"sweep": True, "B": ws.B, "H": 16, "N": N, "d": d, "causal": causal,
+                                 "fwd_ms": round(fm, 4), "bwd_ms": round(bm, 4),
+                                 "fwd_tflops": round(ff / fm / 1e9, 1), "bwd_tflops": round(bf / bm / 1e9, 1),
+                                 "fwd_pct": round(100 * ff / fm / 1e9 / peak, 2),
+                                 "bwd_pct": round(100 * bf / bm / 1e9 / peak, 2)})
+                    print(json.dumps(rows[-1]), flush=True)
+        if args.sweep_md:
+            write_sweep_md(args.sweep_md, rows, out)
+
+
+def write_sweep_md(path: str, rows: list, line: dict) -> None:
+    """The sweep's JSON lines as a markdown table, with the command and the
+    main line of the same run."""
+    argv = [a for a in sys.argv[1:]]
+    t = ["# Sweep: fwd / bwd TFLOP/s and % of the 2.5 PFLOP/s bf16 peak", "",
+         "B*N = 16384 tokens, H = 16, bf16, seeded Gaussian inputs (std 1); whole passes (pre-passes included), "
+         "HIP events, medians.  Made by:", "", "    python bench.py " + " ".join(argv), "",
+         "The same run's main line (workload %s): %.2f TFLOP/s per step, forward %.2f %%, backward %.2f %% of "
+         "peak." % (line["config"]["workload"].split(":")[0], line["value"], line["fwd_pct_peak"],
+                    line["bwd_pct_peak"]), "",
+         "| N | B | d | causal | fwd ms | bwd ms | fwd TFLOP/s (%) | bwd TFLOP/s (%) |",
+         "|---|---|---|---|---|---|---|---|"]
+    for r in rows:
+        t.append("| %d | %d | %d | %s | %.4f | %.4f | %.1f (%.1f) | %.1f (%.1f) |" % (
+            r["N"], r["B"], r["d"], "yes" if r["causal"] else "no", r["fwd_ms"], r["bwd_ms"], r["fwd_tflops"],
+            r["fwd_pct"], r["bwd_tflops"], r["bwd_pct"]))
+    os.makedirs(os.path.dirname(os.path.abspath(path)), exist_ok=True)
+    open(path, "w").write("\n".join(t) + "\n")
+    print("[sweep] wrote", path, flush=True)
 
 
 if __name__ == "__main__":

@@ -96,3 +96,18 @@ def test_profile_modes_run_the_ablations(mode):
         assert argv[argv.index("--") + 1] == "python" and ("--" + mode) in argv
         counters = argv[argv.index("--pmc") + 1:argv.index("--kernel-include-regex")]
         assert 3 * counters.count("FETCH_SIZE") + 2 * counters.count("WRITE_SIZE") <= 4
+
+
+def test_sweep_markdown(tmp_path, monkeypatch):
+    """bench.py --sweep-md: one table row per sweep point, with the command
+    and the same run's main line."""
+    monkeypatch.setattr("sys.argv", ["bench.py", "--sweep", "--sweep-md", "out.md"])
+    rows = [{"sweep": True, "B": 4, "H": 16, "N": 4096, "d": 128, "causal": True, "fwd_ms": 0.25, "bwd_ms": 0.75,
+             "fwd_tflops": 900.0, "bwd_tflops": 700.0, "fwd_pct": 36.0, "bwd_pct": 28.0}]
+    line = {"config": {"workload": "long: B=1 H=16"}, "value": 850.0, "fwd_pct_peak": 42.0, "bwd_pct_peak": 33.0}
+    p = tmp_path / "s.md"
+    bench.write_sweep_md(str(p), rows, line)
+    text = p.read_text()
+    assert "python bench.py --sweep --sweep-md out.md" in text
+    assert "| 4096 | 4 | 128 | yes | 0.2500 | 0.7500 | 900.0 (36.0) | 700.0 (28.0) |" in text
+    assert "workload long): 850.00 TFLOP/s" in text
