@@ -85,6 +85,11 @@ def parse():
     ap.add_argument("--sweep", action="store_true", help="also time the N sweep (extra JSON lines)")
     ap.add_argument("--sweep-md", metavar="PATH", default=None,
                     help="with --sweep: also write the sweep as a markdown table to PATH")
+    ap.add_argument("--power", metavar="SECONDS", type=float, default=0.0,
+                    help="also run the workload's forward, then its backward, back to back for SECONDS each "
+                         "while amd-smi samples socket power and the GFX clock (extra JSON lines)")
+    ap.add_argument("--power-md", metavar="PATH", default=None,
+                    help="with --power: also write the samples' medians as a markdown table to PATH")
     ap.add_argument("--graph", action="store_true",
                     help="also time the step captured in a HIP graph (graph_ms_per_step; value stays eager)")
     ap.add_argument("--io-ablation", action="store_true",
@@ -1114,6 +1119,10 @@ def main():
         compare_standard(ev, max(5, args.steps // 2), 2)
     if args.io_ablation:
         io_ablation(ev, max(2, args.steps // 4), 1)
+    if args.power > 0:
+        prow = power_run(w, args.power)
+        if args.power_md:
+            write_power_md(args.power_md, prow, out)
     if args.sweep:
         rows = []
         for d in (64, 128):
@@ -1131,6 +1140,108 @@ def main():
                     print(json.dumps(rows[-1]), flush=True)
         if args.sweep_md:
             write_sweep_md(args.sweep_md, rows, out)
+
+
+def parse_amd_smi(text: str) -> tuple:
+    """(socket power W, GFX_0 clock MHz) from `amd-smi metric -p -c` text, or
+    None for a value it does not show."""
+    power = clock = None
+    in_gfx0 = False
+    for raw in text.splitlines():
+        l = raw.strip()
+        if l.startswith("SOCKET_POWER:") and power is None:
+            try:
+                power = float(l.split(":", 1)[1].split()[0])
+            except (ValueError, IndexError):
+                pass
+        elif l.startswith("GFX_"):
+            in_gfx0 = l.rstrip(":") == "GFX_0"
+        elif in_gfx0 and l.startswith("CLK:") and clock is None:
+            try:
+                clock = float(l.split(":", 1)[1].split()[0])
+            except (ValueError, IndexError):
+                pass
+    return power, clock
+
+
+def power_run(w, seconds: float) -> list:
+    """Each pass of workload w back to back for `seconds` while a thread runs
+    `amd-smi metric -p -c` every 0.5 s; medians over the samples after the
+    first second (the clock ramps up first)."""
+    import statistics
+    import subprocess
+    import threading
+    import torch
+    import io_aware_exact_tiled_amd as fa
+    import workloads as W
+
+    x = W.make_inputs(w)
+    dev = torch.device("cuda:0")
+    q, k, v, do = (x[n].to(dev) for n in ("q", "k", "v", "do"))
+    kw = dict(causal=w.causal, dropout_p=w.dropout_p, seed=w.dropout_seed, rng_offset=w.rng_offset,
+              key_lens=None if x["key_lens"] is None else x["key_lens"].to(dev),
+              block_mask=None if x["block_mask"] is None else x["block_mask"].to(dev), scale=w.scale)
+    o = torch.empty_like(q)
+    lse = torch.empty(w.B, w.H, w.N, dtype=torch.float32, device=dev)
+    grads = (torch.empty_like(q), torch.empty_like(k), torch.empty_like(v))
+    ws = torch.empty(fa.bwd_workspace_bytes(w.B, w.H, w.N, w.d), dtype=torch.uint8, device=dev)
+    fws = torch.empty(max(1, fa.fwd_workspace_bytes(w.B, w.Hkv, w.N, w.d, q.dtype)), dtype=torch.uint8, device=dev)
+    fa.fwd(q, k, v, out=o, lse=lse, workspace=fws, **kw)
+    passes = {"forward": lambda: fa.fwd(q, k, v, out=o, lse=lse, workspace=fws, **kw),
+              "backward": lambda: fa.bwd(q, k, v, o, do, lse, grads=grads, workspace=ws, **kw)}
+    out = []
+    for name, run in passes.items():
+        samples, stop = [], threading.Event()
+
+        def sample():
+            t0 = time.perf_counter()
+            while not stop.is_set():
+                try:
+                    r = subprocess.run(["amd-smi", "metric", "-p", "-c"], capture_output=True, text=True, timeout=10)
+                    samples.append((time.perf_counter() - t0,) + parse_amd_smi(r.stdout))
+                except (OSError, subprocess.SubprocessError):
+                    return
+                stop.wait(0.5)
+
+        torch.cuda.synchronize()
+        th = threading.Thread(target=sample)
+        t0 = time.perf_counter()
+        th.start()
+        n = 0
+        while time.perf_counter() - t0 < seconds:
+            for _ in range(10):
+                run()
+            torch.cuda.synchronize()
+            n += 10
+        stop.set()
+        th.join()
+        late = [s for s in samples if s[0] >= 1.0 and s[1] is not None and s[2] is not None]
+        out.append({"power": name, "calls": n, "seconds": round(time.perf_counter() - t0, 2),
+                    "samples": len(late),
+                    "socket_power_w": statistics.median(s[1] for s in late) if late else None,
+                    "gfx_clock_mhz": statistics.median(s[2] for s in late) if late else None})
+        print(json.dumps(out[-1]), flush=True)
+    return out
+
+
+def write_power_md(path: str, rows: list, line: dict) -> None:
+    """The power lines as a markdown table, with the command and the main line
+    of the same run."""
+    t = ["# Socket power and GFX clock while each pass runs back to back", "",
+         "Workload %s.  amd-smi (`metric -p -c`) sampled every 0.5 s; medians over the samples after the "
+         "first second.  Made by:" % line["config"]["workload"], "",
+         "    python bench.py " + " ".join(sys.argv[1:]), "",
+         "The same run's main line: %.2f TFLOP/s per step, forward %.2f %%, backward %.2f %% of peak." % (
+             line["value"], line["fwd_pct_peak"], line["bwd_pct_peak"]), "",
+         "| pass | calls | seconds | samples | socket power W | GFX clock MHz |", "|---|---|---|---|---|---|"]
+    for r in rows:
+        t.append("| %s | %d | %.2f | %d | %s | %s |" % (
+            r["power"], r["calls"], r["seconds"], r["samples"],
+            "-" if r["socket_power_w"] is None else "%.0f" % r["socket_power_w"],
+            "-" if r["gfx_clock_mhz"] is None else "%.0f" % r["gfx_clock_mhz"]))
+    os.makedirs(os.path.dirname(os.path.abspath(path)), exist_ok=True)
+    open(path, "w").write("\n".join(t) + "\n")
+    print("[power] wrote", path, flush=True)
 
 
 def write_sweep_md(path: str, rows: list, line: dict) -> None:

@@ -111,3 +111,37 @@ def test_sweep_markdown(tmp_path, monkeypatch):
     assert "python bench.py --sweep --sweep-md out.md" in text
     assert "| 4096 | 4 | 128 | yes | 0.2500 | 0.7500 | 900.0 (36.0) | 700.0 (28.0) |" in text
     assert "workload long): 850.00 TFLOP/s" in text
+
+
+AMD_SMI_SAMPLE = """GPU: 0
+    POWER:
+        SOCKET_POWER: 1339 W
+        GFX_VOLTAGE: N/A
+        THROTTLE_STATUS: N/A
+    CLOCK:
+        GFX_0:
+            CLK: 1799 MHz
+            MIN_CLK: 500 MHz
+            MAX_CLK: 2400 MHz
+        GFX_1:
+            CLK: 1801 MHz
+            MIN_CLK: 500 MHz
+"""
+
+
+def test_amd_smi_parse_and_power_table(tmp_path, monkeypatch):
+    """bench.py --power: the socket power and GFX_0's clock from amd-smi's
+    text (values it does not show are None), and the table it writes."""
+    assert bench.parse_amd_smi(AMD_SMI_SAMPLE) == (1339.0, 1799.0)
+    assert bench.parse_amd_smi("GPU: 0\n    POWER:\n        SOCKET_POWER: N/A\n") == (None, None)
+    monkeypatch.setattr("sys.argv", ["bench.py", "--power", "8", "--power-md", "p.md"])
+    rows = [{"power": "forward", "calls": 5920, "seconds": 6.01, "samples": 9, "socket_power_w": 1339.0,
+             "gfx_clock_mhz": 1799.0},
+            {"power": "backward", "calls": 1840, "seconds": 6.0, "samples": 0, "socket_power_w": None,
+             "gfx_clock_mhz": None}]
+    line = {"config": {"workload": "long: B=1"}, "value": 900.0, "fwd_pct_peak": 43.0, "bwd_pct_peak": 34.0}
+    p = tmp_path / "p.md"
+    bench.write_power_md(str(p), rows, line)
+    text = p.read_text()
+    assert "python bench.py --power 8 --power-md p.md" in text
+    assert "| forward | 5920 | 6.01 | 9 | 1339 | 1799 |" in text and "| backward | 1840 | 6.00 | 0 | - | - |" in text
