@@ -381,7 +381,6 @@ __global__ __launch_bounds__(NW * 64, NW == 8 ? 1 : 2) void bwd_kv_kernel(BwdArg
             // dS = P o (dP - D), kept as packed operands for the next step
 #pragma unroll
             for (int qb = 0; qb < QB; ++qb) {
-                const int qr0 = qb * 32 + hl * 16;
                 float ds[16];
                 if constexpr (PACKED) {
                     // P (and Pd = P o Z s) of the 16 queries from the packed fragments
