@@ -193,7 +193,9 @@ fa_status fa_bwd(const void* Q, const void* K, const void* V, const void* O,
  * kernels.  Every call on one GPU shares that GPU's array: two calls whose
  * work overlaps on one GPU (on different streams, or from different threads
  * without ordering) race and may give wrong gradients; calls ordered on one
- * stream are safe.  Each call writes all of D before reading it. */
+ * stream are safe.  Each call writes all of D before reading it.  The array
+ * used is the one on the calling thread's current device, so `stream` must
+ * belong to that device (as for fa_bwd, whose workspace must live there). */
 #define FA_BWD_SCRATCH_BYTES ((size_t)16 << 20)
 fa_status fa_bwd_noalloc(const void* Q, const void* K, const void* V, const void* O,
                          const void* dO, const float* LSE, void* dQ, void* dK, void* dV,
