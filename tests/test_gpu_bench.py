@@ -1,6 +1,7 @@
-"""bench.py's command line on the GPU: the JSON line it prints keeps the
-contract fields for the fwd+bwd workloads (with the HIP-graph timing) and
-for the decode workload."""
+"""bench.py's output contract on the GPU: one JSON line with the metric, the
+whole-step throughput, the roofline object of the dominant kernel (achieved
+over peak, measured on the kernel's own stream) and the oracle's CPU
+baseline on a bounded sample; and the decode line in GB/s."""
 
 import json
 import os
@@ -12,30 +13,51 @@ import pytest
 pytestmark = pytest.mark.gpu
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
-CONTRACT = ("metric", "value", "unit", "n_gpus", "steps", "warmup", "ms_per_step", "higher_is_better",
-            "scaling", "vs_baseline", "dtype", "data", "config", "roofline")
 
 
-def run_bench(*args):
-    print(f"[case] bench.py {' '.join(args)}", flush=True)
-    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--steps", "3", "--warmup", "1",
-                        "--no-cpu-baseline", *args], capture_output=True, text=True, timeout=110, cwd=ROOT)
+def _bench(*args, timeout=240):
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), *args], capture_output=True, text=True,
+                       timeout=timeout, cwd=ROOT)
     assert r.returncode == 0, r.stderr[-2000:]
-    line = [l for l in r.stdout.splitlines() if l.startswith("{")][-1]
-    d = json.loads(line)
-    for k in CONTRACT:
-        assert k in d, k
-    assert d["n_gpus"] == 1 and d["steps"] == 3 and d["warmup"] == 1 and d["value"] > 0
-    for k in ("bound", "achieved", "peak", "unit", "frac", "traffic"):
-        assert k in d["roofline"], k
-    return d
+    lines = [json.loads(l) for l in r.stdout.splitlines() if l.startswith("{")]
+    assert len(lines) == 1, r.stdout[-2000:]
+    return lines[0]
 
 
-def test_bench_fwd_bwd_line_with_graph_timing():
-    d = run_bench("--workload", "gpt2", "--graph")
-    assert d["unit"] == "TFLOP/s" and d["graph_ms_per_step"] > 0 and d["graph_tflops"] > 0
+def _roofline_consistent(d):
+    rf = d["roofline"]
+    assert rf["bound"] in ("mfma", "hbm") and rf["peak"] > 0 and rf["achieved"] > 0
+    assert rf["frac"] == pytest.approx(rf["achieved"] / rf["peak"], rel=2e-3)
+    assert 0.0 < rf["frac"] < 1.0
+    assert rf["traffic"] is None or rf["traffic"] > 0
 
 
-def test_bench_decode_line():
-    d = run_bench("--workload", "decode")
-    assert d["unit"] == "GB/s" and d["roofline"]["bound"] == "hbm"
+@pytest.mark.timeout(300)
+def test_default_line_contract():
+    """The default workload (long causal, d = 128): the fields the contract
+    names, a positive throughput, and a CPU baseline from a small sample."""
+    print("[case] bench.py default workload, 3 steps, 512-row CPU sample", flush=True)
+    d = _bench("--steps", "3", "--warmup", "1", "--cpu-rows", "512")
+    for key in ("metric", "value", "unit", "n_gpus", "steps", "warmup", "ms_per_step", "higher_is_better",
+                "scaling", "vs_baseline", "dtype", "data", "config", "roofline", "cpu_baseline"):
+        assert key in d, key
+    assert d["n_gpus"] == 1 and d["steps"] == 3 and d["warmup"] == 1 and d["higher_is_better"] is True
+    assert d["unit"] == "TFLOP/s" and d["dtype"] == "bf16" and d["value"] > 0 and d["ms_per_step"] > 0
+    assert d["config"]["workload"].startswith("long")
+    assert d["roofline"]["unit"] == "TFLOP/s" and d["roofline"]["kernel"] == "bwd_kv_kernel"
+    _roofline_consistent(d)
+    cb = d["cpu_baseline"]
+    assert cb["kind"] == "oracle" and cb["unit"] == "TFLOP/s" and cb["value"] > 0 and cb["cores"] >= 1
+    assert "512" in cb["sample"]
+    print(f"[ok] {d['value']} TFLOP/s, frac {d['roofline']['frac']}, cpu {cb['value']}", flush=True)
+
+
+@pytest.mark.timeout(300)
+def test_decode_line_contract():
+    """The decode workload reports HBM GB/s against the 8 TB/s roofline."""
+    print("[case] bench.py --workload decode, 5 steps", flush=True)
+    d = _bench("--workload", "decode", "--steps", "5", "--warmup", "1", "--no-cpu-baseline")
+    assert d["unit"] == "GB/s" and d["value"] > 0 and d["config"]["workload"].startswith("decode")
+    assert d["roofline"]["bound"] == "hbm" and d["roofline"]["unit"] == "GB/s"
+    _roofline_consistent(d)
+    print(f"[ok] decode {d['value']} GB/s, frac {d['roofline']['frac']}", flush=True)
