@@ -1,7 +1,8 @@
 """bench.py's output contract on the GPU: one JSON line with the metric, the
 whole-step throughput, the roofline object of the dominant kernel (achieved
 over peak, measured on the kernel's own stream) and the oracle's CPU
-baseline on a bounded sample; and the decode line in GB/s."""
+baseline on a bounded sample; the decode line in GB/s; and the HIP-graph
+replay timing of --graph."""
 
 import json
 import os
@@ -61,3 +62,15 @@ def test_decode_line_contract():
     assert d["roofline"]["bound"] == "hbm" and d["roofline"]["unit"] == "GB/s"
     _roofline_consistent(d)
     print(f"[ok] decode {d['value']} GB/s, frac {d['roofline']['frac']}", flush=True)
+
+
+@pytest.mark.timeout(300)
+def test_graph_timing_line():
+    """--graph: the same step captured once in a HIP graph and replayed, its
+    time and throughput reported beside the eager ones (GPT-2 shape)."""
+    print("[case] bench.py --workload gpt2 --graph, 3 steps", flush=True)
+    d = _bench("--workload", "gpt2", "--graph", "--steps", "3", "--warmup", "1", "--no-cpu-baseline")
+    assert d["unit"] == "TFLOP/s" and d["value"] > 0
+    assert d["graph_ms_per_step"] > 0 and d["graph_tflops"] > 0
+    _roofline_consistent(d)
+    print(f"[ok] eager {d['ms_per_step']} ms, graph {d['graph_ms_per_step']} ms", flush=True)
