@@ -145,3 +145,21 @@ def test_amd_smi_parse_and_power_table(tmp_path, monkeypatch):
     text = p.read_text()
     assert "python bench.py --power 8 --power-md p.md" in text
     assert "| forward | 5920 | 6.01 | 9 | 1339 | 1799 |" in text and "| backward | 1840 | 6.00 | 0 | - | - |" in text
+
+
+def test_every_committed_summary_names_the_command_that_made_it():
+    """Each profiles/*.md holds the bench.py (and for traces and counters the
+    rocprofv3) command line that regenerates it, and names no file outside
+    the repository's committed tree."""
+    names = sorted(f for f in os.listdir(bench.PROFILES) if f.endswith(".md"))
+    assert names
+    for f in names:
+        text = open(os.path.join(bench.PROFILES, f)).read()
+        assert "python bench.py" in text, f
+        if f.endswith(("_kernel_trace.md", "_counters.md")):
+            assert "rocprofv3 " in text, f
+        assert "_work/" not in text and "/root/reference" not in text, f
+    t = json.load(open(bench.TRAFFIC_FILE))
+    for wl, kernels in t["workloads"].items():
+        for k, e in kernels.items():
+            assert e["counters"] in names, (wl, k)
